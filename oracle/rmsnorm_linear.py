@@ -1,0 +1,289 @@
+"""Plain numpy oracle for the fused RMSNorm -> Linear projection.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+``cpu_baseline`` leg of the benchmark; never by the product path.
+
+Pages this follows (cited by title and section):
+
+* AT-10 page -- "PyPTO-Gym operator design pattern AT-10: RMSNorm + Linear
+  fused (V->C layout), principle and MLAProlog practice":
+  section 2 (CV layout and the standard compute flow),
+  section 3 (V stage: RMSNorm variant A "rsqrt", variant B "sqrt + div",
+  the MLA ``rms_norm`` code, the AT-03 instantiation-parameter table),
+  section 4 (C stage: AT-09 BF16 mode, INT8 W8A8 mode, AT-05 / AT-06),
+  section 5 (MLAProlog: q_a_proj -> norm -> q_b_proj),
+  section 9 (golden reference: ``rms_norm_new`` divides x by sqrt).
+* SK-03 page -- "SK-03 Linear Projection (Norm->MatMul)": the skeleton
+  template, the quant variant (``common.py`` ``quant`` / ``quant_tensor``)
+  and the mhc_pre variant (large reduction x tiny width, FP32 compute).
+* SK-14 page -- "SK-14 General Multi-MatMul skeleton": section 5 mode 1
+  (serial pipeline, MLA q_a_proj -> norm -> q_b_proj) and the
+  QuantMatMulReduceSum example (dequant as acc_fp32 * (x1_scale * x2_scale)).
+* Patterns page -- "PyPTO common coding patterns": section 9.17 table
+  (eps is added before the reciprocal square root) and section 9.18 point 5
+  (``b_trans=True`` means ``a @ b.T``).
+
+Conventions.  bf16 tensors are passed as ``uint16`` bit patterns, fp32 as
+``float32``, int8 as ``int8``.  Every fp32 step is one numpy float32 operation,
+which IEEE-754 rounds to nearest even; numpy never contracts a multiply and an
+add.  Readings of points the pages leave open are marked READING and are
+listed, with their reasons, in the design notes of the repository.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# bf16 <-> fp32
+# ----------------------------------------------------------------------------
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact: bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return (b << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    AT-10 page section 2 casts the fp32 normed values to BF16 before the
+    matmul; the rounding rule is not stated.  READING: IEEE round to nearest
+    even on the 16 discarded bits; a NaN stays a (quiet) NaN.
+    """
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    rounded = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        quiet = ((u >> np.uint64(16)) | np.uint64(0x0040)).astype(np.uint16)
+        rounded = np.where(nan, quiet, rounded)
+    return rounded
+
+
+def _bf16_round_f32(x) -> np.ndarray:
+    """fp32 values rounded to bf16 and widened back to fp32 (exact widening)."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm (AT-03 as used by AT-10)
+# ----------------------------------------------------------------------------
+def _row_mean_square(xf: np.ndarray) -> np.ndarray:
+    """ms[t] = fl( fl(sum_k xf^2) * fl(1/K) ).
+
+    AT-10 page section 3, variant A: square in fp32, sum along the last axis,
+    multiply by 1/D.  The pages ask for fp32 reductions (the C-API-05
+    constraint quoted there) but give no summation order.  READING: the
+    squares (exact in fp64) are summed in fp64 and the sum is rounded to fp32
+    once, so the oracle's sum is the correctly rounded value up to fp64
+    round-off; 1/D is the fp32 constant fl(1/K).
+    """
+    K = xf.shape[-1]
+    x64 = xf.astype(F64)
+    S = F32(np.sum(x64 * x64, axis=-1))  # fp64 sum, one rounding to fp32
+    c = F32(1.0) / F32(K)
+    return (S * c).astype(F32)
+
+
+def rstd_variant_b(ms: np.ndarray, eps: float) -> np.ndarray:
+    """rstd = fl(1 / fl(sqrt(fl(ms + eps)))) -- AT-10 page section 3 variant B
+    (sqrt then divide ones by std), the form the MLA ``rms_norm`` code uses.
+    eps is added to the mean square, before the root (patterns page 9.17)."""
+    var = (ms.astype(F32) + F32(eps)).astype(F32)
+    std = np.sqrt(var).astype(F32)
+    return (F32(1.0) / std).astype(F32)
+
+
+def rstd_variant_a(ms: np.ndarray, eps: float) -> np.ndarray:
+    """rstd = rsqrt(fl(ms + eps)) -- AT-10 page section 3 variant A.
+
+    The hardware rsqrt instruction has its own error; the oracle takes the
+    ideal value: 1/sqrt(var) in fp64, rounded once to fp32.
+    """
+    var = (ms.astype(F32) + F32(eps)).astype(F32)
+    return (1.0 / np.sqrt(var.astype(F64))).astype(F32)
+
+
+def rms_norm_rows(x_bits, gamma_bits, eps: float, rstd=None, variant: str = "B"):
+    """Per-row RMSNorm in fp32.  Returns (n [T,K] fp32, rstd [T] fp32).
+
+    AT-10 page section 3: xf = cast(x, FP32); ms = sum(xf^2)/D; var = ms+eps;
+    rstd = 1/sqrt(var); y = xf * rstd; optional y = y * cast(gamma, FP32)
+    (gamma applied after the rstd product, as the MLA caller does in
+    section 5).  If ``rstd`` is given (for instance the device's own), it is
+    used instead of recomputing it, so that the normed values can be compared
+    bit for bit downstream.
+    """
+    xf = bf16_bits_to_f32(x_bits)
+    if xf.ndim != 2:
+        raise ValueError("x must be [T, K]")
+    if rstd is None:
+        ms = _row_mean_square(xf)
+        rstd = rstd_variant_b(ms, eps) if variant == "B" else rstd_variant_a(ms, eps)
+    rstd = np.asarray(rstd, dtype=F32).reshape(-1)
+    n = (xf * rstd[:, None]).astype(F32)
+    if gamma_bits is not None:
+        g = bf16_bits_to_f32(gamma_bits).reshape(1, -1)
+        n = (n * g).astype(F32)
+    return n, rstd
+
+
+def rms_norm_rows_mla_order(x_bits, eps: float):
+    """Alternative ordering of the MLA ``rms_norm`` code (AT-10 page section 3):
+    each square is multiplied by 1/D before the sum.  Returns (n, rstd); no
+    gamma (the caller applies it).  Used only to cross-check the ordering."""
+    xf = bf16_bits_to_f32(x_bits)
+    K = xf.shape[-1]
+    c = F32(1.0) / F32(K)
+    sq = (xf * xf).astype(F32)
+    scaled = (sq * c).astype(F32)
+    ms = F32(np.sum(scaled.astype(F64), axis=-1))
+    rstd = rstd_variant_b(np.asarray(ms, dtype=F32), eps)
+    return (xf * rstd[:, None]).astype(F32), rstd
+
+
+def rms_norm_rows_golden_div(x_bits, eps: float):
+    """The golden reference form of AT-10 page section 9 (``rms_norm_new``):
+    x / sqrt(mean_sq + eps), a division instead of a product with rstd."""
+    xf = bf16_bits_to_f32(x_bits)
+    ms = _row_mean_square(xf)
+    std = np.sqrt((ms + F32(eps)).astype(F32)).astype(F32)
+    return (xf / std[:, None]).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# Projections
+# ----------------------------------------------------------------------------
+def project_bf16(n: np.ndarray, W_bits) -> np.ndarray:
+    """y = matmul(cast(n, BF16), W, b_trans=True) as fp32 [T, N].
+
+    AT-10 page section 2 and 4: the normed rows are cast to BF16 and
+    multiplied by the weight stored [N, K] (``b_trans=True`` is ``a @ b.T``,
+    patterns page 9.18 point 5).  READING: the products of two bf16 values are
+    exact in fp64; they are accumulated in fp64 and the result is rounded once
+    to fp32.  A bf16 output is that fp32 value rounded to bf16.
+    """
+    a = _bf16_round_f32(n).astype(F64)
+    w = bf16_bits_to_f32(W_bits).astype(F64)
+    return (a @ w.T).astype(F32)
+
+
+def project_fp32(n: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """FP32 compute of the SK-03 page's mhc_pre variant: normed rows stay fp32,
+    W is fp32 [N, K]; fp32 x fp32 products are exact in fp64, summed in fp64,
+    rounded once to fp32."""
+    return (n.astype(F64) @ np.asarray(W, dtype=F32).astype(F64).T).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# INT8 W8A8 (AT-09 INT8 mode, AT-05 quant, AT-06 dequant)
+# ----------------------------------------------------------------------------
+def quant_values(n: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """q = saturate_int8(round_half_even(fl(n * s))), saturating at +-127.
+
+    SK-03 page, quant variant: ``common.py quant`` casts with RINT, then
+    ROUND, then TRUNC with saturation to INT8.  READING: one round-to-nearest-
+    even to an integer; the later casts leave an in-range integer unchanged;
+    saturation is symmetric at +-127 (the symmetric scale never needs -128).
+    """
+    v = (n.astype(F32) * np.asarray(s, dtype=F32)).astype(F32)
+    r = np.rint(v)  # numpy rint rounds half to even
+    return np.clip(r, -127.0, 127.0).astype(np.int8)
+
+
+def quant_rows(n: np.ndarray):
+    """Per-token symmetric dynamic quant (AT-05; SK-03 page ``quant_tensor``).
+
+    amax[t] = max_k |n[t,k]|; s = fl(127 / amax) (AT-10 page section 4: 127.0 /
+    max gives the scale); q = quant_values(n, s); dequant scale x_scale =
+    fl(amax / 127) (SK-03 page: the symmetric scale is max/127.0 and is
+    returned for dequant).  READING for an all-zero row (amax = 0, which the
+    pages leave open): q = 0 and x_scale = 0.
+    Returns (q int8 [T,K], x_scale fp32 [T], s fp32 [T]).
+    """
+    n = n.astype(F32)
+    amax = np.max(np.abs(n), axis=-1).astype(F32)
+    zero = amax == 0
+    safe = np.where(zero, F32(1.0), amax).astype(F32)
+    s = (F32(127.0) / safe).astype(F32)
+    s = np.where(zero, F32(0.0), s).astype(F32)
+    q = quant_values(n, s[:, None])
+    x_scale = (amax / F32(127.0)).astype(F32)
+    return q, x_scale, s
+
+
+def int8_gemm(q: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+    """acc[t, j] = sum_k q[t,k] * Wq[j,k], exact in int64 (AT-09 INT8 mode:
+    int8 x int8 -> INT32 matmul with b_trans).  Raises if a sum leaves int32."""
+    acc = q.astype(np.int64) @ np.asarray(Wq, dtype=np.int8).astype(np.int64).T
+    if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -(2**31)):
+        raise OverflowError("int8 GEMM result does not fit int32")
+    return acc
+
+
+def dequant(acc: np.ndarray, x_scale: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+    """y = fl( fl(float(acc)) * fl(x_scale[t] * w_scale[j]) ) as fp32.
+
+    AT-06 multiplies the int32 result by the activation and weight scales; the
+    SK-14 page's QuantMatMulReduceSum fixes the order: cast the int32 result to
+    fp32, form scale_mul = x1_scale * x2_scale, multiply.  The int -> fp32
+    cast rounds to nearest even.
+    """
+    accf = acc.astype(F32)
+    sm = (np.asarray(x_scale, dtype=F32)[:, None] * np.asarray(w_scale, dtype=F32)[None, :]).astype(F32)
+    return (accf * sm).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# Entry points (same names and argument meanings as the C-ABI library)
+# ----------------------------------------------------------------------------
+def rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd=None):
+    """AT-10: RMSNorm (fp32) -> bf16 cast -> matmul(W[N,K], b_trans).
+
+    Returns (y32 fp32 [T,N], y_bf16 bits [T,N], rstd [T]).
+    """
+    n, rstd = rms_norm_rows(x_bits, gamma_bits, eps, rstd)
+    y32 = project_bf16(n, W_bits)
+    return y32, f32_to_bf16_bits(y32), rstd
+
+
+def rmsnorm_linear_fp32w(x_bits, gamma_bits, eps, W, rstd=None):
+    """SK-03 page mhc_pre variant: normed rows kept fp32 (no bf16 cast), fp32
+    weight [N, K], fp32 output.  Returns (y32 [T,N], rstd [T])."""
+    n, rstd = rms_norm_rows(x_bits, gamma_bits, eps, rstd)
+    return project_fp32(n, W), rstd
+
+
+def rmsnorm_linear_int8(x_bits, gamma_bits, eps, Wq, w_scale, rstd=None):
+    """AT-11 = AT-10 with the INT8 W8A8 projection (AT-05 -> INT32 matmul ->
+    AT-06).  The fp32 normed rows are quantized (AT-10 page section 6: the
+    Phase-1 sketch quantizes ``normed``).  Returns a dict with q, x_scale,
+    acc (int64), y32 (fp32), y_bf16 (bits), rstd."""
+    n, rstd = rms_norm_rows(x_bits, gamma_bits, eps, rstd)
+    q, x_scale, _ = quant_rows(n)
+    acc = int8_gemm(q, Wq)
+    y32 = dequant(acc, x_scale, w_scale)
+    return {"q": q, "x_scale": x_scale, "acc": acc, "y32": y32,
+            "y_bf16": f32_to_bf16_bits(y32), "rstd": rstd}
+
+
+def norm_proj_chain(x_bits, Wa_bits, gamma_bits, eps, Wb_bits, rstd=None, qa_bits=None):
+    """MLA q_a_proj -> RMSNorm -> q_b_proj (AT-10 page section 5; SK-14 page
+    section 5 mode 1).
+
+    q_a = bf16(matmul(x, W_a, BF16)); qr = bf16(rms_norm(q_a) * gamma) is
+    assembled into ``qr_out``; y = bf16(matmul(qr, W_b, BF16)).  If ``qa_bits``
+    is given (the device's q_a) the norm starts from it, and if ``rstd`` is
+    given it replaces the recomputed one.  Returns a dict with qa (bits),
+    qr (bits), y32 (fp32), y_bf16 (bits), rstd.
+    """
+    if qa_bits is None:
+        qa_bits = f32_to_bf16_bits(project_bf16(bf16_bits_to_f32(x_bits), Wa_bits))
+    n, rstd = rms_norm_rows(qa_bits, gamma_bits, eps, rstd)
+    qr_bits = f32_to_bf16_bits(n)
+    y32 = project_bf16(bf16_bits_to_f32(qr_bits), Wb_bits)
+    return {"qa": qa_bits, "qr": qr_bits, "y32": y32, "y_bf16": f32_to_bf16_bits(y32), "rstd": rstd}

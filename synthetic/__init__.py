@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the fused RMSNorm -> Linear projection workloads.
+
+This module only draws random tensors.  It holds none of the arithmetic of the
+method (no norm, no quantisation, no contraction): the HIP path and the CPU
+oracle both take their inputs from here and from nowhere else.
+
+Every tensor comes from its own CPU ``torch.Generator`` seeded from
+``(seed, stream)``, so a tensor does not change when another one is added or
+resized.  Float draws are made in fp32 and stored through torch's own bf16
+conversion; int8 weights are drawn uniformly from [-127, 127].
+
+Distributions follow the workload statements: activations x ~ N(0, 1) bf16,
+gamma ~ U(0.5, 1.5) bf16, weights W[N, K] ~ N(0, std = 1/sqrt(K)), int8
+weights uniform in [-127, 127] with per-output-channel fp32 scales
+U(1e-3, 1e-2), eps = 1e-6.  The pages (AT-10 "RMSNorm + Linear (Fused)" and
+SK-03 "Linear Projection (Norm->MatMul)") print no dataset; dense iid values
+with no sparsity or outliers stand in for the model activations their
+operators see.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+EPS = 1e-6
+
+# stream ids: one per tensor role, so that adding a tensor never shifts another
+_S_X, _S_GAMMA, _S_W, _S_WSCALE, _S_WA, _S_WB = 1, 2, 3, 4, 5, 6
+
+
+def _gen(seed: int, stream: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed((int(seed) * 1_000_003 + int(stream)) & 0x7FFF_FFFF_FFFF_FFFF)
+    return g
+
+
+def normal(shape, std: float, seed: int, stream: int, dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0, std^2) draws, made in fp32 and stored as ``dtype`` (CPU tensor)."""
+    t = torch.randn(tuple(shape), generator=_gen(seed, stream), dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype).contiguous()
+
+
+def uniform(shape, lo: float, hi: float, seed: int, stream: int, dtype=torch.bfloat16) -> torch.Tensor:
+    """U(lo, hi) draws, made in fp32 and stored as ``dtype`` (CPU tensor)."""
+    t = torch.rand(tuple(shape), generator=_gen(seed, stream), dtype=torch.float32)
+    t.mul_(hi - lo).add_(lo)
+    return t.to(dtype).contiguous()
+
+
+def int8_uniform(shape, seed: int, stream: int) -> torch.Tensor:
+    """Integers uniform in [-127, 127] as int8 (-128 is never drawn)."""
+    return torch.randint(-127, 128, tuple(shape), generator=_gen(seed, stream), dtype=torch.int8)
+
+
+@dataclass
+class Case:
+    """One workload instance: CPU tensors plus scalar arguments."""
+
+    name: str
+    tensors: dict = field(default_factory=dict)
+    eps: float = EPS
+    dims: dict = field(default_factory=dict)
+
+    def __getitem__(self, k):
+        return self.tensors[k]
+
+
+def norm_linear_case(T: int, K: int, N: int, seed: int = 0, gamma: bool = True,
+                     w_dtype: str = "bf16", name: str | None = None) -> Case:
+    """x[T,K] bf16, optional gamma[K] bf16, W[N,K] (bf16 or fp32)."""
+    wdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[w_dtype]
+    t = {
+        "x": normal((T, K), 1.0, seed, _S_X),
+        "gamma": uniform((K,), 0.5, 1.5, seed, _S_GAMMA) if gamma else None,
+        "W": normal((N, K), 1.0 / math.sqrt(K), seed, _S_W, dtype=wdt),
+    }
+    return Case(name or f"norm_linear_T{T}_K{K}_N{N}_{w_dtype}", t, EPS, {"T": T, "K": K, "N": N})
+
+
+def int8_case(T: int, K: int, N: int, seed: int = 0, gamma: bool = True, name: str | None = None) -> Case:
+    """x[T,K] bf16, optional gamma[K] bf16, Wq[N,K] int8 in [-127,127], w_scale[N] fp32."""
+    t = {
+        "x": normal((T, K), 1.0, seed, _S_X),
+        "gamma": uniform((K,), 0.5, 1.5, seed, _S_GAMMA) if gamma else None,
+        "Wq": int8_uniform((N, K), seed, _S_W),
+        "w_scale": uniform((N,), 1e-3, 1e-2, seed, _S_WSCALE, dtype=torch.float32),
+    }
+    return Case(name or f"int8_T{T}_K{K}_N{N}", t, EPS, {"T": T, "K": K, "N": N})
+
+
+def chain_case(T: int, K: int, R: int, N: int, seed: int = 0, gamma: bool = True,
+               name: str | None = None) -> Case:
+    """x[T,K] -> W_a[R,K] -> RMSNorm(R, gamma) -> W_b[N,R]; all bf16."""
+    t = {
+        "x": normal((T, K), 1.0, seed, _S_X),
+        "W_a": normal((R, K), 1.0 / math.sqrt(K), seed, _S_WA),
+        "gamma": uniform((R,), 0.5, 1.5, seed, _S_GAMMA) if gamma else None,
+        "W_b": normal((N, R), 1.0 / math.sqrt(R), seed, _S_WB),
+    }
+    return Case(name or f"chain_T{T}_K{K}_R{R}_N{N}", t, EPS, {"T": T, "K": K, "R": R, "N": N})
+
+
+# The five workloads, by what they are.
+def small_norm_linear(seed: int = 0) -> Case:
+    """bf16 RMSNorm + Linear, T=8 tokens, K=256, N=128."""
+    return norm_linear_case(8, 256, 128, seed, name="norm_linear_bf16_T8_K256_N128")
+
+
+def preattn_qkv(T: int = 4096, seed: int = 0) -> Case:
+    """Pre-attention norm + fused QKV projection, K=4096, N=6144 (Q 4096 + K 1024 + V 1024)."""
+    return norm_linear_case(T, 4096, 6144, seed, name=f"preattn_qkv_bf16_T{T}_K4096_N6144")
+
+
+def int8_w8a8(seed: int = 0) -> Case:
+    """INT8 W8A8 norm + linear, T=2048, K=4096, N=4096."""
+    return int8_case(2048, 4096, 4096, seed, name="int8_w8a8_T2048_K4096_N4096")
+
+
+def mla_q_chain(seed: int = 0) -> Case:
+    """Low-rank query chain x[1024,7168] -> W_a[1536,7168] -> norm -> W_b[24576,1536]."""
+    return chain_case(1024, 7168, 1536, 24576, seed, name="mla_q_chain_T1024_K7168_R1536_N24576")
+
+
+def skinny_fp32(seed: int = 0) -> Case:
+    """Large-reduction tiny-width norm + linear, no gamma, T=512, K=28672, N=24, fp32 W."""
+    return norm_linear_case(512, 28672, 24, seed, gamma=False, w_dtype="fp32",
+                            name="skinny_fp32_T512_K28672_N24")

@@ -1,0 +1,414 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test checks the oracle against something it does not compute itself:
+exact rational arithmetic, closed forms, invariants of the definition, special
+cases that reduce to a known answer, independent library conversions, and a
+hand-derived fixture (tests/golden/int8_quant_ties.txt).  The pages print no
+worked numeric example, so no test compares against page values.
+"""
+from __future__ import annotations
+
+import decimal
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic
+from tests._util import bits, fraction_to_f32, ulp_diff
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def _rand_bf16_rows(T, K, seed=0, std=1.0):
+    return bits(synthetic.normal((T, K), std, seed, 99))
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversions
+# ---------------------------------------------------------------------------
+def test_bf16_rne_against_nearest_neighbour():
+    """Round-to-nearest-even chosen by exact distance to the two bf16 neighbours."""
+    raw = RNG.integers(0, 2**32, size=4000, dtype=np.uint64).astype(np.uint32)
+    # add exact ties (low half = 0x8000) with both parities of the kept lsb
+    ties = (raw[:1000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    vals = np.concatenate([raw, ties]).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) < 3e38)]
+    got = O.f32_to_bf16_bits(vals)
+    for v, g in zip(vals[:3000], got[:3000]):
+        u = int(np.float32(v).view(np.uint32))
+        lo = u & 0xFFFF0000
+        hi = lo + 0x10000
+        flo = Fraction(float(np.uint32(lo).view(np.float32)))
+        fhi = Fraction(float(np.uint32(hi).view(np.float32)))
+        fv = Fraction(float(v))
+        dlo, dhi = abs(fv - flo), abs(fhi - fv)
+        if dlo < dhi or (dlo == dhi and ((lo >> 16) & 1) == 0):
+            want = lo >> 16
+        else:
+            want = hi >> 16
+        assert int(g) == want, hex(u)
+
+
+def test_bf16_conversions_match_torch():
+    vals = (RNG.standard_normal(20000) * 10.0 ** RNG.integers(-20, 20, 20000)).astype(np.float32)
+    ref = bits(torch.from_numpy(vals).to(torch.bfloat16))
+    assert np.array_equal(O.f32_to_bf16_bits(vals), ref)
+    b = RNG.integers(0, 2**16, 5000, dtype=np.uint64).astype(np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]  # finite only
+    want = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.bf16_bits_to_f32(b), want)
+
+
+def test_bf16_nan_stays_nan():
+    v = np.array([np.nan, -np.nan], dtype=np.float32)
+    back = O.bf16_bits_to_f32(O.f32_to_bf16_bits(v))
+    assert np.isnan(back).all()
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+def _exact_rstd(x_row_f32, eps):
+    """rstd from exact rationals (sum of squares exact) and 60-digit decimals,
+    following the stated roundings: fl(S), fl(S*fl(1/K)), fl(ms+eps)."""
+    K = len(x_row_f32)
+    S = sum(Fraction(float(v)) ** 2 for v in x_row_f32)
+    S32 = fraction_to_f32(S)
+    c = fraction_to_f32(Fraction(1, K))
+    ms = fraction_to_f32(Fraction(float(S32)) * Fraction(float(c)))
+    var = fraction_to_f32(Fraction(float(ms)) + Fraction(float(np.float32(eps))))
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        r = decimal.Decimal(1) / decimal.Decimal(float(var)).sqrt()
+    return Fraction(r)
+
+
+@pytest.mark.parametrize("K", [256, 1536, 4104])
+def test_rstd_within_one_ulp_of_exact(K):
+    x = _rand_bf16_rows(24, K, seed=K)
+    _, rstd = O.rms_norm_rows(x, None, 1e-6)
+    xf = O.bf16_bits_to_f32(x)
+    for t in range(x.shape[0]):
+        exact = _exact_rstd(xf[t], 1e-6)
+        assert ulp_diff(rstd[t], fraction_to_f32(exact)) <= 1
+
+
+def test_rsqrt_and_sqrt_div_variants_agree():
+    """AT-10 page section 3: variant A (rsqrt) and B (sqrt + div) agree."""
+    for K in (8, 256, 1000, 4096):
+        x = _rand_bf16_rows(2500 if K <= 1000 else 300, K, seed=K + 1)
+        _, ra = O.rms_norm_rows(x, None, 1e-6, variant="A")
+        _, rb = O.rms_norm_rows(x, None, 1e-6, variant="B")
+        assert ulp_diff(ra, rb).max() <= 1
+
+
+def test_division_form_matches_product_form():
+    """Golden ``rms_norm_new`` divides by sqrt; the kernel multiplies by rstd."""
+    x = _rand_bf16_rows(64, 4096, seed=7)
+    n, _ = O.rms_norm_rows(x, None, 1e-6)
+    nd = O.rms_norm_rows_golden_div(x, 1e-6)
+    assert ulp_diff(n, nd).max() <= 2
+
+
+def test_mla_ordering_equivalent():
+    """1/D applied per element before the sum (MLA code) vs after (variant A)."""
+    for K in (256, 4096):  # power of two: scaling by 1/K is exact
+        x = _rand_bf16_rows(200, K, seed=K + 3)
+        _, r1 = O.rms_norm_rows(x, None, 1e-6)
+        _, r2 = O.rms_norm_rows_mla_order(x, 1e-6)
+        assert np.array_equal(r1, r2)
+    x = _rand_bf16_rows(200, 1536, seed=11)
+    _, r1 = O.rms_norm_rows(x, None, 1e-6)
+    _, r2 = O.rms_norm_rows_mla_order(x, 1e-6)
+    assert ulp_diff(r1, r2).max() <= 4
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5, 3.0])
+def test_unit_rms_invariant(eps):
+    """With gamma = 1: rms(n) = sqrt(ms / (ms + eps)); exactly 1 when eps = 0."""
+    x = _rand_bf16_rows(128, 2048, seed=5)
+    n, _ = O.rms_norm_rows(x, None, eps)
+    xf = O.bf16_bits_to_f32(x).astype(np.float64)
+    ms = np.mean(xf * xf, axis=1)
+    want = np.sqrt(ms / (ms + eps))
+    got = np.sqrt(np.mean(n.astype(np.float64) ** 2, axis=1))
+    assert np.max(np.abs(got / want - 1.0)) < 5e-7
+
+
+def test_scale_invariance_eps0():
+    """eps = 0: scaling x by 2^p leaves n unchanged bit for bit."""
+    x = _rand_bf16_rows(64, 512, seed=9)
+    n0, _ = O.rms_norm_rows(x, None, 0.0)
+    xf = O.bf16_bits_to_f32(x)
+    for p in (-6, -1, 3, 9):
+        xs = O.f32_to_bf16_bits((xf * np.float32(2.0**p)).astype(np.float32))
+        n1, _ = O.rms_norm_rows(xs, None, 0.0)
+        assert np.array_equal(n0, n1)
+
+
+@pytest.mark.parametrize("c", [1.0, -0.375, 3.25, 1e-3])
+@pytest.mark.parametrize("eps", [1e-6, 0.25])
+def test_constant_row_closed_form(c, eps):
+    """x_k = c for all k: n = c / sqrt(c^2 + eps)."""
+    cb = O.f32_to_bf16_bits(np.array([c], dtype=np.float32))[0]
+    cf = float(O.bf16_bits_to_f32(np.array([cb]))[0])
+    x = np.full((1, 64), cb, dtype=np.uint16)
+    n, _ = O.rms_norm_rows(x, None, eps)
+    want = np.float32(cf / np.sqrt(cf * cf + float(np.float32(eps))))
+    assert ulp_diff(n[0], np.full(64, want, dtype=np.float32)).max() <= 2
+
+
+def test_gamma_scales_columns():
+    """gamma = 2^j_k per column multiplies column k exactly and leaves rstd alone."""
+    K = 64
+    x = _rand_bf16_rows(16, K, seed=21)
+    j = (np.arange(K) % 7) - 3
+    g = O.f32_to_bf16_bits((2.0 ** j).astype(np.float32))
+    n0, r0 = O.rms_norm_rows(x, None, 1e-6)
+    n1, r1 = O.rms_norm_rows(x, g, 1e-6)
+    assert np.array_equal(r0, r1)
+    assert np.array_equal(n1, (n0 * (2.0 ** j)[None, :]).astype(np.float32))
+
+
+def test_given_rstd_is_used():
+    x = _rand_bf16_rows(4, 32, seed=2)
+    r = np.array([0.5, 1.0, 2.0, 0.25], dtype=np.float32)
+    n, r2 = O.rms_norm_rows(x, None, 1e-6, rstd=r)
+    assert np.array_equal(r2, r)
+    assert np.array_equal(n, (O.bf16_bits_to_f32(x) * r[:, None]).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# projections
+# ---------------------------------------------------------------------------
+def _exact_proj(a_f32, w_f32):
+    T, K = a_f32.shape
+    N = w_f32.shape[0]
+    out = np.zeros((T, N), dtype=np.float32)
+    af = [[Fraction(float(v)) for v in row] for row in a_f32]
+    wf = [[Fraction(float(v)) for v in row] for row in w_f32]
+    for t in range(T):
+        for j in range(N):
+            out[t, j] = fraction_to_f32(sum(af[t][k] * wf[j][k] for k in range(K)))
+    return out
+
+
+@pytest.mark.parametrize("T,K,N", [(3, 16, 5), (5, 40, 7), (2, 64, 3)])
+def test_bf16_projection_is_correctly_rounded(T, K, N):
+    case = synthetic.norm_linear_case(T, K, N, seed=T * K + N)
+    x, g, W = bits(case["x"]), bits(case["gamma"]), bits(case["W"])
+    y32, ybf, _ = O.rmsnorm_linear_bf16(x, g, 1e-6, W)
+    n, _ = O.rms_norm_rows(x, g, 1e-6)
+    a = O.bf16_bits_to_f32(O.f32_to_bf16_bits(n))
+    want = _exact_proj(a, O.bf16_bits_to_f32(W))
+    assert np.array_equal(y32, want)
+    assert np.array_equal(ybf, O.f32_to_bf16_bits(want))
+
+
+def test_bf16_projection_identity_weight():
+    """W = I: y = bf16(n) exactly."""
+    K = 48
+    x = _rand_bf16_rows(6, K, seed=4)
+    g = bits(synthetic.uniform((K,), 0.5, 1.5, 0, 7))
+    I = O.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    y32, ybf, _ = O.rmsnorm_linear_bf16(x, g, 1e-6, I)
+    n, _ = O.rms_norm_rows(x, g, 1e-6)
+    assert np.array_equal(ybf, O.f32_to_bf16_bits(n))
+
+
+def test_bf16_projection_selects_weight_rows():
+    """W[j, k_j] = 1 (N != K): y[:, j] = a[:, k_j] -- catches a transposed W."""
+    T, K, N = 5, 32, 9
+    x = _rand_bf16_rows(T, K, seed=6)
+    kj = RNG.permutation(K)[:N]
+    Wf = np.zeros((N, K), dtype=np.float32)
+    Wf[np.arange(N), kj] = 1.0
+    y32, _, _ = O.rmsnorm_linear_bf16(x, None, 1e-6, O.f32_to_bf16_bits(Wf))
+    n, _ = O.rms_norm_rows(x, None, 1e-6)
+    a = O.bf16_bits_to_f32(O.f32_to_bf16_bits(n))
+    assert np.array_equal(y32, a[:, kj])
+
+
+def test_bf16_projection_square_permutation():
+    """Square W = permutation matrix P (not symmetric): y = a @ P.T, so
+    y[:, j] = a[:, perm[j]]; a transposed W would give the inverse permutation."""
+    K = 16
+    x = _rand_bf16_rows(4, K, seed=8)
+    perm = np.roll(np.arange(K), 3)
+    Wf = np.zeros((K, K), dtype=np.float32)
+    Wf[np.arange(K), perm] = 1.0
+    y32, _, _ = O.rmsnorm_linear_bf16(x, None, 1e-6, O.f32_to_bf16_bits(Wf))
+    n, _ = O.rms_norm_rows(x, None, 1e-6)
+    a = O.bf16_bits_to_f32(O.f32_to_bf16_bits(n))
+    assert np.array_equal(y32, a[:, perm])
+
+
+def test_fp32_projection_exact_and_keeps_fp32():
+    """mhc_pre FP32 compute: normed rows are not cast to bf16."""
+    T, K, N = 3, 24, 4
+    case = synthetic.norm_linear_case(T, K, N, seed=3, gamma=False, w_dtype="fp32")
+    x, W = bits(case["x"]), case["W"].numpy()
+    y32, _ = O.rmsnorm_linear_fp32w(x, None, 1e-6, W)
+    n, _ = O.rms_norm_rows(x, None, 1e-6)
+    assert np.array_equal(y32, _exact_proj(n, W))
+    yI, _ = O.rmsnorm_linear_fp32w(x, None, 1e-6, np.eye(K, dtype=np.float32))
+    assert np.array_equal(yI, n)
+    assert not np.array_equal(n, O.bf16_bits_to_f32(O.f32_to_bf16_bits(n)))
+
+
+# ---------------------------------------------------------------------------
+# int8 W8A8
+# ---------------------------------------------------------------------------
+def _parse_fraction(tok):
+    if "/" in tok:
+        a, b = tok.split("/")
+        return float(Fraction(a) / Fraction(b))
+    return float(tok)
+
+
+def _golden_cases(path):
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {"name": vals[0], "x": [], "q": [], "x_scale": []}
+            cases.append(cur)
+        elif key in ("K",):
+            cur[key] = int(vals[0])
+        elif key == "eps":
+            cur[key] = float(vals[0])
+        elif key == "gamma":
+            cur[key] = [_parse_fraction(v) for v in vals]
+        elif key in ("x", "q"):
+            cur[key].append([_parse_fraction(v) for v in vals])
+        elif key == "x_scale":
+            cur[key].append(_parse_fraction(vals[0]))
+    return cases
+
+
+def test_int8_quant_golden_ties():
+    for c in _golden_cases(os.path.join(GOLDEN, "int8_quant_ties.txt")):
+        x = O.f32_to_bf16_bits(np.array(c["x"], dtype=np.float32))
+        g = O.f32_to_bf16_bits(np.array(c["gamma"], dtype=np.float32))
+        # the fixture's values must be bf16-exact
+        assert np.array_equal(O.bf16_bits_to_f32(x), np.array(c["x"], dtype=np.float32))
+        assert np.array_equal(O.bf16_bits_to_f32(g), np.array(c["gamma"], dtype=np.float32))
+        n, _ = O.rms_norm_rows(x, g, c["eps"])
+        q, xs, _ = O.quant_rows(n)
+        assert np.array_equal(q, np.array(c["q"], dtype=np.int8)), c["name"]
+        assert np.array_equal(xs, np.array(c["x_scale"], dtype=np.float32)), c["name"]
+
+
+def test_int8_saturation_rule():
+    n = np.array([[1.0, -1.0, 0.5, 0.63, -0.0]], dtype=np.float32)
+    q = O.quant_values(n, np.array([[200.0]], dtype=np.float32))
+    assert q.tolist() == [[127, -127, 100, 126, 0]]
+
+
+def test_int8_quant_invariants():
+    case = synthetic.int8_case(64, 512, 8, seed=1)
+    n, _ = O.rms_norm_rows(bits(case["x"]), bits(case["gamma"]), 1e-6)
+    q, xs, s = O.quant_rows(n)
+    assert q.dtype == np.int8 and np.abs(q.astype(int)).max() <= 127
+    amax_idx = np.argmax(np.abs(n), axis=1)
+    assert np.array_equal(np.abs(q[np.arange(64), amax_idx]).astype(int), np.full(64, 127))
+    # reconstruction error is at most half a step (plus fp32 slack)
+    err = np.abs(q.astype(np.float64) * xs[:, None] - n)
+    assert np.all(err <= xs[:, None] * (0.5 + 1e-5))
+    # scale multiplier and dequant scale are the pages' 127/amax and amax/127
+    amax = np.abs(n).max(axis=1).astype(np.float64)
+    assert np.max(np.abs(s / (127.0 / amax) - 1)) <= 2**-24
+    assert np.max(np.abs(xs / (amax / 127.0) - 1)) <= 2**-24
+
+
+def test_int8_gemm_brute_force_and_unit_rows():
+    T, K, N = 4, 32, 6
+    q = RNG.integers(-127, 128, (T, K)).astype(np.int8)
+    Wq = RNG.integers(-127, 128, (N, K)).astype(np.int8)
+    acc = O.int8_gemm(q, Wq)
+    for t in range(T):
+        for j in range(N):
+            assert acc[t, j] == sum(int(q[t, k]) * int(Wq[j, k]) for k in range(K))
+    sel = RNG.permutation(K)[:N]
+    E = np.zeros((N, K), dtype=np.int8)
+    E[np.arange(N), sel] = 1
+    assert np.array_equal(O.int8_gemm(q, E), q[:, sel].astype(np.int64))
+
+
+def test_int8_gemm_overflow_detected():
+    K = 133160  # K * 127 * 127 > 2^31 - 1
+    q = np.full((1, K), 127, dtype=np.int8)
+    with pytest.raises(OverflowError):
+        O.int8_gemm(q, q)
+
+
+def test_dequant_closed_form():
+    """w_scale = 2^-k, x_scale exact: y = float(acc) * x_scale * w_scale exactly,
+    with the int -> fp32 cast rounding acc above 2^24."""
+    acc = np.array([[3, -5, 2**24 + 1, 2**25 + 3]], dtype=np.int64)
+    xs = np.array([0.015625], dtype=np.float32)
+    ws = np.array([2.0**-3, 2.0**-7, 2.0**-1, 1.0], dtype=np.float32)
+    y = O.dequant(acc, xs, ws)
+    want = np.array([[3 / 512, -5 / 8192, 2**24 / 128, (2**25 + 4) / 64]], dtype=np.float32)
+    assert np.array_equal(y, want)
+
+
+def test_dequant_rounding_order():
+    """SK-14 page, QuantMatMulReduceSum: scale_mul = x1_scale * x2_scale is
+    formed first (one rounding), then acc_fp32 * scale_mul (one rounding).
+    Expected values from exact rationals with those two roundings."""
+    acc = RNG.integers(-2**20, 2**20, (6, 40)).astype(np.int64)
+    xs = RNG.uniform(1e-3, 1e-1, 6).astype(np.float32)
+    ws = RNG.uniform(1e-3, 1e-2, 40).astype(np.float32)
+    y = O.dequant(acc, xs, ws)
+    diff = 0
+    for t in range(6):
+        for j in range(40):
+            sm = fraction_to_f32(Fraction(float(xs[t])) * Fraction(float(ws[j])))
+            want = fraction_to_f32(Fraction(int(acc[t, j])) * Fraction(float(sm)))
+            assert y[t, j] == want
+            step = fraction_to_f32(Fraction(int(acc[t, j])) * Fraction(float(xs[t])))
+            other = fraction_to_f32(Fraction(float(step)) * Fraction(float(ws[j])))
+            diff += int(other != want)
+    assert diff > 0  # the two orders are distinguishable on this data
+
+
+def test_int8_zero_row():
+    x = np.zeros((2, 16), dtype=np.uint16)
+    Wq = RNG.integers(-127, 128, (3, 16)).astype(np.int8)
+    r = O.rmsnorm_linear_int8(x, None, 1e-6, Wq, np.ones(3, dtype=np.float32))
+    assert (r["q"] == 0).all() and (r["x_scale"] == 0).all() and (r["y32"] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# chain
+# ---------------------------------------------------------------------------
+def test_chain_identity_stages():
+    """W_a = I: q_a = x, qr = bf16(norm(x)); W_b = I: y = qr."""
+    K = 32
+    x = _rand_bf16_rows(5, K, seed=13)
+    g = bits(synthetic.uniform((K,), 0.5, 1.5, 0, 8))
+    I = O.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    r = O.norm_proj_chain(x, I, g, 1e-6, I)
+    assert np.array_equal(r["qa"], x)
+    n, _ = O.rms_norm_rows(x, g, 1e-6)
+    assert np.array_equal(r["qr"], O.f32_to_bf16_bits(n))
+    assert np.array_equal(r["y_bf16"], r["qr"])
+
+
+def test_chain_stage_one_exact():
+    case = synthetic.chain_case(3, 24, 16, 5, seed=2)
+    x, Wa, g, Wb = (bits(case[k]) for k in ("x", "W_a", "gamma", "W_b"))
+    r = O.norm_proj_chain(x, Wa, g, 1e-6, Wb)
+    qa32 = _exact_proj(O.bf16_bits_to_f32(x), O.bf16_bits_to_f32(Wa))
+    assert np.array_equal(r["qa"], O.f32_to_bf16_bits(qa32))
+    y = _exact_proj(O.bf16_bits_to_f32(r["qr"]), O.bf16_bits_to_f32(Wb))
+    assert np.array_equal(r["y32"], y)
