@@ -1,0 +1,167 @@
+/*
+ * rnl.h -- C ABI of the MI355X (gfx950) fused RMSNorm -> Linear projection library.
+ *
+ * The operation (AT-10 page "PyPTO-Gym operator design pattern AT-10: RMSNorm +
+ * Linear fused (V->C layout)", section 2 "CV layout and standard compute flow"):
+ * per token t,
+ *     xf     = float(x[t, :])
+ *     ms     = fl( fl(sum_k xf^2) * fl(1/K) )         (fp32 reduction)
+ *     rstd   = 1 / sqrt(ms + eps)                      (section 3, variant B)
+ *     n[k]   = fl( fl(xf[k] * rstd) * float(gamma[k]) ) (gamma optional)
+ *     y[t,:] = matmul(bf16(n), W, b_trans=True)        (W stored [N, K])
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory, row-major and contiguous, owned by
+ *     the caller; outputs are preallocated by the caller (SK-14 page, the host
+ *     wrapper preallocates outputs).  Outputs must not alias inputs.
+ *   - Calls are asynchronous: they enqueue kernels on `stream` (a hipStream_t;
+ *     NULL means the default stream) and return.  Nothing is allocated and no
+ *     host synchronisation happens inside a call.
+ *   - Return value: RNL_OK (0) when the work was enqueued, else a negative
+ *     RNL_ERR_* code.  Arguments are validated before any HIP call, so an
+ *     invalid call touches no memory.  rnl_last_error() gives a detail string
+ *     for the calling thread.  No exception or abort crosses the ABI.
+ *   - Sizes are int64_t and must be >= 1.  K must be a multiple of 8 (16-byte
+ *     vectors of bf16) and at most 2^20; T and N at most 2^24.  Any T and N
+ *     in range are accepted: partial tiles are masked (the pages'
+ *     valid_shape tails).
+ *   - Alignment: x, gamma, W, Wq, W_a, W_b, y, qr_out, xq_out must be 16-byte
+ *     aligned; rstd_out, x_scale_out, w_scale 4-byte; workspace 256-byte.
+ *   - eps must be finite and >= 0; it is used as the fp32 value fl(eps).
+ *   - `workspace` is scratch device memory of at least the size the matching
+ *     *_workspace_bytes() query returns for the same arguments (0 means none
+ *     is needed and the pointer may be NULL).  Its contents on entry do not
+ *     matter and are undefined afterwards.
+ *   - Environment variable RNL_VARIANT (read at every call) may force a kernel
+ *     family for testing: "decode" (T <= 16 only) or "gemm"; anything else,
+ *     or unset, lets the shape decide.
+ */
+#ifndef RNL_H
+#define RNL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point below is exported from librnl.so; nothing else is. */
+#define RNL_API __attribute__((visibility("default")))
+
+/* dtype codes */
+#define RNL_BF16 1
+#define RNL_FP32 2
+#define RNL_INT8 3
+#define RNL_INT32 4
+
+/* status codes */
+#define RNL_OK 0
+#define RNL_ERR_NULL (-1)      /* a required pointer is NULL                    */
+#define RNL_ERR_SHAPE (-2)     /* size <= 0, K % 8 != 0, or a size limit exceeded */
+#define RNL_ERR_DTYPE (-3)     /* unsupported dtype code or combination          */
+#define RNL_ERR_ARG (-4)       /* eps negative or not finite                     */
+#define RNL_ERR_ALIGN (-5)     /* a pointer is not aligned as required           */
+#define RNL_ERR_WORKSPACE (-6) /* workspace NULL or smaller than required        */
+#define RNL_ERR_HIP (-7)       /* a HIP runtime call or kernel launch failed     */
+
+/*
+ * rmsnorm_linear_bf16 -- fused RMSNorm -> Linear (AT-10).
+ *
+ * AT-10 page, section 2 (compute flow), section 3 (AT-03 RMSNorm: fp32 inside,
+ * optional gamma, optional rstd output), section 4 (AT-09 BF16 mode:
+ * matmul(x, w, BF16, b_trans=True)).  With w_dtype == RNL_FP32 this is the
+ * SK-03 page's mhc_pre variant ("large reduction x tiny output width", FP32
+ * compute): the normed rows stay fp32 and are multiplied by an fp32 weight.
+ *
+ *   x         [T, K] bf16 activations.
+ *   gamma     [K] bf16 scale, or NULL for no gamma (has_gamma = false).
+ *   eps       added to the mean square before the root.
+ *   W         [N, K] weight, row n holds output column n (b_trans = True);
+ *             bf16 when w_dtype == RNL_BF16, fp32 when w_dtype == RNL_FP32.
+ *   y         [T, N] output, bf16 (out_dtype RNL_BF16) or fp32 (RNL_FP32).
+ *             bf16 weights: y = round_bf16(fp32 accumulation of
+ *             bf16(n) * W).  fp32 weights: y = fp32 accumulation of n * W.
+ *   rstd_out  [T] fp32 per-token rstd (AT-03 output_rstd), or NULL.
+ *   With fp32 weights the normed rows are not rounded to bf16, and the
+ *   reduction over K is split across workgroups and added in a fixed order,
+ *   so repeated calls give identical results.
+ *
+ * Errors: RNL_ERR_NULL (x, W or y NULL), RNL_ERR_SHAPE, RNL_ERR_DTYPE
+ * (w_dtype not BF16/FP32, out_dtype not BF16/FP32), RNL_ERR_ARG,
+ * RNL_ERR_ALIGN, RNL_ERR_WORKSPACE, RNL_ERR_HIP.
+ */
+RNL_API int rmsnorm_linear_bf16(const void* x, const void* gamma, float eps, const void* W, int w_dtype,
+                        void* y, int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes rmsnorm_linear_bf16 needs for these arguments (0 = none). */
+RNL_API size_t rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t N, int w_dtype,
+                                           int out_dtype);
+
+/*
+ * rmsnorm_linear_int8 -- fused RMSNorm -> per-token int8 quant -> int8 GEMM ->
+ * dequant (AT-11 = AT-10 with AT-09's INT8 W8A8 mode).
+ *
+ * AT-10 page, section 4: x_int8, x_scale = AT-05(normed); y_int32 =
+ * matmul(x_int8, w_int8, INT32); y = AT-06(y_int32, x_scale, w_scale).
+ * AT-05 (AT-10 page section 4; SK-03 page quant variant, common.py quant):
+ * amax[t] = max_k |n[t,k]|, s = fl(127 / amax), q = saturate_+-127(rint(fl(n*s)))
+ * with round-half-to-even, x_scale = fl(amax / 127); an all-zero row gives
+ * q = 0 and x_scale = 0.  AT-06 in the order of the SK-14 page's
+ * QuantMatMulReduceSum: y = fl(float(acc) * fl(x_scale[t] * w_scale[n])).
+ *
+ *   x, gamma, eps  as in rmsnorm_linear_bf16 (normed rows are fp32, not bf16).
+ *   Wq        [N, K] int8 weight, values in [-127, 127].
+ *   w_scale   [N] fp32 per-output-channel weight scale.
+ *   y         [T, N]: bf16 or fp32 dequantised output, or, with out_dtype ==
+ *             RNL_INT32, the raw int32 accumulators acc[t, n].
+ *   xq_out    [T, K] int8 quantised activations, or NULL.
+ *   x_scale_out [T] fp32 dequant scale amax/127, or NULL.
+ *   rstd_out  [T] fp32, or NULL.
+ *   K must be a multiple of 16 (16-byte int8 vectors) and at most 133144, so
+ *   that |acc| <= K * 127 * 127 fits int32.
+ *
+ * Errors: as rmsnorm_linear_bf16 (w_scale and Wq are required).
+ */
+RNL_API int rmsnorm_linear_int8(const void* x, const void* gamma, float eps, const int8_t* Wq,
+                        const float* w_scale, void* y, int out_dtype, int8_t* xq_out,
+                        float* x_scale_out, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+RNL_API size_t rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype);
+
+/*
+ * norm_proj_chain -- two-stage low-rank projection q_a_proj -> RMSNorm -> q_b_proj.
+ *
+ * AT-10 page, section 5 (MLAProlog: q = matmul(x_tile, wq_a, BF16);
+ * qr = rms_norm(q) * gamma_cq; qr = cast(qr, BF16); assemble(qr, qr_out);
+ * q = matmul(qr, wq_b, BF16)) and SK-14 page section 5, orchestration mode 1
+ * (serial pipeline).
+ *
+ *   x       [T, K] bf16.
+ *   W_a     [R, K] bf16 (b_trans).   q_a = round_bf16(x . W_a^T)   [T, R]
+ *   gamma   [R] bf16 or NULL; eps.   qr  = round_bf16(RMSNorm(q_a) * gamma)
+ *   W_b     [N, R] bf16 (b_trans).   y   = round_bf16(qr . W_b^T)  [T, N]
+ *   qr_out  [T, R] bf16, required (the normed low-rank query).
+ *   y       [T, N] bf16.
+ *   rstd_out [T] fp32 rstd of the q_a rows, or NULL.
+ *   R must be a multiple of 8.
+ */
+RNL_API int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps, const void* W_b,
+                    void* qr_out, void* y, float* rstd_out, int64_t T, int64_t K, int64_t R,
+                    int64_t N, void* workspace, size_t workspace_bytes, void* stream);
+
+RNL_API size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N);
+
+/* Static description of a status code. */
+RNL_API const char* rnl_status_str(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+RNL_API const char* rnl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNL_H */

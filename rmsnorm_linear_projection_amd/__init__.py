@@ -1,0 +1,239 @@
+"""Fused RMSNorm -> Linear projection on MI355X (gfx950).
+
+Thin Python binding of ``librnl.so`` (the C ABI declared in include/rnl.h).
+It only marshals arguments: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or cannot be loaded, every
+call raises.
+
+Entry points (same names as the C ABI):
+
+* :func:`rmsnorm_linear_bf16` -- RMSNorm -> bf16 cast -> matmul(W[N,K], b_trans)
+  (fp32 weights: the normed rows stay fp32, the large-reduction split-K path);
+* :func:`rmsnorm_linear_int8` -- RMSNorm -> per-token int8 quant -> int8 GEMM ->
+  dequant;
+* :func:`norm_proj_chain` -- q_a = x W_a^T -> RMSNorm -> qr -> y = qr W_b^T.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "rmsnorm_linear_bf16",
+    "rmsnorm_linear_int8",
+    "norm_proj_chain",
+    "workspace_bytes",
+    "load_library",
+    "RnlError",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librnl.so")
+
+# codes from include/rnl.h
+RNL_BF16, RNL_FP32, RNL_INT8, RNL_INT32 = 1, 2, 3, 4
+_DTYPE_CODE = {torch.bfloat16: RNL_BF16, torch.float32: RNL_FP32, torch.int8: RNL_INT8, torch.int32: RNL_INT32}
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+
+class RnlError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"rnl status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load librnl.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m rmsnorm_linear_projection_amd.build_lib` "
+            "or __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.rmsnorm_linear_bf16.argtypes = [_c_p, _c_p, ctypes.c_float, _c_p, ctypes.c_int, _c_p, ctypes.c_int,
+                                        _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+    lib.rmsnorm_linear_bf16.restype = ctypes.c_int
+    lib.rmsnorm_linear_bf16_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
+    lib.rmsnorm_linear_bf16_workspace_bytes.restype = ctypes.c_size_t
+    lib.rmsnorm_linear_int8.argtypes = [_c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p,
+                                        _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+    lib.rmsnorm_linear_int8.restype = ctypes.c_int
+    lib.rmsnorm_linear_int8_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.c_int]
+    lib.rmsnorm_linear_int8_workspace_bytes.restype = ctypes.c_size_t
+    lib.norm_proj_chain.argtypes = [_c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                                    _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+    lib.norm_proj_chain.restype = ctypes.c_int
+    lib.norm_proj_chain_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64]
+    lib.norm_proj_chain_workspace_bytes.restype = ctypes.c_size_t
+    lib.rnl_status_str.argtypes = [ctypes.c_int]
+    lib.rnl_status_str.restype = ctypes.c_char_p
+    lib.rnl_last_error.argtypes = []
+    lib.rnl_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load_library()
+        raise RnlError(rc, f"{lib.rnl_status_str(rc).decode()}: {lib.rnl_last_error().decode()}")
+
+
+def _dev_tensor(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+
+
+def _shape(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(nbytes: int, dev, given):
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        _dev_tensor(given, "workspace")
+        return given, given.numel() * given.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev), nbytes
+
+
+def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.bfloat16) -> int:
+    """Workspace a call needs: kind 'bf16' (T, K, N), 'int8' (T, K, N) or 'chain' (T, K, R, N)."""
+    lib = load_library()
+    if kind == "bf16":
+        return int(lib.rmsnorm_linear_bf16_workspace_bytes(*shape, _DTYPE_CODE[w_dtype], _DTYPE_CODE[out_dtype]))
+    if kind == "int8":
+        return int(lib.rmsnorm_linear_int8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
+    if kind == "chain":
+        return int(lib.norm_proj_chain_workspace_bytes(*shape))
+    raise ValueError(kind)
+
+
+def rmsnorm_linear_bf16(x, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=None, y=None, workspace=None):
+    """y[T,N] = matmul(bf16(RMSNorm(x) * gamma), W[N,K], b_trans) -- AT-10.
+
+    ``W`` bf16 [N, K], or fp32 [N, K] for the fp32-compute variant.  ``gamma``
+    may be None.  ``rstd_out`` (fp32 [T]) receives the per-token rstd.
+    """
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(W, "W", (torch.bfloat16, torch.float32), 2)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    N = W.shape[0]
+    _shape(W.shape[1] == K, "W must be [N, K]")
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    wcode = _DTYPE_CODE[W.dtype]
+    ocode = _DTYPE_CODE[out_dtype]
+    if y is None:
+        y = torch.empty((T, N), dtype=out_dtype, device=x.device)
+    _dev_tensor(y, "y", out_dtype)
+    _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
+    with torch.cuda.device(x.device):
+        need = int(lib.rmsnorm_linear_bf16_workspace_bytes(T, K, N, wcode, ocode))
+        ws, ws_bytes = _workspace(need, x.device, workspace)
+        rc = lib.rmsnorm_linear_bf16(_ptr(x), _ptr(gamma), float(eps), _ptr(W), wcode, _ptr(y), ocode,
+                                     _ptr(rstd_out), T, K, N, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(rc)
+    return y
+
+
+def rmsnorm_linear_int8(x, gamma, eps, Wq, w_scale, out_dtype=torch.bfloat16, xq_out=None, x_scale_out=None,
+                        rstd_out=None, y=None, workspace=None):
+    """AT-11: RMSNorm -> per-token symmetric int8 quant -> int8 x int8 -> int32 ->
+    dequant with x_scale and w_scale.  ``out_dtype`` torch.int32 returns the raw
+    accumulators."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(Wq, "Wq", torch.int8, 2)
+    _dev_tensor(w_scale, "w_scale", torch.float32, 1)
+    _dev_tensor(xq_out, "xq_out", torch.int8)
+    _dev_tensor(x_scale_out, "x_scale_out", torch.float32)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    N = Wq.shape[0]
+    _shape(Wq.shape[1] == K, "Wq must be [N, K]")
+    _shape(w_scale.numel() == N, "w_scale must be [N]")
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(xq_out is None or xq_out.numel() == T * K, "xq_out must be [T, K]")
+    _shape(x_scale_out is None or x_scale_out.numel() >= T, "x_scale_out must hold T values")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    ocode = _DTYPE_CODE[out_dtype]
+    if y is None:
+        y = torch.empty((T, N), dtype=out_dtype, device=x.device)
+    _dev_tensor(y, "y", out_dtype)
+    _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
+    with torch.cuda.device(x.device):
+        need = int(lib.rmsnorm_linear_int8_workspace_bytes(T, K, N, ocode))
+        if xq_out is not None and x_scale_out is not None:
+            need = 0
+        ws, ws_bytes = _workspace(need, x.device, workspace)
+        rc = lib.rmsnorm_linear_int8(_ptr(x), _ptr(gamma), float(eps), _ptr(Wq), _ptr(w_scale), _ptr(y), ocode,
+                                     _ptr(xq_out), _ptr(x_scale_out), _ptr(rstd_out), T, K, N, _ptr(ws),
+                                     ws_bytes, _stream(x.device))
+    _check(rc)
+    return y
+
+
+def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None, workspace=None):
+    """q_a_proj -> RMSNorm -> q_b_proj (MLA low-rank query).  Returns (y, qr_out)."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(W_a, "W_a", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(W_b, "W_b", torch.bfloat16, 2)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    R = W_a.shape[0]
+    N = W_b.shape[0]
+    _shape(W_a.shape[1] == K, "W_a must be [R, K]")
+    _shape(W_b.shape[1] == R, "W_b must be [N, R]")
+    _shape(gamma is None or gamma.numel() == R, "gamma must be [R]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    if qr_out is None:
+        qr_out = torch.empty((T, R), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _dev_tensor(qr_out, "qr_out", torch.bfloat16)
+    _dev_tensor(y, "y", torch.bfloat16)
+    _shape(tuple(qr_out.shape) == (T, R), "qr_out must be [T, R]")
+    _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
+    with torch.cuda.device(x.device):
+        need = int(lib.norm_proj_chain_workspace_bytes(T, K, R, N))
+        ws, ws_bytes = _workspace(need, x.device, workspace)
+        rc = lib.norm_proj_chain(_ptr(x), _ptr(W_a), _ptr(gamma), float(eps), _ptr(W_b), _ptr(qr_out), _ptr(y),
+                                 _ptr(rstd_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(rc)
+    return y, qr_out

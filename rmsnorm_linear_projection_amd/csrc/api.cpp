@@ -1,0 +1,247 @@
+// C ABI of the fused RMSNorm -> Linear library: argument validation, workspace
+// sizing, kernel-family dispatch and launches.  Declarations and the contract
+// of every entry point are in include/rnl.h.
+#include "rnl.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return RNL_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RNL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxK_int8 = 133144;  // K * 127 * 127 <= 2^31 - 1
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 32-bit tile offsets in range
+constexpr int64_t kDecodeMaxT = 16;
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+enum Variant { V_AUTO, V_DECODE, V_GEMM };
+
+Variant forced_variant() {
+  const char* v = std::getenv("RNL_VARIANT");
+  if (v == nullptr) return V_AUTO;
+  if (std::strcmp(v, "decode") == 0) return V_DECODE;
+  if (std::strcmp(v, "gemm") == 0) return V_GEMM;
+  return V_AUTO;
+}
+
+// bf16 weights: T <= 16 streams the weight in one fused launch, larger T runs
+// the norm pre-pass and the tiled GEMM.
+bool use_decode(int64_t T) {
+  const Variant v = forced_variant();
+  if (v == V_DECODE) return T <= kDecodeMaxT;
+  if (v == V_GEMM) return false;
+  return T <= kDecodeMaxT;
+}
+
+int check_dims(int64_t T, int64_t K, int64_t N, int64_t maxK) {
+  if (T <= 0 || K <= 0 || N <= 0) return fail(RNL_ERR_SHAPE, "sizes must be >= 1 (T=%lld K=%lld N=%lld)", (long long)T, (long long)K, (long long)N);
+  if (K % 8 != 0) return fail(RNL_ERR_SHAPE, "K=%lld is not a multiple of 8", (long long)K);
+  if (K > maxK) return fail(RNL_ERR_SHAPE, "K=%lld exceeds the limit %lld", (long long)K, (long long)maxK);
+  if (T > kMaxDim || N > kMaxDim) return fail(RNL_ERR_SHAPE, "T and N must be <= 2^24");
+  return RNL_OK;
+}
+
+int check_eps(float eps) {
+  if (!std::isfinite(eps) || eps < 0.f) return fail(RNL_ERR_ARG, "eps must be finite and >= 0");
+  return RNL_OK;
+}
+
+#define RNL_TRY(expr)              \
+  do {                             \
+    int _rc = (expr);              \
+    if (_rc != RNL_OK) return _rc; \
+  } while (0)
+
+#define RNL_ALIGN(p, a, name)                                                          \
+  do {                                                                                 \
+    if ((p) != nullptr && !aligned((p), (a)))                                          \
+      return fail(RNL_ERR_ALIGN, "%s is not %d-byte aligned", name, (int)(a));          \
+  } while (0)
+
+size_t bf16_ws(int64_t T, int64_t K, int64_t N, int w_dtype) {
+  if (w_dtype == RNL_FP32) return rnl::skinny_workspace_bytes(T, K, N);
+  if (use_decode(T)) return 0;
+  return align256((size_t)T * (size_t)K * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rnl_status_str(int status) {
+  switch (status) {
+    case RNL_OK: return "ok";
+    case RNL_ERR_NULL: return "a required pointer is NULL";
+    case RNL_ERR_SHAPE: return "invalid or unsupported shape";
+    case RNL_ERR_DTYPE: return "unsupported dtype";
+    case RNL_ERR_ARG: return "invalid scalar argument";
+    case RNL_ERR_ALIGN: return "misaligned pointer";
+    case RNL_ERR_WORKSPACE: return "workspace missing or too small";
+    case RNL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* rnl_last_error(void) { return g_last_error; }
+
+size_t rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t N, int w_dtype,
+                                           int out_dtype) {
+  (void)out_dtype;
+  if (T <= 0 || K <= 0 || N <= 0) return 0;
+  return bf16_ws(T, K, N, w_dtype);
+}
+
+int rmsnorm_linear_bf16(const void* x, const void* gamma, float eps, const void* W, int w_dtype,
+                        void* y, int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "x, W and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK));
+  if (w_dtype != RNL_BF16 && w_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "w_dtype must be RNL_BF16 or RNL_FP32");
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(W, 16, "W");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  const size_t need = bf16_ws(T, K, N, w_dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+  const int ok_kind = out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32;
+  if (w_dtype == RNL_FP32) {
+    return hip_status(rnl::launch_skinny_fp32w(xb, gb, eps, static_cast<const float*>(W), y, ok_kind,
+                                               rstd_out, T, K, N, workspace, s),
+                      "skinny split-K launch");
+  }
+  const uint16_t* wb = static_cast<const uint16_t*>(W);
+  if (use_decode(T)) {
+    return hip_status(rnl::launch_decode_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, K, N, s),
+                      "decode launch");
+  }
+  uint16_t* a = static_cast<uint16_t*>(workspace);
+  hipError_t e = rnl::launch_norm_rows_bf16(xb, gb, eps, T, K, a, rstd_out, s);
+  if (e != hipSuccess) return hip_status(e, "norm pre-pass launch");
+  return hip_status(rnl::launch_gemm_bf16(a, wb, y, ok_kind, T, N, K, s), "bf16 GEMM launch");
+}
+
+size_t rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype) {
+  (void)N;
+  (void)out_dtype;
+  if (T <= 0 || K <= 0) return 0;
+  return align256((size_t)T * (size_t)K) + align256((size_t)T * 4);
+}
+
+int rmsnorm_linear_int8(const void* x, const void* gamma, float eps, const int8_t* Wq,
+                        const float* w_scale, void* y, int out_dtype, int8_t* xq_out,
+                        float* x_scale_out, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || Wq == nullptr || w_scale == nullptr || y == nullptr)
+    return fail(RNL_ERR_NULL, "x, Wq, w_scale and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK_int8));
+  if (K % 16 != 0) return fail(RNL_ERR_SHAPE, "int8 path needs K %% 16 == 0 (K=%lld)", (long long)K);
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32 && out_dtype != RNL_INT32)
+    return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16, RNL_FP32 or RNL_INT32");
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(Wq, 16, "Wq");
+  RNL_ALIGN(w_scale, 4, "w_scale");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(xq_out, 16, "xq_out");
+  RNL_ALIGN(x_scale_out, 4, "x_scale_out");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  const size_t q_bytes = xq_out ? 0 : align256((size_t)T * (size_t)K);
+  const size_t s_bytes = x_scale_out ? 0 : align256((size_t)T * 4);
+  const size_t need = q_bytes + s_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* q = xq_out ? xq_out : static_cast<int8_t*>(workspace);
+  float* xs = x_scale_out ? x_scale_out
+                          : reinterpret_cast<float*>(static_cast<char*>(workspace) + q_bytes);
+  hipError_t e = rnl::launch_norm_rows_int8(static_cast<const uint16_t*>(x),
+                                            static_cast<const uint16_t*>(gamma), eps, T, K, q, xs,
+                                            rstd_out, s);
+  if (e != hipSuccess) return hip_status(e, "norm+quant pre-pass launch");
+  const int kind = out_dtype == RNL_INT32 ? rnl::OUT_I32 : (out_dtype == RNL_FP32 ? rnl::OUT_F32 : rnl::OUT_BF16);
+  return hip_status(rnl::launch_gemm_int8(q, Wq, y, kind, xs, w_scale, T, N, K, s), "int8 GEMM launch");
+}
+
+size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N) {
+  (void)K;
+  (void)N;
+  if (T <= 0 || R <= 0) return 0;
+  return align256((size_t)T * (size_t)R * 2);
+}
+
+int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps, const void* W_b,
+                    void* qr_out, void* y, float* rstd_out, int64_t T, int64_t K, int64_t R,
+                    int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || W_a == nullptr || W_b == nullptr || qr_out == nullptr || y == nullptr)
+    return fail(RNL_ERR_NULL, "x, W_a, W_b, qr_out and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK));
+  RNL_TRY(check_dims(T, R, N, kMaxK));
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(W_a, 16, "W_a");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(W_b, 16, "W_b");
+  RNL_ALIGN(qr_out, 16, "qr_out");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  const size_t need = norm_proj_chain_workspace_bytes(T, K, R, N);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* qa = static_cast<uint16_t*>(workspace);
+  hipError_t e = rnl::launch_gemm_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W_a),
+                                       qa, rnl::OUT_BF16, T, R, K, s);
+  if (e != hipSuccess) return hip_status(e, "chain stage-1 GEMM launch");
+  e = rnl::launch_norm_rows_bf16(qa, static_cast<const uint16_t*>(gamma), eps, T, R,
+                                 static_cast<uint16_t*>(qr_out), rstd_out, s);
+  if (e != hipSuccess) return hip_status(e, "chain norm launch");
+  return hip_status(rnl::launch_gemm_bf16(static_cast<const uint16_t*>(qr_out), static_cast<const uint16_t*>(W_b),
+                                          y, rnl::OUT_BF16, T, N, R, s),
+                    "chain stage-2 GEMM launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal launchers of the gfx950 kernels.  Host code only; every launcher
+// trusts its arguments (the C ABI validates them first) and returns the HIP
+// status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rnl {
+
+enum OutKind : int { OUT_BF16 = 1, OUT_F32 = 2, OUT_I32 = 4 };
+
+// Row-wise RMSNorm pre-pass: one pass over each row computes the fp32 sum of
+// squares, rstd, and writes the normed row either as bf16 (a_out) or as
+// per-token symmetric int8 (q_out, x_scale_out).  rstd_out may be null.
+hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
+                                 int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s);
+hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
+                                 int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
+                                 hipStream_t s);
+
+// C[M,N] = A[M,K] . B[N,K]^T on bf16 MFMA, fp32 accumulation, C bf16 or fp32.
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
+                            int64_t N, int64_t K, hipStream_t s);
+
+// acc[M,N] = A[M,K] . B[N,K]^T on int8 MFMA (int32 accumulation).  With
+// out_kind OUT_I32 C receives acc; otherwise C = fl(float(acc) * fl(xs[m] * ws[n]))
+// as bf16 or fp32.
+hipError_t launch_gemm_int8(const int8_t* A, const int8_t* B, void* C, int out_kind,
+                            const float* xs, const float* ws, int64_t M, int64_t N, int64_t K,
+                            hipStream_t s);
+
+// Fused RMSNorm + projection for T <= 16 tokens (weight streaming).
+hipError_t launch_decode_bf16(const uint16_t* x, const uint16_t* gamma, float eps,
+                              const uint16_t* W, void* y, int out_kind, float* rstd_out, int64_t T,
+                              int64_t K, int64_t N, hipStream_t s);
+
+// fp32-weight projection of the fp32 normed rows, split over K.
+size_t skinny_workspace_bytes(int64_t T, int64_t K, int64_t N);
+hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float eps, const float* W,
+                               void* y, int out_kind, float* rstd_out, int64_t T, int64_t K,
+                               int64_t N, void* workspace, hipStream_t s);
+
+}  // namespace rnl

@@ -1,0 +1,198 @@
+// Row-wise RMSNorm pre-pass for the large-T GEMM paths (gfx950).
+//
+// One 256-thread workgroup per token row.  The row is read once with 16-byte
+// coalesced loads (kept in registers when K <= 16384), the fp32 sum of squares
+// is reduced across the wavefront and the workgroup, and the normed row is
+// written either as bf16 (the A operand of the bf16 GEMM) or as per-token
+// symmetric int8 plus its dequant scale (the A operand of the int8 GEMM).
+//
+// Arithmetic (AT-10 page, section 3, variant B; AT-10 page section 4, AT-05):
+//   S = sum_k xf^2 (fp32, any order), rstd = 1/sqrt(fl(fl(S*fl(1/K)) + eps)),
+//   n = fl(fl(xf * rstd) * gamma), bf16 out = round_nearest_even(n);
+//   int8: amax = max|n|, s = fl(127/amax), q = clamp(rint(fl(n*s)), -127, 127),
+//   x_scale = fl(amax/127); an all-zero row gives q = 0, x_scale = 0.
+#include "common.cuh"
+#include "launch.h"
+
+namespace rnl {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float sumsq8(u32x4 w) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float a = bf16lo(w[j]), b = bf16hi(w[j]);
+    s += a * a;
+    s += b * b;
+  }
+  return s;
+}
+
+// normed values of one 8-element chunk: n = fl(fl(xf * rstd) * g)
+__device__ __forceinline__ void normed8(u32x4 w, const u32x4* gr, int idx, float rstd, float n[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    n[2 * j] = __fmul_rn(bf16lo(w[j]), rstd);
+    n[2 * j + 1] = __fmul_rn(bf16hi(w[j]), rstd);
+  }
+  if (gr != nullptr) {
+    u32x4 g = gr[idx];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      n[2 * j] = __fmul_rn(n[2 * j], bf16lo(g[j]));
+      n[2 * j + 1] = __fmul_rn(n[2 * j + 1], bf16hi(g[j]));
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t q4(const float n[8], int base, float s) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float q = rintf(__fmul_rn(n[base + j], s));
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    r |= ((uint32_t)(int)q & 0xFFu) << (8 * j);
+  }
+  return r;
+}
+
+// CPT > 0: each thread keeps CPT 16-byte chunks of the row in registers.
+// CPT == 0: the row is re-read from global memory for each pass.
+template <int CPT, bool INT8>
+__global__ __launch_bounds__(kThreads) void norm_rows_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps, float inv_k,
+    int64_t K, void* __restrict__ out, float* __restrict__ x_scale_out,
+    float* __restrict__ rstd_out) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int nch = (int)(K >> 3);
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * K);
+  const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
+
+  constexpr int NV = CPT > 0 ? CPT : 1;
+  u32x4 v[NV];
+  float ss = 0.f;
+  if constexpr (CPT > 0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kThreads;
+      v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+      ss += sumsq8(v[c]);
+    }
+  } else {
+    for (int idx = tid; idx < nch; idx += kThreads) ss += sumsq8(xr[idx]);
+  }
+  const float S = block_sum(ss, red);
+  const float rstd = rstd_from_sumsq(S, inv_k, eps);
+  if (tid == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
+
+  if constexpr (!INT8) {
+    u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + t * K);
+    auto emit = [&](u32x4 w, int idx) {
+      float n[8];
+      normed8(w, gr, idx, rstd, n);
+      orow[idx] = u32x4{pack_bf16x2(n[0], n[1]), pack_bf16x2(n[2], n[3]), pack_bf16x2(n[4], n[5]),
+                        pack_bf16x2(n[6], n[7])};
+    };
+    if constexpr (CPT > 0) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + c * kThreads;
+        if (idx < nch) emit(v[c], idx);
+      }
+    } else {
+      for (int idx = tid; idx < nch; idx += kThreads) emit(xr[idx], idx);
+    }
+  } else {
+    float amax = 0.f;
+    auto amax_of = [&](u32x4 w, int idx) {
+      float n[8];
+      normed8(w, gr, idx, rstd, n);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(n[j]));
+    };
+    if constexpr (CPT > 0) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + c * kThreads;
+        if (idx < nch) amax_of(v[c], idx);
+      }
+    } else {
+      for (int idx = tid; idx < nch; idx += kThreads) amax_of(xr[idx], idx);
+    }
+    amax = block_max(amax, red);
+    const float s = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
+    if (tid == 0 && x_scale_out != nullptr) x_scale_out[t] = __fdiv_rn(amax, 127.0f);
+    u32x2* orow = reinterpret_cast<u32x2*>(static_cast<int8_t*>(out) + t * K);
+    auto emit = [&](u32x4 w, int idx) {
+      float n[8];
+      normed8(w, gr, idx, rstd, n);
+      orow[idx] = u32x2{q4(n, 0, s), q4(n, 4, s)};
+    };
+    if constexpr (CPT > 0) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + c * kThreads;
+        if (idx < nch) emit(v[c], idx);
+      }
+    } else {
+      for (int idx = tid; idx < nch; idx += kThreads) emit(xr[idx], idx);
+    }
+  }
+}
+
+template <bool INT8>
+hipError_t launch_norm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T, int64_t K,
+                       void* out, float* x_scale_out, float* rstd_out, hipStream_t s) {
+  const float inv_k = 1.0f / (float)K;  // fl(1/K): K < 2^24 converts exactly
+  const int64_t nch = K / 8;
+  const int64_t per = (nch + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)T), block(kThreads);
+#define RNL_NORM_LAUNCH(C) \
+  hipLaunchKernelGGL((norm_rows_kernel<C, INT8>), grid, block, 0, s, x, gamma, eps, inv_k, K, out, x_scale_out, rstd_out)
+  if (per <= 1) RNL_NORM_LAUNCH(1);
+  else if (per <= 2) RNL_NORM_LAUNCH(2);
+  else if (per <= 4) RNL_NORM_LAUNCH(4);
+  else if (per <= 8) RNL_NORM_LAUNCH(8);
+  else RNL_NORM_LAUNCH(0);
+#undef RNL_NORM_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
+                                 int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
+  return launch_norm<false>(x, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
+}
+
+hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
+                                 int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
+                                 hipStream_t s) {
+  return launch_norm<true>(x, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+}
+
+}  // namespace rnl

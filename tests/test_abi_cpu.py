@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/rnl.h declares, and rejects invalid arguments before any HIP call
+(validation is host code that returns before touching the device)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import rmsnorm_linear_projection_amd as rnl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rnl.h")
+
+NULL = None
+FAKE = ctypes.c_void_p(0x10000)  # 16- and 256-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10002)  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"RNL_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def header_define(name):
+    m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rnl.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"rmsnorm_linear_bf16", "rmsnorm_linear_int8", "norm_proj_chain",
+                          "rnl_status_str", "rnl_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_python_codes_match_header():
+    for name, val in (("RNL_BF16", rnl.RNL_BF16), ("RNL_FP32", rnl.RNL_FP32),
+                      ("RNL_INT8", rnl.RNL_INT8), ("RNL_INT32", rnl.RNL_INT32)):
+        assert header_define(name) == val
+
+
+def test_status_strings(lib):
+    for code in range(0, -8, -1):
+        s = lib.rnl_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.rnl_status_str(-99).decode() == "unknown status"
+
+
+E = {n: header_define(n) for n in ("RNL_ERR_NULL", "RNL_ERR_SHAPE", "RNL_ERR_DTYPE", "RNL_ERR_ARG",
+                                   "RNL_ERR_ALIGN", "RNL_ERR_WORKSPACE")}
+
+
+def bf16_call(lib, x=FAKE, g=NULL, eps=1e-6, W=FAKE, wd=1, y=FAKE, od=1, rstd=NULL, T=4, K=64, N=8,
+              ws=FAKE, wsb=1 << 30):
+    return lib.rmsnorm_linear_bf16(x, g, eps, W, wd, y, od, rstd, T, K, N, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=NULL), "RNL_ERR_NULL"),
+    (dict(W=NULL), "RNL_ERR_NULL"),
+    (dict(y=NULL), "RNL_ERR_NULL"),
+    (dict(T=0), "RNL_ERR_SHAPE"),
+    (dict(N=-1), "RNL_ERR_SHAPE"),
+    (dict(K=12), "RNL_ERR_SHAPE"),
+    (dict(K=(1 << 20) + 8), "RNL_ERR_SHAPE"),
+    (dict(T=(1 << 24) + 1), "RNL_ERR_SHAPE"),
+    (dict(wd=3), "RNL_ERR_DTYPE"),
+    (dict(od=4), "RNL_ERR_DTYPE"),
+    (dict(eps=-1.0), "RNL_ERR_ARG"),
+    (dict(eps=float("nan")), "RNL_ERR_ARG"),
+    (dict(eps=float("inf")), "RNL_ERR_ARG"),
+    (dict(x=ODD), "RNL_ERR_ALIGN"),
+    (dict(g=ODD), "RNL_ERR_ALIGN"),
+    (dict(rstd=ctypes.c_void_p(0x10001)), "RNL_ERR_ALIGN"),
+    (dict(T=64, ws=NULL), "RNL_ERR_WORKSPACE"),
+    (dict(T=64, wsb=100), "RNL_ERR_WORKSPACE"),
+    (dict(wd=2, wsb=10), "RNL_ERR_WORKSPACE"),
+])
+def test_bf16_validation(lib, kw, code):
+    assert bf16_call(lib, **kw) == E[code]
+    assert lib.rnl_last_error().decode() != ""
+
+
+def test_workspace_queries(lib):
+    # decode (T <= 16) needs none; the GEMM path needs the normed activations
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(16, 4096, 6144, 1, 1) == 0
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(4096, 4096, 6144, 1, 1) >= 4096 * 4096 * 2
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(512, 28672, 24, 2, 2) > 512 * 24 * 4
+    assert lib.rmsnorm_linear_int8_workspace_bytes(2048, 4096, 4096, 1) >= 2048 * 4096 + 2048 * 4
+    assert lib.norm_proj_chain_workspace_bytes(1024, 7168, 1536, 24576) >= 1024 * 1536 * 2
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(0, 4096, 6144, 1, 1) == 0
+
+
+def test_forced_variant_changes_workspace(lib, monkeypatch):
+    monkeypatch.setenv("RNL_VARIANT", "gemm")
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(8, 256, 128, 1, 1) == 8 * 256 * 2
+    monkeypatch.setenv("RNL_VARIANT", "decode")
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(8, 256, 128, 1, 1) == 0
+
+
+def int8_call(lib, x=FAKE, g=NULL, eps=1e-6, Wq=FAKE, ws=FAKE, y=FAKE, od=1, xq=NULL, xs=NULL, rstd=NULL,
+              T=4, K=64, N=8, wsp=FAKE, wsb=1 << 30):
+    return lib.rmsnorm_linear_int8(x, g, eps, Wq, ws, y, od, xq, xs, rstd, T, K, N, wsp, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Wq=NULL), "RNL_ERR_NULL"),
+    (dict(ws=NULL), "RNL_ERR_NULL"),
+    (dict(K=24), "RNL_ERR_SHAPE"),  # int8 needs K % 16 == 0
+    (dict(K=133152), "RNL_ERR_SHAPE"),
+    (dict(od=3), "RNL_ERR_DTYPE"),
+    (dict(xq=ODD), "RNL_ERR_ALIGN"),
+    (dict(wsp=NULL), "RNL_ERR_WORKSPACE"),
+    (dict(wsb=16), "RNL_ERR_WORKSPACE"),
+])
+def test_int8_validation(lib, kw, code):
+    assert int8_call(lib, **kw) == E[code]
+
+
+def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, T=4, K=64, R=32,
+               N=8, ws=FAKE, wsb=1 << 30):
+    return lib.norm_proj_chain(x, Wa, g, eps, Wb, qr, y, rstd, T, K, R, N, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qr=NULL), "RNL_ERR_NULL"),
+    (dict(Wb=NULL), "RNL_ERR_NULL"),
+    (dict(R=12), "RNL_ERR_SHAPE"),
+    (dict(K=0), "RNL_ERR_SHAPE"),
+    (dict(eps=-0.5), "RNL_ERR_ARG"),
+    (dict(Wa=ODD), "RNL_ERR_ALIGN"),
+    (dict(ws=NULL), "RNL_ERR_WORKSPACE"),
+])
+def test_chain_validation(lib, kw, code):
+    assert chain_call(lib, **kw) == E[code]
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rnl.rmsnorm_linear_bf16(x, None, 1e-6, torch.zeros(8, 64, dtype=torch.bfloat16))

@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Acceptance rules (spec tolerances; readings of the pages as in the
+oracle):
+  * rstd: within 8 fp32 ulps of the oracle's own rstd;
+  * bf16 outputs: |y - y_ref| <= 1e-2 * (|y_ref| + 1e-2), y_ref from the oracle
+    evaluated with the device's rstd, so that both sides feed identical bf16
+    normed rows to the projection;
+  * int8: xq and x_scale bit-exact against the oracle's quantisation of the
+    rows normed with the device's rstd; int32 accumulators bit-exact against
+    the int64 GEMM of the device's xq; the fp32 dequant within 1e-5 relative
+    of the oracle's dequant of those accumulators;
+  * fp32 weights (no bf16 cast): |y - y_ref| <= 1e-5 * max(|y_ref|, rms(y_ref));
+  * every path is deterministic: two runs give identical bits.
+Large workloads are checked on sampled rows (rows are independent in every
+entry point), at the sizes and launch configuration the benchmark times.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rmsnorm_linear_projection_amd as rnl
+import synthetic
+from tests._util import bits, f32, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    rnl.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture
+def variant(monkeypatch):
+    def set_(v):
+        if v is None:
+            monkeypatch.delenv("RNL_VARIANT", raising=False)
+        else:
+            monkeypatch.setenv("RNL_VARIANT", v)
+    return set_
+
+
+def dev(t):
+    return None if t is None else t.cuda()
+
+
+def sample_rows(T, n=24, seed=0):
+    if T <= 64:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, T // 2, T - 2, T - 1]
+    return np.unique(np.concatenate([fixed, rng.choice(T, n, replace=False)]))
+
+
+def assert_bf16_close(y, y_ref, what):
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    bound = 1e-2 * (np.abs(y_ref) + 1e-2)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
+                           f"worst err {err.max():.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def assert_rstd(rstd_gpu, rstd_ref, what, ulps=8):
+    d = ulp_diff(rstd_gpu, rstd_ref)
+    assert d.max() <= ulps, f"{what}: rstd off by {int(d.max())} ulps"
+
+
+# ---------------------------------------------------------------------------
+# bf16 path (decode kernel for T <= 16, norm pre-pass + tiled GEMM otherwise)
+# ---------------------------------------------------------------------------
+def run_bf16(case, out_dtype=torch.bfloat16):
+    x, g, W = dev(case["x"]), dev(case["gamma"]), dev(case["W"])
+    T = x.shape[0]
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y = rnl.rmsnorm_linear_bf16(x, g, EPS, W, out_dtype=out_dtype, rstd_out=rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), rstd.cpu().numpy()
+
+
+def check_bf16_case(case, rows=None, out_dtype=torch.bfloat16):
+    y, rstd = run_bf16(case, out_dtype)
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb = bits(case["x"])[rows]
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    Wb = bits(case["W"])
+    _, rstd_own = O.rms_norm_rows(xb, gb, EPS)
+    assert_rstd(rstd[rows], rstd_own, case.name)
+    y32, ybf, _ = O.rmsnorm_linear_bf16(xb, gb, EPS, Wb, rstd=rstd[rows])
+    assert_bf16_close(f32(y)[rows], y32, case.name)
+    return y
+
+
+BF16_SMALL = [
+    (8, 256, 128),  # bf16 RMSNorm + Linear, T=8 K=256 N=128
+    (1, 4096, 64),
+    (16, 512, 48),
+    (3, 72, 5),  # K tail inside a 32-wide step, ragged N
+    (5, 64, 1),
+    (16, 8, 17),  # K = 8, the smallest
+    (17, 256, 130),
+    (300, 1032, 200),  # K tail of a 64-wide k-step
+    (129, 64, 33),
+]
+
+
+@pytest.mark.parametrize("T,K,N", BF16_SMALL)
+@pytest.mark.parametrize("gamma", [True, False])
+@pytest.mark.parametrize("force", [None, "gemm"])
+def test_bf16_small(T, K, N, gamma, force, variant):
+    variant(force)
+    check_bf16_case(synthetic.norm_linear_case(T, K, N, seed=T + K + N, gamma=gamma))
+
+
+@pytest.mark.parametrize("T,K,N", [(8, 256, 128), (300, 1032, 200), (1, 64, 7)])
+def test_bf16_fp32_output(T, K, N):
+    check_bf16_case(synthetic.norm_linear_case(T, K, N, seed=5), out_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("T,K,N", [
+    (4000, 264, 6100),  # 256 x 192 tiles, ragged M, N and K
+    (2000, 136, 4000),  # 256 x 128 tiles, ragged M, N and K
+])
+def test_bf16_large_tiles_ragged(T, K, N):
+    case = synthetic.norm_linear_case(T, K, N, seed=11)
+    check_bf16_case(case, rows=sample_rows(T))
+
+
+def test_bf16_zero_and_scaled_rows():
+    case = synthetic.norm_linear_case(40, 512, 96, seed=3)
+    x = case.tensors["x"].clone()
+    x[3] = 0
+    x[7] = (x[7].float() * 1024).to(torch.bfloat16)
+    x[9] = (x[9].float() / 4096).to(torch.bfloat16)
+    case.tensors["x"] = x
+    y = check_bf16_case(case)
+    assert (f32(y)[3] == 0).all()
+
+
+@pytest.mark.parametrize("T", [4096, 1, 16])
+def test_bf16_preattn_qkv_full_size(T):
+    """Pre-attention norm + fused QKV projection, K=4096, N=6144, at full size."""
+    case = synthetic.preattn_qkv(T)
+    y1 = check_bf16_case(case, rows=sample_rows(T, 40))
+    y2, _ = run_bf16(case)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+
+
+# ---------------------------------------------------------------------------
+# int8 W8A8 path
+# ---------------------------------------------------------------------------
+def run_int8(case, out_dtype):
+    x, g, Wq, ws = dev(case["x"]), dev(case["gamma"]), dev(case["Wq"]), dev(case["w_scale"])
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(T, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y = rnl.rmsnorm_linear_int8(x, g, EPS, Wq, ws, out_dtype=out_dtype, xq_out=xq, x_scale_out=xs, rstd_out=rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), xq.cpu().numpy(), xs.cpu().numpy(), rstd.cpu().numpy()
+
+
+def check_int8_case(case, rows=None):
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb = bits(case["x"])[rows]
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    Wq = case["Wq"].numpy()
+    wsc = case["w_scale"].numpy()
+
+    acc, xq, xs, rstd = run_int8(case, torch.int32)
+    _, rstd_own = O.rms_norm_rows(xb, gb, EPS)
+    assert_rstd(rstd[rows], rstd_own, case.name)
+    n, _ = O.rms_norm_rows(xb, gb, EPS, rstd=rstd[rows])
+    q_ref, xs_ref, _ = O.quant_rows(n)
+    assert np.array_equal(xq[rows], q_ref), f"{case.name}: xq not bit-exact ({int((xq[rows] != q_ref).sum())} differ)"
+    assert np.array_equal(xs[rows], xs_ref), f"{case.name}: x_scale not bit-exact"
+    acc_ref = O.int8_gemm(xq[rows], Wq)
+    assert np.array_equal(acc.numpy()[rows].astype(np.int64), acc_ref), f"{case.name}: int32 acc not bit-exact"
+
+    yf, xq2, xs2, _ = run_int8(case, torch.float32)
+    assert np.array_equal(xq2, xq) and np.array_equal(xs2, xs)
+    y_ref = O.dequant(acc_ref, xs_ref, wsc)
+    rel = np.abs(yf.numpy()[rows] - y_ref) / np.maximum(np.abs(y_ref), 1e-30)
+    assert (rel <= 1e-5).all(), f"{case.name}: fp32 dequant off by {rel.max():.3g}"
+
+    yb, _, _, _ = run_int8(case, torch.bfloat16)
+    assert_bf16_close(f32(yb)[rows], y_ref, case.name)
+    return yb
+
+
+INT8_SMALL = [
+    (37, 256, 72),
+    (1, 64, 16),
+    (16, 128, 130),
+    (130, 4112, 100),  # K tail of a 128-byte k-step
+    (3, 16, 3),
+]
+
+
+@pytest.mark.parametrize("T,K,N", INT8_SMALL)
+@pytest.mark.parametrize("gamma", [True, False])
+def test_int8_small(T, K, N, gamma):
+    check_int8_case(synthetic.int8_case(T, K, N, seed=T * 3 + N, gamma=gamma))
+
+
+def test_int8_tiles_ragged():
+    case = synthetic.int8_case(2000, 144, 4000, seed=17)  # 256 x 128 tiles
+    check_int8_case(case, rows=sample_rows(2000))
+
+
+def test_int8_zero_row():
+    case = synthetic.int8_case(20, 256, 40, seed=2)
+    x = case.tensors["x"].clone()
+    x[4] = 0
+    case.tensors["x"] = x
+    yb = check_int8_case(case)
+    assert (f32(yb)[4] == 0).all()
+
+
+def test_int8_w8a8_full_size():
+    """INT8 W8A8 norm + linear, T=2048, K=4096, N=4096, at full size."""
+    case = synthetic.int8_w8a8()
+    y1 = check_int8_case(case, rows=sample_rows(2048, 32))
+    y2, _, _, _ = run_int8(case, torch.bfloat16)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+
+
+# ---------------------------------------------------------------------------
+# fp32 weights: the large-reduction split-K path
+# ---------------------------------------------------------------------------
+def check_fp32w_case(case, out_dtype=torch.float32):
+    y, rstd = run_bf16(case, out_dtype)
+    xb = bits(case["x"])
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    W = case["W"].numpy()
+    _, rstd_own = O.rms_norm_rows(xb, gb, EPS)
+    assert_rstd(rstd, rstd_own, case.name)
+    y_ref, _ = O.rmsnorm_linear_fp32w(xb, gb, EPS, W, rstd=rstd)
+    if out_dtype == torch.float32:
+        scale = max(float(np.sqrt(np.mean(y_ref.astype(np.float64) ** 2))), 1e-30)
+        err = np.abs(y.numpy().astype(np.float64) - y_ref)
+        bound = 1e-5 * np.maximum(np.abs(y_ref), scale)
+        assert (err <= bound).all(), f"{case.name}: max err {err.max():.3g} (rms {scale:.3g})"
+    else:
+        assert_bf16_close(f32(y), y_ref, case.name)
+    return y
+
+
+@pytest.mark.parametrize("T,K,N,gamma", [
+    (3, 64, 5, False),
+    (70, 4104, 33, False),  # > 64 tokens, > 32 columns, K tail
+    (16, 1024, 24, True),
+    (130, 256, 64, True),
+])
+def test_fp32w_small(T, K, N, gamma):
+    check_fp32w_case(synthetic.norm_linear_case(T, K, N, seed=T + N, gamma=gamma, w_dtype="fp32"))
+
+
+def test_fp32w_bf16_output():
+    check_fp32w_case(synthetic.norm_linear_case(20, 512, 24, seed=1, gamma=False, w_dtype="fp32"),
+                     out_dtype=torch.bfloat16)
+
+
+def test_skinny_fp32_full_size():
+    """Large-reduction tiny-width norm + linear, T=512, K=28672, N=24, fp32 W."""
+    case = synthetic.skinny_fp32()
+    y1 = check_fp32w_case(case)
+    y2, _ = run_bf16(case, torch.float32)
+    assert torch.equal(y1, y2), "not deterministic"
+
+
+# ---------------------------------------------------------------------------
+# q_a -> norm -> q_b chain
+# ---------------------------------------------------------------------------
+def run_chain(case):
+    x, Wa, g, Wb = (dev(case[k]) for k in ("x", "W_a", "gamma", "W_b"))
+    T = x.shape[0]
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y, qr = rnl.norm_proj_chain(x, Wa, g, EPS, Wb, rstd_out=rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), qr.cpu(), rstd.cpu().numpy()
+
+
+def check_chain_case(case, rows=None):
+    y, qr, rstd = run_chain(case)
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb = bits(case["x"])[rows]
+    Wa, Wb = bits(case["W_a"]), bits(case["W_b"])
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    ref = O.norm_proj_chain(xb, Wa, gb, EPS, Wb)
+    # stage 1 + norm: qr is a bf16 output; its input q_a is itself a rounded
+    # accumulation, so rstd is compared with a relative bound
+    rel = np.abs(rstd[rows].astype(np.float64) / ref["rstd"] - 1)
+    assert rel.max() < 1e-3, f"{case.name}: rstd rel err {rel.max():.3g}"
+    assert_bf16_close(f32(qr)[rows], O.bf16_bits_to_f32(ref["qr"]), case.name + " qr")
+    # stage 2 from the device's qr: identical bf16 inputs
+    y_ref = O.project_bf16(O.bf16_bits_to_f32(bits(qr)[rows]), Wb)
+    assert_bf16_close(f32(y)[rows], y_ref, case.name + " y")
+    return y
+
+
+@pytest.mark.parametrize("T,K,R,N,gamma", [
+    (37, 256, 64, 80, True),
+    (5, 128, 48, 30, False),
+    (300, 520, 136, 260, True),
+])
+def test_chain_small(T, K, R, N, gamma):
+    check_chain_case(synthetic.chain_case(T, K, R, N, seed=T + R, gamma=gamma))
+
+
+def test_mla_q_chain_full_size():
+    """Low-rank query chain x[1024,7168] -> W_a[1536,7168] -> norm -> W_b[24576,1536]."""
+    case = synthetic.mla_q_chain()
+    y1 = check_chain_case(case, rows=sample_rows(1024, 24))
+    y2, _, _ = run_chain(case)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
