@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of the fused RMSNorm -> Linear hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME | --all]
+
+A step is one call of the entry point over one batch of seeded synthetic
+input already resident in HBM.  The default workload is the pre-attention
+norm + fused QKV projection (bf16, T=4096, K=4096, N=6144).  One JSON line is
+printed per workload with:
+  value / unit   whole-step throughput: TFLOP/s (TOP/s for int8) where the
+                 path is bound by MFMA, HBM GB/s where it is bound by memory;
+  roofline       the dominant kernel's algorithmic flops or bytes per launch
+                 over its average duration, timed with HIP events on the
+                 stream it runs on, against the MI355X peak;
+  cpu_baseline   the CPU oracle timed on a bounded sample of the same
+                 workload on this host's cores.
+Weight-bound workloads rotate through enough input copies that the 256 MB
+Infinity Cache cannot serve them between steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused RMSNorm+Linear TFLOP/s (TOP/s int8) and HBM GB/s, % of roofline"
+PEAK = {"bf16": 2500.0, "int8": 5000.0, "hbm": 8000.0}  # TFLOP/s, TOP/s, GB/s (MI355X dense)
+CSRC = os.path.join(ROOT, "rmsnorm_linear_projection_amd", "csrc")
+
+WORKLOADS = {
+    "preattn_qkv_T4096": dict(kind="bf16", T=4096, K=4096, N=6144, bound="mfma", dtype="bf16",
+                              desc="pre-attention norm + fused QKV projection (Q 4096 + K 1024 + V 1024)"),
+    "preattn_qkv_T16": dict(kind="bf16", T=16, K=4096, N=6144, bound="hbm", dtype="bf16",
+                            desc="pre-attention norm + QKV, 16 decode tokens"),
+    "preattn_qkv_T1": dict(kind="bf16", T=1, K=4096, N=6144, bound="hbm", dtype="bf16",
+                           desc="pre-attention norm + QKV, 1 decode token"),
+    "small_T8": dict(kind="bf16", T=8, K=256, N=128, bound="hbm", dtype="bf16",
+                     desc="bf16 RMSNorm + Linear, T=8 K=256 N=128"),
+    "int8_w8a8": dict(kind="int8", T=2048, K=4096, N=4096, bound="mfma", dtype="int8",
+                      desc="RMSNorm -> per-token int8 quant -> int8 GEMM -> dequant"),
+    "mla_q_chain": dict(kind="chain", T=1024, K=7168, R=1536, N=24576, bound="mfma", dtype="bf16",
+                        desc="x -> W_a[1536,7168] -> RMSNorm -> W_b[24576,1536]"),
+    "skinny_fp32": dict(kind="fp32w", T=512, K=28672, N=24, bound="hbm", dtype="f32",
+                        desc="large-reduction tiny-width norm + linear, fp32 weight, no gamma"),
+}
+DEFAULT = "preattn_qkv_T4096"
+KERNEL_SOURCES = {
+    "gemm": ["gemm.hip", "common.cuh"],
+    "decode": ["decode.hip", "common.cuh"],
+    "skinny": ["skinny.hip", "common.cuh"],
+}
+
+
+def flops_of(w):
+    if w["kind"] == "chain":
+        return 2.0 * w["T"] * (w["K"] * w["R"] + w["R"] * w["N"])
+    return 2.0 * w["T"] * w["K"] * w["N"]
+
+
+def bytes_of(w):
+    """Algorithmic bytes: every input read once, every output written once."""
+    T, K, N = w["T"], w["K"], w["N"]
+    if w["kind"] == "bf16":
+        return T * K * 2 + K * 2 + N * K * 2 + T * N * 2
+    if w["kind"] == "int8":
+        return T * K * 2 + K * 2 + N * K + N * 4 + T * N * 2
+    if w["kind"] == "fp32w":
+        return T * K * 2 + N * K * 4 + T * N * 4
+    R = w["R"]
+    return T * K * 2 + R * K * 2 + R * 2 + N * R * 2 + T * R * 2 + T * N * 2
+
+
+def src_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, kernel_key, launches_per_step=1):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counters (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, each scaled by the
+    factor a plain copy of known size gives), or None when the counters were
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get("workloads", {}).get(name)
+    if not rec or rec.get("src_sha") != src_sha(KERNEL_SOURCES[kernel_key]):
+        return None
+    cal = data["copy_calibration"]
+    return (rec["fetch_kib"] * cal["fetch_scale"] + rec["write_kib"] * cal["write_scale"]) * 1024.0
+
+
+class Setup:
+    """Device inputs, outputs and the step / dominant-kernel closures."""
+
+    def __init__(self, name, w):
+        import torch
+
+        import rmsnorm_linear_projection_amd as rnl
+        import synthetic
+
+        self.name, self.w = name, w
+        dev = torch.device("cuda:0")
+        kind = w["kind"]
+        self.case = {
+            "bf16": lambda: synthetic.norm_linear_case(w["T"], w["K"], w["N"], name=name),
+            "fp32w": lambda: synthetic.norm_linear_case(w["T"], w["K"], w["N"], gamma=False, w_dtype="fp32", name=name),
+            "int8": lambda: synthetic.int8_case(w["T"], w["K"], w["N"], name=name),
+            "chain": lambda: synthetic.chain_case(w["T"], w["K"], w["R"], w["N"], name=name),
+        }[kind]()
+        t = {k: (v.to(dev) if v is not None else None) for k, v in self.case.tensors.items()}
+        T, K, N = w["T"], w["K"], w["N"]
+        eps = self.case.eps
+        # rotate copies of the streamed operand when the path is bound by HBM
+        self.copies = 1
+        if w["bound"] == "hbm":
+            rot = "W" if kind == "bf16" else "x"
+            nbytes = t[rot].numel() * t[rot].element_size()
+            self.copies = max(1, math.ceil(640e6 / nbytes)) if nbytes > 1e6 else 1
+            t[rot + "_copies"] = [t[rot]] + [t[rot].clone() for _ in range(self.copies - 1)]
+        self.t = t
+        self.kernel = None
+        self.kernel_key = None
+        if kind == "bf16":
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(1, rnl.workspace_bytes("bf16", T, K, N)), dtype=torch.uint8, device=dev)
+            Wc = t.get("W_copies", [t["W"]])
+            self.step = lambda i: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], y=y, workspace=ws)
+            if T <= 16:
+                self.kernel, self.kernel_key = "decode_kernel", "decode"
+                self.kern = self.step
+                self.kern_units = ("hbm", bytes_of(w))
+            else:
+                a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
+                self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
+                self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
+                self.kern_units = ("bf16", flops_of(w))
+        elif kind == "fp32w":
+            y = torch.empty((T, N), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(1, rnl.workspace_bytes("bf16", T, K, N, w_dtype=torch.float32,
+                                                        out_dtype=torch.float32)), dtype=torch.uint8, device=dev)
+            xc = t.get("x_copies", [t["x"]])
+            self.step = lambda i: rnl.rmsnorm_linear_bf16(xc[i % len(xc)], None, eps, t["W"], out_dtype=torch.float32,
+                                                          y=y, workspace=ws)
+            self.kernel, self.kernel_key = "skinny_partial_kernel+skinny_finalize_kernel", "skinny"
+            self.kern = self.step
+            self.kern_units = ("hbm", bytes_of(w))
+        elif kind == "int8":
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(rnl.workspace_bytes("int8", T, K, N), dtype=torch.uint8, device=dev)
+            self.step = lambda i: rnl.rmsnorm_linear_int8(t["x"], t["gamma"], eps, t["Wq"], t["w_scale"], y=y,
+                                                          workspace=ws)
+            xq, xs = rnl.rms_norm_quant_int8(t["x"], t["gamma"], eps)
+            self.kernel, self.kernel_key = "gemm_nt_kernel<int8>", "gemm"
+            self.kern = lambda i: rnl.linear_int8(xq, xs, t["Wq"], t["w_scale"], y=y)
+            self.kern_units = ("int8", flops_of(w))
+        else:
+            R = w["R"]
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            qr = torch.empty((T, R), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(rnl.workspace_bytes("chain", T, K, R, N), dtype=torch.uint8, device=dev)
+            self.step = lambda i: rnl.norm_proj_chain(t["x"], t["W_a"], t["gamma"], eps, t["W_b"], qr_out=qr, y=y,
+                                                      workspace=ws)
+            self.step(0)
+            self.kernel, self.kernel_key = "gemm_nt_kernel<bf16> (stage 2, qr . W_b^T)", "gemm"
+            self.kern = lambda i: rnl.linear_bf16(qr, t["W_b"], y=y)
+            self.kern_units = ("bf16", 2.0 * T * R * N)
+        torch.cuda.synchronize()
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def cpu_baseline(setup, target_s=8.0):
+    """The oracle as it stands, on a bounded row sample of the same inputs."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    w, c = setup.w, setup.case
+
+    def bits(x):
+        return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    kind = w["kind"]
+    T = w["T"]
+
+    def run(rows):
+        x = bits(c["x"][:rows])
+        g = None if c["gamma"] is None else bits(c["gamma"])
+        if kind == "bf16":
+            O.rmsnorm_linear_bf16(x, g, c.eps, bits(c["W"]))
+        elif kind == "fp32w":
+            O.rmsnorm_linear_fp32w(x, g, c.eps, c["W"].numpy())
+        elif kind == "int8":
+            O.rmsnorm_linear_int8(x, g, c.eps, c["Wq"].numpy(), c["w_scale"].numpy())
+        else:
+            O.norm_proj_chain(x, bits(c["W_a"]), g, c.eps, bits(c["W_b"]))
+
+    rows = min(T, 16)
+    t0 = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t0
+    # grow the row sample toward ~1/4 of the budget per call, then repeat
+    while rows < T and dt < target_s / 4:
+        rows = min(T, rows * 2)
+        t0 = time.perf_counter()
+        run(rows)
+        dt = time.perf_counter() - t0
+    calls, t_total = 0, 0.0
+    while calls == 0 or t_total < target_s:
+        t0 = time.perf_counter()
+        run(rows)
+        t_total += time.perf_counter() - t0
+        calls += 1
+    per_call = t_total / calls
+    sub = dict(w, T=rows)
+    if w["bound"] == "hbm":
+        value, unit = bytes_of(sub) / per_call / 1e9, "GB/s"
+    else:
+        value, unit = flops_of(sub) / per_call / 1e12, "TOP/s" if kind == "int8" else "TFLOP/s"
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: BLAS thread count unknown
+        cores = None
+    return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} of {T} token rows, {calls} call(s), {per_call:.3f} s per call"}
+
+
+def bench_one(name, steps, warmup, with_cpu=True):
+    import torch
+
+    w = WORKLOADS[name]
+    s = Setup(name, w)
+    ms = time_loop(s.step, steps, warmup)
+    kms = time_loop(s.kern, steps, warmup) if s.kern is not s.step else ms
+    if w["bound"] == "hbm":
+        value, unit = bytes_of(w) / (ms * 1e-3) / 1e9, "GB/s"
+    else:
+        value = flops_of(w) / (ms * 1e-3) / 1e12
+        unit = "TOP/s" if w["kind"] == "int8" else "TFLOP/s"
+    peak_key, per_launch = s.kern_units
+    if peak_key == "hbm":
+        achieved, ru, bound = per_launch / (kms * 1e-3) / 1e9, "GB/s", "hbm"
+    else:
+        achieved, ru, bound = per_launch / (kms * 1e-3) / 1e12, ("TOP/s" if peak_key == "int8" else "TFLOP/s"), "mfma"
+    traffic = load_traffic(name, s.kernel_key)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": s.case.name, "description": w["desc"],
+                   **{k: w[k] for k in ("T", "K", "R", "N") if k in w},
+                   "parallelism": "none (1 GPU)", "input_copies": s.copies},
+        "roofline": {"bound": bound, "kernel": s.kernel, "achieved": round(achieved, 3), "peak": PEAK[peak_key],
+                     "unit": ru, "frac": round(achieved / PEAK[peak_key], 4),
+                     "kernel_ms": round(kms, 6),
+                     "traffic": None if traffic is None else int(traffic)},
+    }
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(s)
+    del s
+    torch.cuda.empty_cache()
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="one line per workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not supported",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    import rmsnorm_linear_projection_amd as rnl
+
+    if not os.path.exists(rnl.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    names = sorted(WORKLOADS, key=lambda n: n != DEFAULT) if args.all else [args.workload]
+    for n in names:
+        print(json.dumps(bench_one(n, args.steps, args.warmup, with_cpu=not args.no_cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -154,6 +154,47 @@ RNL_API int norm_proj_chain(const void* x, const void* W_a, const void* gamma, f
 
 RNL_API size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N);
 
+/*
+ * The atoms the fused entry points are built from.  They run the same kernels
+ * and follow the same conventions (device pointers, asynchronous on `stream`,
+ * validation before any HIP call, status codes); none needs a workspace.
+ *
+ * rms_norm_bf16 -- AT-03 RMSNorm (AT-10 page, section 3: fp32 inside, variant B
+ * rstd, optional gamma, bf16 output, optional rstd output):
+ *   y[t,k] = round_bf16(fl(fl(float(x[t,k]) * rstd[t]) * float(gamma[k]))).
+ *   x [T,K] bf16; gamma [K] bf16 or NULL; y [T,K] bf16; rstd_out [T] or NULL.
+ */
+RNL_API int rms_norm_bf16(const void* x, const void* gamma, float eps, void* y, float* rstd_out,
+                          int64_t T, int64_t K, void* stream);
+
+/*
+ * rms_norm_quant_int8 -- AT-03 followed by AT-05 per-token symmetric int8
+ * quantisation of the fp32 normed rows (AT-10 page section 4; SK-03 page quant
+ * variant).  xq [T,K] int8 and x_scale [T] fp32 (amax/127) are required;
+ * rstd_out may be NULL.  K must be a multiple of 16.
+ */
+RNL_API int rms_norm_quant_int8(const void* x, const void* gamma, float eps, int8_t* xq,
+                                float* x_scale, float* rstd_out, int64_t T, int64_t K,
+                                void* stream);
+
+/*
+ * linear_bf16 -- AT-09 Linear Projection, BF16 mode (AT-10 page section 4):
+ * y[M,N] = a[M,K] . W[N,K]^T (b_trans), bf16 operands, fp32 accumulation,
+ * y bf16 (out_dtype RNL_BF16, rounded once) or fp32 (RNL_FP32).
+ */
+RNL_API int linear_bf16(const void* a, const void* W, void* y, int out_dtype, int64_t M, int64_t K,
+                        int64_t N, void* stream);
+
+/*
+ * linear_int8 -- AT-09 Linear Projection, INT8 W8A8 mode, with the AT-06
+ * dequant: acc = xq[M,K] . Wq[N,K]^T in int32; y = fl(float(acc) *
+ * fl(x_scale[m] * w_scale[n])) as bf16 or fp32, or acc itself for RNL_INT32.
+ * K must be a multiple of 16 and at most 133144.
+ */
+RNL_API int linear_int8(const int8_t* xq, const float* x_scale, const int8_t* Wq,
+                        const float* w_scale, void* y, int out_dtype, int64_t M, int64_t K,
+                        int64_t N, void* stream);
+
 /* Static description of a status code. */
 RNL_API const char* rnl_status_str(int status);
 

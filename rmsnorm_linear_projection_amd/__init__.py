@@ -25,6 +25,10 @@ __all__ = [
     "rmsnorm_linear_bf16",
     "rmsnorm_linear_int8",
     "norm_proj_chain",
+    "rms_norm_bf16",
+    "rms_norm_quant_int8",
+    "linear_bf16",
+    "linear_int8",
     "workspace_bytes",
     "load_library",
     "RnlError",
@@ -77,6 +81,14 @@ def load_library() -> ctypes.CDLL:
     lib.norm_proj_chain.restype = ctypes.c_int
     lib.norm_proj_chain_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64]
     lib.norm_proj_chain_workspace_bytes.restype = ctypes.c_size_t
+    lib.rms_norm_bf16.argtypes = [_c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_i64, _c_i64, _c_p]
+    lib.rms_norm_bf16.restype = ctypes.c_int
+    lib.rms_norm_quant_int8.argtypes = [_c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p]
+    lib.rms_norm_quant_int8.restype = ctypes.c_int
+    lib.linear_bf16.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
+    lib.linear_bf16.restype = ctypes.c_int
+    lib.linear_int8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
+    lib.linear_int8.restype = ctypes.c_int
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -237,3 +249,87 @@ def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None,
                                  _ptr(rstd_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
     _check(rc)
     return y, qr_out
+
+
+def rms_norm_bf16(x, gamma, eps, y=None, rstd_out=None):
+    """AT-03 RMSNorm: y = bf16(fl(fl(x * rstd) * gamma)); returns y [T, K] bf16."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    if y is None:
+        y = torch.empty_like(x)
+    _dev_tensor(y, "y", torch.bfloat16)
+    _shape(tuple(y.shape) == (T, K), "y must be [T, K]")
+    with torch.cuda.device(x.device):
+        rc = lib.rms_norm_bf16(_ptr(x), _ptr(gamma), float(eps), _ptr(y), _ptr(rstd_out), T, K, _stream(x.device))
+    _check(rc)
+    return y
+
+
+def rms_norm_quant_int8(x, gamma, eps, xq=None, x_scale=None, rstd_out=None):
+    """AT-03 + AT-05: per-token symmetric int8 quant of the normed rows.
+    Returns (xq [T, K] int8, x_scale [T] fp32)."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    if xq is None:
+        xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(T, dtype=torch.float32, device=x.device)
+    _dev_tensor(xq, "xq", torch.int8)
+    _dev_tensor(x_scale, "x_scale", torch.float32)
+    _shape(xq.numel() == T * K and x_scale.numel() >= T, "xq must be [T, K] and x_scale [T]")
+    with torch.cuda.device(x.device):
+        rc = lib.rms_norm_quant_int8(_ptr(x), _ptr(gamma), float(eps), _ptr(xq), _ptr(x_scale), _ptr(rstd_out),
+                                     T, K, _stream(x.device))
+    _check(rc)
+    return xq, x_scale
+
+
+def linear_bf16(a, W, out_dtype=torch.bfloat16, y=None):
+    """AT-09 BF16 mode: y[M, N] = a[M, K] . W[N, K]^T, fp32 accumulation."""
+    lib = load_library()
+    _dev_tensor(a, "a", torch.bfloat16, 2)
+    _dev_tensor(W, "W", torch.bfloat16, 2)
+    M, K = a.shape
+    N = W.shape[0]
+    _shape(W.shape[1] == K, "W must be [N, K]")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _dev_tensor(y, "y", out_dtype)
+    _shape(tuple(y.shape) == (M, N), "y must be [M, N]")
+    with torch.cuda.device(a.device):
+        rc = lib.linear_bf16(_ptr(a), _ptr(W), _ptr(y), _DTYPE_CODE[out_dtype], M, K, N, _stream(a.device))
+    _check(rc)
+    return y
+
+
+def linear_int8(xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, y=None):
+    """AT-09 INT8 W8A8 mode + AT-06 dequant (out_dtype torch.int32: raw accumulators)."""
+    lib = load_library()
+    _dev_tensor(xq, "xq", torch.int8, 2)
+    _dev_tensor(Wq, "Wq", torch.int8, 2)
+    _dev_tensor(x_scale, "x_scale", torch.float32)
+    _dev_tensor(w_scale, "w_scale", torch.float32)
+    M, K = xq.shape
+    N = Wq.shape[0]
+    _shape(Wq.shape[1] == K, "Wq must be [N, K]")
+    _shape(x_scale is None or x_scale.numel() >= M, "x_scale must be [M]")
+    _shape(w_scale is None or w_scale.numel() >= N, "w_scale must be [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _dev_tensor(y, "y", out_dtype)
+    _shape(tuple(y.shape) == (M, N), "y must be [M, N]")
+    with torch.cuda.device(xq.device):
+        rc = lib.linear_int8(_ptr(xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), _ptr(y), _DTYPE_CODE[out_dtype],
+                             M, K, N, _stream(xq.device))
+    _check(rc)
+    return y

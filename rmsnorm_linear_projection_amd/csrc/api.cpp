@@ -244,4 +244,69 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
                     "chain stage-2 GEMM launch");
 }
 
+int rms_norm_bf16(const void* x, const void* gamma, float eps, void* y, float* rstd_out, int64_t T,
+                  int64_t K, void* stream) {
+  if (x == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "x and y are required");
+  RNL_TRY(check_dims(T, K, 1, kMaxK));
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  return hip_status(rnl::launch_norm_rows_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma),
+                                               eps, T, K, static_cast<uint16_t*>(y), rstd_out,
+                                               static_cast<hipStream_t>(stream)),
+                    "norm launch");
+}
+
+int rms_norm_quant_int8(const void* x, const void* gamma, float eps, int8_t* xq, float* x_scale,
+                        float* rstd_out, int64_t T, int64_t K, void* stream) {
+  if (x == nullptr || xq == nullptr || x_scale == nullptr) return fail(RNL_ERR_NULL, "x, xq and x_scale are required");
+  RNL_TRY(check_dims(T, K, 1, kMaxK_int8));
+  if (K % 16 != 0) return fail(RNL_ERR_SHAPE, "int8 path needs K %% 16 == 0 (K=%lld)", (long long)K);
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(xq, 16, "xq");
+  RNL_ALIGN(x_scale, 4, "x_scale");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  return hip_status(rnl::launch_norm_rows_int8(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma),
+                                               eps, T, K, xq, x_scale, rstd_out,
+                                               static_cast<hipStream_t>(stream)),
+                    "norm+quant launch");
+}
+
+int linear_bf16(const void* a, const void* W, void* y, int out_dtype, int64_t M, int64_t K, int64_t N,
+                void* stream) {
+  if (a == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "a, W and y are required");
+  RNL_TRY(check_dims(M, K, N, kMaxK));
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
+  RNL_ALIGN(a, 16, "a");
+  RNL_ALIGN(W, 16, "W");
+  RNL_ALIGN(y, 16, "y");
+  return hip_status(rnl::launch_gemm_bf16(static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(W), y,
+                                          out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32, M, N, K,
+                                          static_cast<hipStream_t>(stream)),
+                    "bf16 GEMM launch");
+}
+
+int linear_int8(const int8_t* xq, const float* x_scale, const int8_t* Wq, const float* w_scale, void* y,
+                int out_dtype, int64_t M, int64_t K, int64_t N, void* stream) {
+  if (xq == nullptr || Wq == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "xq, Wq and y are required");
+  if (out_dtype != RNL_INT32 && (x_scale == nullptr || w_scale == nullptr))
+    return fail(RNL_ERR_NULL, "x_scale and w_scale are required to dequantise");
+  RNL_TRY(check_dims(M, K, N, kMaxK_int8));
+  if (K % 16 != 0) return fail(RNL_ERR_SHAPE, "int8 path needs K %% 16 == 0 (K=%lld)", (long long)K);
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32 && out_dtype != RNL_INT32)
+    return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16, RNL_FP32 or RNL_INT32");
+  RNL_ALIGN(xq, 16, "xq");
+  RNL_ALIGN(Wq, 16, "Wq");
+  RNL_ALIGN(x_scale, 4, "x_scale");
+  RNL_ALIGN(w_scale, 4, "w_scale");
+  RNL_ALIGN(y, 16, "y");
+  const int kind = out_dtype == RNL_INT32 ? rnl::OUT_I32 : (out_dtype == RNL_FP32 ? rnl::OUT_F32 : rnl::OUT_BF16);
+  return hip_status(rnl::launch_gemm_int8(xq, Wq, y, kind, x_scale, w_scale, M, N, K, static_cast<hipStream_t>(stream)),
+                    "int8 GEMM launch");
+}
+
 }  // extern "C"
