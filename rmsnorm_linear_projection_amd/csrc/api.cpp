@@ -205,10 +205,11 @@ int rmsnorm_linear_int8(const void* x, const void* gamma, float eps, const int8_
 }
 
 size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N) {
-  (void)K;
   (void)N;
-  if (T <= 0 || R <= 0) return 0;
-  return align256((size_t)T * (size_t)R * 2);
+  if (T <= 0 || R <= 0 || K <= 0) return 0;
+  const int ks = rnl::gemm_split_plan(T, R, K, 2, nullptr);
+  if (ks > 1) return align256((size_t)ks * (size_t)T * (size_t)R * 4);  // fp32 split-K partials of q_a
+  return align256((size_t)T * (size_t)R * 2);                           // bf16 q_a
 }
 
 int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps, const void* W_b,
@@ -232,13 +233,27 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
     return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* qa = static_cast<uint16_t*>(workspace);
-  hipError_t e = rnl::launch_gemm_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W_a),
-                                       qa, rnl::OUT_BF16, T, R, K, s);
-  if (e != hipSuccess) return hip_status(e, "chain stage-1 GEMM launch");
-  e = rnl::launch_norm_rows_bf16(qa, static_cast<const uint16_t*>(gamma), eps, T, R,
-                                 static_cast<uint16_t*>(qr_out), rstd_out, s);
-  if (e != hipSuccess) return hip_status(e, "chain norm launch");
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wa = static_cast<const uint16_t*>(W_a);
+  const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+  uint16_t* qr = static_cast<uint16_t*>(qr_out);
+  const int ks = rnl::gemm_split_plan(T, R, K, 2, nullptr);
+  hipError_t e;
+  if (ks > 1) {
+    // q_a is too small to fill the chip: split its K, then add the partials in split
+    // order inside the norm pre-pass (q_a = bf16 of the sum)
+    float* part = static_cast<float*>(workspace);
+    e = rnl::launch_gemm_bf16_splitk(xb, wa, part, T, R, K, ks, s);
+    if (e != hipSuccess) return hip_status(e, "chain stage-1 split-K GEMM launch");
+    e = rnl::launch_reduce_norm_bf16(part, ks, gb, eps, T, R, qr, rstd_out, s);
+    if (e != hipSuccess) return hip_status(e, "chain reduce+norm launch");
+  } else {
+    uint16_t* qa = static_cast<uint16_t*>(workspace);
+    e = rnl::launch_gemm_bf16(xb, wa, qa, rnl::OUT_BF16, T, R, K, s);
+    if (e != hipSuccess) return hip_status(e, "chain stage-1 GEMM launch");
+    e = rnl::launch_norm_rows_bf16(qa, gb, eps, T, R, qr, rstd_out, s);
+    if (e != hipSuccess) return hip_status(e, "chain norm launch");
+  }
   return hip_status(rnl::launch_gemm_bf16(static_cast<const uint16_t*>(qr_out), static_cast<const uint16_t*>(W_b),
                                           y, rnl::OUT_BF16, T, N, R, s),
                     "chain stage-2 GEMM launch");

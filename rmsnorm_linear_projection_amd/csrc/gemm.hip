@@ -1,24 +1,39 @@
 // Tiled MFMA GEMM for the projection step: C[M,N] = A[M,K] . B[N,K]^T (b_trans).
 //
-// A is the normed activation tile (bf16, or per-token int8), B the weight
-// stored [N, K] (AT-10 page section 2: the weight enters with b_trans=True).
-// Both operands are K-contiguous, so both are staged through LDS the same way:
-// a k-step is 128 bytes of every tile row (64 bf16 or 128 int8), one 16-byte
-// chunk per lane, which is exactly one MFMA operand register quad:
-//   bf16: v_mfma_f32_16x16x32_bf16  (8 bf16 per lane, fp32 accumulate)
-//   int8: v_mfma_i32_16x16x64_i8    (16 int8 per lane, int32 accumulate)
+// A is the normed activation (bf16, or per-token int8), B the weight stored
+// [N, K] (AT-10 page section 2: the weight enters with b_trans=True).  Both
+// operands are K-contiguous and staged through LDS identically: a k-step is 128
+// bytes of every tile row (64 bf16 or 128 int8), cut into 16-byte chunks, and
+// one chunk is exactly one lane's MFMA operand:
+//   bf16: v_mfma_f32_16x16x32_bf16  (8 bf16 per lane, fp32 accumulation)
+//   int8: v_mfma_i32_16x16x64_i8    (16 int8 per lane, int32 accumulation)
+// A k-step therefore holds two MFMA k-chunks ("halves").
 //
-// Workgroup: 256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN tile.
-// The weight fragment is the MFMA "A" source and the activation fragment the
-// "B" source, so each lane ends up holding 4 consecutive output columns of one
-// token row, which it stores as one 8- or 16-byte vector.
+// Workgroup: 256 threads = 4 wavefronts (one per SIMD) in a 2 x 2 grid over a
+// BM x BN tile.  The weight fragment is the MFMA "A" source and the activation
+// fragment the "B" source, so each lane ends up with 4 consecutive output
+// columns of one token row and stores them as one vector.
 //
-// Data movement: buffer loads (out-of-range rows and the K tail read as zero)
-// into registers one k-step ahead, then into a double-buffered LDS stage with
-// an XOR swizzle of the 16-byte chunk index so that the 16 lanes reading one
-// operand column hit distinct banks.  Workgroup ids are remapped so that each
-// of the 8 XCDs (dispatched round-robin) works on a contiguous, grouped block
-// of tiles that share A and B panels in its L2.
+// Pipeline (one barrier per k-step):
+//   * global -> LDS with buffer_load ... lds (direct-to-LDS DMA, no VGPR
+//     staging); out-of-range rows and the K tail read as zero;
+//   * NST LDS stages; a stage is refilled as soon as every wavefront has read
+//     its fragments, so NST-1 stages are in flight;
+//   * per half: the MFMAs of the fragments already in registers are issued
+//     interleaved with the LDS reads of the next half's fragments and with the
+//     DMA loads of the refill, in fixed groups, so the in-order issue of a
+//     wavefront never stalls behind a burst of memory instructions.
+// LDS layout: row-major, 128 bytes per row, 16-byte chunk c of row r stored at
+// slot c ^ (r & 7); the 16 lanes that read one MFMA operand column then hit
+// distinct banks (measured conflict-free on gfx950).
+//
+// Workgroup ids are remapped so that each of the 8 XCDs (dispatched
+// round-robin) works on a contiguous block of tiles, grouped GROUP_M tiles
+// tall, which share A and B panels in that XCD's L2.
+//
+// Split-K: with KSPLIT > 1 the grid holds KSPLIT workgroups per tile, each
+// reducing one contiguous range of k-steps and writing a partial tile (fp32 or
+// int32) to slice z of a [KSPLIT, M, N] buffer; the caller reduces the slices.
 #include "common.cuh"
 #include "launch.h"
 
@@ -46,126 +61,175 @@ struct Mfma<int8_t> {
   }
 };
 
-enum Epi : int { EPI_BF16 = 0, EPI_F32 = 1, EPI_I32 = 2, EPI_DEQ_BF16 = 3, EPI_DEQ_F32 = 4 };
+enum Epi : int {
+  EPI_BF16 = 0,      // C bf16 = round(acc)
+  EPI_F32 = 1,       // C fp32 = acc
+  EPI_I32 = 2,       // C int32 = acc
+  EPI_DEQ_BF16 = 3,  // C bf16 = round(fl(float(acc) * fl(xs[m] * ws[n])))
+  EPI_DEQ_F32 = 4,   // C fp32 = fl(float(acc) * fl(xs[m] * ws[n]))
+  EPI_PART = 5,      // C[z] = acc (fp32 or int32 partial of split z)
+};
 
-// 16-byte chunk slot of tile row r: distinct over any 16 consecutive rows that
-// share a parity and over any 8 consecutive rows, so a 16-lane column read is
-// conflict-free whether the LDS serves 8 or 16 lanes of a b128 read per cycle.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt unchanged (gfx9 encoding)
+#define RNL_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
 
-template <typename TIn, int BM, int BN, int GROUP_M, int EPI>
+template <typename TIn, int BM, int BN, int NST, int GROUP_M, int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* __restrict__ C,
                     const float* __restrict__ xs, const float* __restrict__ ws, int M, int N, int K,
-                    int tiles_m, int tiles_n) {
+                    int tiles_m, int tiles_n, int ksplit, int steps_per_split) {
   using Acc = typename Mfma<TIn>::Acc;
   constexpr int ROWB = 128;
-  constexpr int A_CH = BM * 8 / 256;
+  constexpr int A_CH = BM * 8 / 256;  // DMA instructions per wave and stage for A
   constexpr int B_CH = BN * 8 / 256;
+  constexpr int LPS = A_CH + B_CH;    // DMA instructions per wave and stage
   constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int MI = WM / 16, NI = WN / 16;
+  constexpr int NMI = WM / 16, NNI = WN / 16;
+  constexpr int NF = NMI + NNI;       // fragment reads per half
+  constexpr int NMM = NMI * NNI;      // MFMAs per half
   constexpr int STAGE = (BM + BN) * ROWB;
   static_assert(BM % 32 == 0 && BN % 32 == 0, "tile rows must be multiples of 32");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  static_assert(LPS * (NST - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // workgroup -> tile: contiguous range per XCD, grouped along M inside it
+  // workgroup -> (split, tile): contiguous range per XCD, grouped along M inside it
   const int bid = blockIdx.x, nwg = gridDim.x;
   const int logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int z = logical % ksplit;
+  const int tile = logical / ksplit;
   const int per_group = GROUP_M * tiles_n;
-  const int group = logical / per_group;
+  const int group = tile / per_group;
   const int first_m = group * GROUP_M;
   const int gm = min(tiles_m - first_m, GROUP_M);
-  const int in_group = logical - group * per_group;
+  const int in_group = tile - group * per_group;
   const int tm = first_m + in_group % gm;
   const int tn = in_group / gm;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const uint32_t kbytes = (uint32_t)K * (uint32_t)sizeof(TIn);
-  const int nk = (int)((kbytes + ROWB - 1) / ROWB);
+  const int nk_all = (int)((kbytes + ROWB - 1) / ROWB);
+  const int kbeg = min(nk_all, z * steps_per_split);
+  const int nk = min(nk_all, kbeg + steps_per_split) - kbeg;
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * kbytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * kbytes);
 
-  // global chunk owned by this thread: row (tid >> 3) of each 32-row slab, chunk (tid & 7)
-  const int crow = tid >> 3, ccol = tid & 7;
-  const uint32_t g_base = (uint32_t)crow * kbytes + (uint32_t)ccol * 16u;
-  const uint32_t g_slab = 32u * kbytes;
-  const uint32_t l_base = (uint32_t)crow * ROWB + (uint32_t)((ccol ^ swz(crow)) * 16);
-
-  // fragment read offsets: operand row = lane & 15, chunk = kk * 4 + (lane >> 4)
-  const int frow = lane & 15;
-  const uint32_t f_off0 = (uint32_t)frow * ROWB + (uint32_t)((((lane >> 4)) ^ swz(frow)) * 16);
-  const uint32_t f_off1 = (uint32_t)frow * ROWB + (uint32_t)(((4 + (lane >> 4)) ^ swz(frow)) * 16);
-
-  u32x4 ga[A_CH], gb[B_CH];
-  auto gload = [&](int kt) {
-    const uint32_t kb = (uint32_t)kt * ROWB;
-    const bool in_k = kb + (uint32_t)ccol * 16u < kbytes;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ga[i] = buf_load16(ra, in_k ? g_base + i * g_slab + kb : kOOB);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) gb[i] = buf_load16(rb, in_k ? g_base + i * g_slab + kb : kOOB);
-  };
-  auto lstore = [&](int buf) {
+  // DMA: one instruction fills 8 consecutive tile rows (1 KiB); lane -> row lane/8, slot lane%8
+  const int drow = lane >> 3, dslot = lane & 7;
+  const int dchunk = dslot ^ drow;  // the chunk that lands in this lane's slot
+  const uint32_t d_goff = (uint32_t)drow * kbytes + (uint32_t)dchunk * 16u;
+  auto dload_one = [&](int kt, int buf, int g) {
+    const uint32_t kb = (uint32_t)(kbeg + kt) * ROWB;
+    const bool live = kt < nk && kb + (uint32_t)dchunk * 16u < kbytes;
     char* s = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(s + l_base + i * 32 * ROWB) = ga[i];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      *reinterpret_cast<u32x4*>(s + BM * ROWB + l_base + i * 32 * ROWB) = gb[i];
+    if (g < A_CH) {
+      const int j = wave * A_CH + g;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(s + j * 1024), 16,
+          live ? d_goff + (uint32_t)j * 8u * kbytes + kb : kOOB, 0, 0, 0);
+    } else {
+      const int j = wave * B_CH + (g - A_CH);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(s + BM * ROWB + j * 1024), 16,
+          live ? d_goff + (uint32_t)j * 8u * kbytes + kb : kOOB, 0, 0, 0);
+    }
   };
 
-  Acc acc[MI][NI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NI; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  // fragment reads: operand row = lane & 15, chunk = half * 4 + (lane >> 4)
+  const int frow = lane & 15;
+  const uint32_t foff0 = (uint32_t)frow * ROWB + (uint32_t)(((lane >> 4) ^ (frow & 7)) * 16);
+  const uint32_t foff1 = (uint32_t)frow * ROWB + (uint32_t)(((4 + (lane >> 4)) ^ (frow & 7)) * 16);
+  struct Frag {
+    u32x4 a[NMI];
+    u32x4 b[NNI];
+  };
+  auto fload_one = [&](Frag& f, int buf, int half, int q) {
+    const uint32_t fo = half ? foff1 : foff0;
+    if (q < NMI)
+      f.a[q] = *reinterpret_cast<const u32x4*>(smem + buf * STAGE + (wm * WM + q * 16) * ROWB + fo);
+    else
+      f.b[q - NMI] = *reinterpret_cast<const u32x4*>(smem + buf * STAGE + (BM + wn * WN + (q - NMI) * 16) * ROWB + fo);
+  };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  Acc acc[NMI][NNI];
+#pragma unroll
+  for (int i = 0; i < NMI; ++i)
+#pragma unroll
+    for (int j = 0; j < NNI; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  auto mma_one = [&](const Frag& f, int t) {
+    const int i = t / NNI, j = t % NNI;
+    acc[i][j] = Mfma<TIn>::mma(f.b[j], f.a[i], acc[i][j]);
+  };
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* sa = smem + cur * STAGE + (wm * WM) * ROWB;
-    const char* sb = smem + cur * STAGE + BM * ROWB + (wn * WN) * ROWB;
+  // MFMAs of Fc, interleaved with the reads of (fbuf, fhalf) into Fn (if fhalf >= 0) and
+  // with the DMA refill of k-step dk into stage dbuf (if dk >= 0)
+  auto phase = [&](const Frag& Fc, Frag& Fn, int fbuf, int fhalf, int dk, int dbuf) {
+    constexpr int G = LPS > (NF + 1) / 2 ? LPS : (NF + 1) / 2;
+    constexpr int MPG = NMM / G;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t fo = kk ? f_off1 : f_off0;
-      u32x4 fa[MI], fb[NI];
+    for (int g = 0; g < G; ++g) {
+      if (dk >= 0 && g < LPS) dload_one(dk, dbuf, g);
+      if (fhalf >= 0 && 2 * g < NF) fload_one(Fn, fbuf, fhalf, 2 * g);
+      if (fhalf >= 0 && 2 * g + 1 < NF) fload_one(Fn, fbuf, fhalf, 2 * g + 1);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * ROWB + fo);
-#pragma unroll
-      for (int j = 0; j < NI; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * ROWB + fo);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = Mfma<TIn>::mma(fb[j], fa[i], acc[i][j]);
+      for (int t = g * MPG; t < (g + 1) * MPG; ++t) mma_one(Fc, t);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int t = G * MPG; t < NMM; ++t) mma_one(Fc, t);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Every stage slot is always filled (k-steps past the range read as zero), so the
+  // number of DMA loads in flight is the same at every wait.
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int g = 0; g < LPS; ++g) dload_one(st, st, g);
+  RNL_WAIT_VM_LGKM0((NST - 1) * LPS);
+  __builtin_amdgcn_s_barrier();
+
+  Frag F0, F1;
+#pragma unroll
+  for (int q = 0; q < NF; ++q) fload_one(F0, 0, 0, q);
+  int slot = 0;
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const int nslot = (slot + 1 == NST) ? 0 : slot + 1;
+    phase(F0, F1, slot, 1, -1, 0);  // first half: read the second half's fragments
+    // k-step kt+1 has landed and this wave's reads of stage `slot` are complete
+    RNL_WAIT_VM_LGKM0((NST - 2) * LPS);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    phase(F1, F0, nslot, 0, kt + NST, slot);  // second half: refill `slot`, read next first half
+    slot = nslot;
   }
+  if (nk > 0) {
+    phase(F0, F1, slot, 1, -1, 0);
+    phase(F1, F0, 0, -1, -1, 0);
+  }
+  RNL_WAIT_VM_LGKM0(0);
 
   // epilogue: lane holds C[m][n .. n+3]
   const bool vec_ok = (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < NMI; ++i) {
     const int m = m0 + wm * WM + i * 16 + (lane & 15);
     if (m >= M) continue;
     float xsm = 0.f;
     if constexpr (EPI == EPI_DEQ_BF16 || EPI == EPI_DEQ_F32) xsm = xs[m];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NNI; ++j) {
       const int n = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
       if (n >= N) continue;
       const size_t off = (size_t)m * (size_t)N + (size_t)n;
       const bool full = vec_ok && (n + 3 < N);
-      if constexpr (EPI == EPI_I32) {
+      if constexpr (EPI == EPI_I32 || (EPI == EPI_PART && sizeof(TIn) == 1)) {
         int32_t* c = static_cast<int32_t*>(C) + off;
+        if constexpr (EPI == EPI_PART) c += (size_t)z * (size_t)M * (size_t)N;
         if (full) {
           *reinterpret_cast<i32x4*>(c) = acc[i][j];
         } else {
@@ -182,8 +246,9 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
             v[r] = (float)acc[i][j][r];
           }
         }
-        if constexpr (EPI == EPI_F32 || EPI == EPI_DEQ_F32) {
+        if constexpr (EPI == EPI_F32 || EPI == EPI_DEQ_F32 || EPI == EPI_PART) {
           float* c = static_cast<float*>(C) + off;
+          if constexpr (EPI == EPI_PART) c += (size_t)z * (size_t)M * (size_t)N;
           if (full) {
             *reinterpret_cast<f32x4*>(c) = f32x4{v[0], v[1], v[2], v[3]};
           } else {
@@ -194,8 +259,7 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
           if (full) {
             *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
-            for (int r = 0; r < 4 && n + r < N; ++r)
-              c[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xFFFFu);
+            for (int r = 0; r < 4 && n + r < N; ++r) c[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xFFFFu);
           }
         }
       }
@@ -203,43 +267,81 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
   }
 }
 
-template <typename TIn, int BM, int BN, int EPI>
-hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws,
-                       int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  const int nwg = tiles_m * tiles_n;
-  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, 8, EPI>), dim3(nwg), dim3(256), 0, s, A, B, C,
-                     xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+#undef RNL_WAIT_VM_LGKM0
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <typename TIn, int BM, int BN, int NST, int EPI>
+hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws, int64_t M,
+                       int64_t N, int64_t K, int ksplit, hipStream_t s) {
+  const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
+  const int nk = (int)cdiv(K * (int64_t)sizeof(TIn), 128);
+  const int sps = (int)cdiv(nk, ksplit);
+  const int nwg = tiles_m * tiles_n * ksplit;
+  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI>), dim3(nwg), dim3(256), 0, s, A, B, C,
+                     xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n, ksplit, sps);
   return hipGetLastError();
 }
 
-int64_t tiles_of(int64_t M, int64_t N, int bm, int bn) {
-  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+// Tile shapes, largest first: 256x192 (2 LDS stages, 112 KiB), 256x128 and 128x256
+// (3 stages, 144 KiB), 128x128 (4 stages, 128 KiB).
+enum Shape { S256x192, S256x128, S128x256, S128x128 };
+
+Shape pick_shape(int64_t M, int64_t N) {
+  // Largest tile that still gives every CU at least one workgroup.
+  if (cdiv(M, 256) * cdiv(N, 192) >= 256) return S256x192;
+  if (cdiv(M, 256) * cdiv(N, 128) >= 256) return S256x128;
+  if (cdiv(M, 128) * cdiv(N, 256) >= 256) return S128x256;
+  return S128x128;
 }
 
 template <typename TIn, int EPI>
-hipError_t launch_shape(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws,
-                        int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  // Largest tile that still gives every CU at least one workgroup.
-  if (tiles_of(M, N, 256, 192) >= 256) return launch_tile<TIn, 256, 192, EPI>(A, B, C, xs, ws, M, N, K, s);
-  if (tiles_of(M, N, 256, 128) >= 256) return launch_tile<TIn, 256, 128, EPI>(A, B, C, xs, ws, M, N, K, s);
-  return launch_tile<TIn, 128, 128, EPI>(A, B, C, xs, ws, M, N, K, s);
+hipError_t launch_shape(Shape sh, const TIn* A, const TIn* B, void* C, const float* xs, const float* ws,
+                        int64_t M, int64_t N, int64_t K, int ksplit, hipStream_t s) {
+  switch (sh) {
+    case S256x192: return launch_tile<TIn, 256, 192, 2, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    case S256x128: return launch_tile<TIn, 256, 128, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    case S128x256: return launch_tile<TIn, 128, 256, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    default: return launch_tile<TIn, 128, 128, 4, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
+  }
 }
 
 }  // namespace
 
+int gemm_split_plan(int64_t M, int64_t N, int64_t K, int elem_bytes, int* shape) {
+  // For outputs too small to fill the chip, split K so that tiles x splits reaches
+  // at least 256 workgroups with at least 8 k-steps each.
+  const Shape sh = pick_shape(M, N);
+  if (shape != nullptr) *shape = (int)sh;
+  const int64_t bm = (sh == S256x192 || sh == S256x128) ? 256 : 128;
+  const int64_t bn = sh == S256x192 ? 192 : (sh == S128x256 ? 256 : 128);
+  const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
+  const int64_t nk = cdiv(K * elem_bytes, 128);
+  int64_t ks = 1;
+  while (tiles * ks < 256 && nk / (ks * 2) >= 8) ks *= 2;
+  return (int)ks;
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
                             int64_t N, int64_t K, hipStream_t s) {
-  if (out_kind == OUT_F32) return launch_shape<uint16_t, EPI_F32>(A, B, C, nullptr, nullptr, M, N, K, s);
-  return launch_shape<uint16_t, EPI_BF16>(A, B, C, nullptr, nullptr, M, N, K, s);
+  const Shape sh = pick_shape(M, N);
+  if (out_kind == OUT_F32) return launch_shape<uint16_t, EPI_F32>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
+  return launch_shape<uint16_t, EPI_BF16>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
+}
+
+hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, float* partial, int64_t M,
+                                   int64_t N, int64_t K, int ksplit, hipStream_t s) {
+  return launch_shape<uint16_t, EPI_PART>(pick_shape(M, N), A, B, partial, nullptr, nullptr, M, N, K,
+                                          ksplit, s);
 }
 
 hipError_t launch_gemm_int8(const int8_t* A, const int8_t* B, void* C, int out_kind,
                             const float* xs, const float* ws, int64_t M, int64_t N, int64_t K,
                             hipStream_t s) {
-  if (out_kind == OUT_I32) return launch_shape<int8_t, EPI_I32>(A, B, C, xs, ws, M, N, K, s);
-  if (out_kind == OUT_F32) return launch_shape<int8_t, EPI_DEQ_F32>(A, B, C, xs, ws, M, N, K, s);
-  return launch_shape<int8_t, EPI_DEQ_BF16>(A, B, C, xs, ws, M, N, K, s);
+  const Shape sh = pick_shape(M, N);
+  if (out_kind == OUT_I32) return launch_shape<int8_t, EPI_I32>(sh, A, B, C, xs, ws, M, N, K, 1, s);
+  if (out_kind == OUT_F32) return launch_shape<int8_t, EPI_DEQ_F32>(sh, A, B, C, xs, ws, M, N, K, 1, s);
+  return launch_shape<int8_t, EPI_DEQ_BF16>(sh, A, B, C, xs, ws, M, N, K, 1, s);
 }
 
 }  // namespace rnl

@@ -19,10 +19,21 @@ hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s);
+// Same norm (bf16 out) applied to rows that are the bf16 rounding of the sum of S
+// fp32 split-K partials part[S, T, K], added in split order.
+hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,
+                                   int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s);
 
 // C[M,N] = A[M,K] . B[N,K]^T on bf16 MFMA, fp32 accumulation, C bf16 or fp32.
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);
+
+// Number of K splits the bf16/int8 GEMM would use for an output of M x N (1 when
+// the tiles alone fill the chip); elem_bytes is the operand size.
+int gemm_split_plan(int64_t M, int64_t N, int64_t K, int elem_bytes, int* shape);
+// Split-K bf16 GEMM: partial[z, M, N] (fp32) for z < ksplit; sum over z is A . B^T.
+hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, float* partial, int64_t M,
+                                   int64_t N, int64_t K, int ksplit, hipStream_t s);
 
 // acc[M,N] = A[M,K] . B[N,K]^T on int8 MFMA (int32 accumulation).  With
 // out_kind OUT_I32 C receives acc; otherwise C = fl(float(acc) * fl(xs[m] * ws[n]))

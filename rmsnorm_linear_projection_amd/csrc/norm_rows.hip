@@ -11,6 +11,10 @@
 //   n = fl(fl(xf * rstd) * gamma), bf16 out = round_nearest_even(n);
 //   int8: amax = max|n|, s = fl(127/amax), q = clamp(rint(fl(n*s)), -127, 127),
 //   x_scale = fl(amax/127); an all-zero row gives q = 0, x_scale = 0.
+//
+// The row may also be the bf16 rounding of the sum of split-K partial rows of
+// a preceding projection (the q_a -> norm step of the low-rank chain): the
+// partials are added in split order, so the result does not depend on timing.
 #include "common.cuh"
 #include "launch.h"
 
@@ -78,18 +82,41 @@ __device__ __forceinline__ uint32_t q4(const float n[8], int base, float s) {
   return r;
 }
 
+// Row sources: chunk idx (8 consecutive elements, packed bf16) of row t.
+struct RowBf16 {
+  const uint16_t* x;  // [T, K] bf16
+  int64_t K;
+  __device__ u32x4 operator()(int64_t t, int idx) const {
+    return reinterpret_cast<const u32x4*>(x + t * K)[idx];
+  }
+};
+struct RowPartials {
+  const float* part;  // [S, T, K] fp32
+  int64_t TK;         // T * K
+  int64_t K;
+  int S;
+  __device__ u32x4 operator()(int64_t t, int idx) const {
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+    for (int z = 0; z < S; ++z) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)z * (size_t)TK + (size_t)t * (size_t)K) + 2 * idx;
+      lo += p[0];
+      hi += p[1];
+    }
+    return u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                 pack_bf16x2(hi[2], hi[3])};
+  }
+};
+
 // CPT > 0: each thread keeps CPT 16-byte chunks of the row in registers.
-// CPT == 0: the row is re-read from global memory for each pass.
-template <int CPT, bool INT8>
+// CPT == 0: the row is re-read (re-derived) for each pass.
+template <int CPT, bool INT8, class Row>
 __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps, float inv_k,
-    int64_t K, void* __restrict__ out, float* __restrict__ x_scale_out,
-    float* __restrict__ rstd_out) {
+    Row row, const uint16_t* __restrict__ gamma, float eps, float inv_k, int64_t K,
+    void* __restrict__ out, float* __restrict__ x_scale_out, float* __restrict__ rstd_out) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int nch = (int)(K >> 3);
-  const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * K);
   const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
 
   constexpr int NV = CPT > 0 ? CPT : 1;
@@ -99,11 +126,11 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * kThreads;
-      v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+      v[c] = idx < nch ? row(t, idx) : u32x4{0u, 0u, 0u, 0u};
       ss += sumsq8(v[c]);
     }
   } else {
-    for (int idx = tid; idx < nch; idx += kThreads) ss += sumsq8(xr[idx]);
+    for (int idx = tid; idx < nch; idx += kThreads) ss += sumsq8(row(t, idx));
   }
   const float S = block_sum(ss, red);
   const float rstd = rstd_from_sumsq(S, inv_k, eps);
@@ -124,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
         if (idx < nch) emit(v[c], idx);
       }
     } else {
-      for (int idx = tid; idx < nch; idx += kThreads) emit(xr[idx], idx);
+      for (int idx = tid; idx < nch; idx += kThreads) emit(row(t, idx), idx);
     }
   } else {
     float amax = 0.f;
@@ -141,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
         if (idx < nch) amax_of(v[c], idx);
       }
     } else {
-      for (int idx = tid; idx < nch; idx += kThreads) amax_of(xr[idx], idx);
+      for (int idx = tid; idx < nch; idx += kThreads) amax_of(row(t, idx), idx);
     }
     amax = block_max(amax, red);
     const float s = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
@@ -159,20 +186,21 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
         if (idx < nch) emit(v[c], idx);
       }
     } else {
-      for (int idx = tid; idx < nch; idx += kThreads) emit(xr[idx], idx);
+      for (int idx = tid; idx < nch; idx += kThreads) emit(row(t, idx), idx);
     }
   }
 }
 
-template <bool INT8>
-hipError_t launch_norm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T, int64_t K,
-                       void* out, float* x_scale_out, float* rstd_out, hipStream_t s) {
+template <bool INT8, class Row>
+hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int64_t K, void* out,
+                       float* x_scale_out, float* rstd_out, hipStream_t s) {
   const float inv_k = 1.0f / (float)K;  // fl(1/K): K < 2^24 converts exactly
   const int64_t nch = K / 8;
   const int64_t per = (nch + kThreads - 1) / kThreads;
   dim3 grid((unsigned)T), block(kThreads);
-#define RNL_NORM_LAUNCH(C) \
-  hipLaunchKernelGGL((norm_rows_kernel<C, INT8>), grid, block, 0, s, x, gamma, eps, inv_k, K, out, x_scale_out, rstd_out)
+#define RNL_NORM_LAUNCH(C)                                                                              \
+  hipLaunchKernelGGL((norm_rows_kernel<C, INT8, Row>), grid, block, 0, s, row, gamma, eps, inv_k, K, out, \
+                     x_scale_out, rstd_out)
   if (per <= 1) RNL_NORM_LAUNCH(1);
   else if (per <= 2) RNL_NORM_LAUNCH(2);
   else if (per <= 4) RNL_NORM_LAUNCH(4);
@@ -186,13 +214,18 @@ hipError_t launch_norm(const uint16_t* x, const uint16_t* gamma, float eps, int6
 
 hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
-  return launch_norm<false>(x, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
+  return launch_norm<false>(RowBf16{x, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
 
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s) {
-  return launch_norm<true>(x, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+  return launch_norm<true>(RowBf16{x, K}, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+}
+
+hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,
+                                   int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s) {
+  return launch_norm<false>(RowPartials{part, T * K, K, S}, gamma, eps, T, K, out, nullptr, rstd_out, s);
 }
 
 }  // namespace rnl

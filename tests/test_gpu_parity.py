@@ -318,6 +318,8 @@ def check_chain_case(case, rows=None):
     (37, 256, 64, 80, True),
     (5, 128, 48, 30, False),
     (300, 520, 136, 260, True),
+    (64, 4096, 128, 64, True),  # stage 1 split over K (8 slices)
+    (50, 2056, 72, 33, False),  # split over K with a K tail
 ])
 def test_chain_small(T, K, R, N, gamma):
     check_chain_case(synthetic.chain_case(T, K, R, N, seed=T + R, gamma=gamma))
@@ -329,3 +331,57 @@ def test_mla_q_chain_full_size():
     y1 = check_chain_case(case, rows=sample_rows(1024, 24))
     y2, _, _ = run_chain(case)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+
+
+# ---------------------------------------------------------------------------
+# the atoms: AT-03 RMSNorm, AT-03 + AT-05 quant, AT-09 Linear (BF16, INT8)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,K", [(7, 64), (130, 4104), (3, 20480)])
+def test_atom_rms_norm_bf16(T, K):
+    case = synthetic.norm_linear_case(T, K, 1, seed=T + K)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y = rnl.rms_norm_bf16(dev(case["x"]), dev(case["gamma"]), EPS, rstd_out=rstd)
+    torch.cuda.synchronize()
+    xb, gb = bits(case["x"]), bits(case["gamma"])
+    r = rstd.cpu().numpy()
+    _, r_own = O.rms_norm_rows(xb, gb, EPS)
+    assert_rstd(r, r_own, "rms_norm_bf16")
+    n, _ = O.rms_norm_rows(xb, gb, EPS, rstd=r)
+    assert np.array_equal(bits(y.cpu()), O.f32_to_bf16_bits(n)), "normed rows not bit-exact given rstd"
+
+
+@pytest.mark.parametrize("T,K", [(9, 64), (65, 4112)])
+def test_atom_rms_norm_quant_int8(T, K):
+    case = synthetic.int8_case(T, K, 1, seed=T)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    xq, xs = rnl.rms_norm_quant_int8(dev(case["x"]), dev(case["gamma"]), EPS, rstd_out=rstd)
+    torch.cuda.synchronize()
+    n, _ = O.rms_norm_rows(bits(case["x"]), bits(case["gamma"]), EPS, rstd=rstd.cpu().numpy())
+    q, s, _ = O.quant_rows(n)
+    assert np.array_equal(xq.cpu().numpy(), q) and np.array_equal(xs.cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("M,K,N", [(33, 72, 17), (300, 1032, 200), (4000, 264, 6100)])
+def test_atom_linear_bf16(M, K, N):
+    a = synthetic.normal((M, K), 1.0, 3, 11)
+    W = synthetic.normal((N, K), 1.0 / np.sqrt(K), 3, 12)
+    y = rnl.linear_bf16(dev(a), dev(W), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    ref = O.project_bf16(O.bf16_bits_to_f32(bits(a)[rows]), bits(W))
+    assert_bf16_close(f32(y)[rows], ref, "linear_bf16")
+
+
+@pytest.mark.parametrize("M,K,N", [(33, 64, 17), (257, 4112, 130)])
+def test_atom_linear_int8(M, K, N):
+    q = synthetic.int8_uniform((M, K), 4, 1)
+    W = synthetic.int8_uniform((N, K), 4, 2)
+    xs = synthetic.uniform((M,), 1e-3, 1e-2, 4, 3, dtype=torch.float32)
+    ws = synthetic.uniform((N,), 1e-3, 1e-2, 4, 4, dtype=torch.float32)
+    acc = rnl.linear_int8(dev(q), dev(xs), dev(W), dev(ws), out_dtype=torch.int32)
+    y = rnl.linear_int8(dev(q), dev(xs), dev(W), dev(ws), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    acc_ref = O.int8_gemm(q.numpy(), W.numpy())
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    y_ref = O.dequant(acc_ref, xs.numpy(), ws.numpy())
+    assert np.array_equal(y.cpu().numpy(), y_ref)
