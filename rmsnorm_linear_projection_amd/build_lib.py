@@ -29,6 +29,12 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# per-source code-generation options (see the source's header comment)
+EXTRA_FLAGS = {
+    "gemm_int8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def flags() -> list[str]:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
@@ -46,7 +52,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [hipcc, *flags(), "-x", "hip", "-c", src, "-o", obj]
+        cmd = [hipcc, *flags(), *EXTRA_FLAGS.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -1,0 +1,34 @@
+// bf16 instantiations of the projection GEMM (kernel in gemm_kernel.cuh).
+#include "gemm_kernel.cuh"
+
+namespace rnl {
+using namespace gemm_detail;
+
+int gemm_split_plan(int64_t M, int64_t N, int64_t K, int elem_bytes, int* shape) {
+  // For outputs too small to fill the chip, split K so that tiles x splits reaches
+  // at least 256 workgroups with at least 8 k-steps each.
+  const Shape sh = pick_shape(M, N);
+  if (shape != nullptr) *shape = (int)sh;
+  const int64_t bm = (sh == S256x192 || sh == S256x128) ? 256 : 128;
+  const int64_t bn = sh == S256x192 ? 192 : (sh == S128x256 ? 256 : 128);
+  const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
+  const int64_t nk = cdiv(K * elem_bytes, 128);
+  int64_t ks = 1;
+  while (tiles * ks < 256 && nk / (ks * 2) >= 8) ks *= 2;
+  return (int)ks;
+}
+
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
+                            int64_t N, int64_t K, hipStream_t s) {
+  const Shape sh = pick_shape(M, N);
+  if (out_kind == OUT_F32) return launch_shape<uint16_t, EPI_F32>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
+  return launch_shape<uint16_t, EPI_BF16>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
+}
+
+hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, float* partial, int64_t M,
+                                   int64_t N, int64_t K, int ksplit, hipStream_t s) {
+  return launch_shape<uint16_t, EPI_PART>(pick_shape(M, N), A, B, partial, nullptr, nullptr, M, N, K,
+                                          ksplit, s);
+}
+
+}  // namespace rnl

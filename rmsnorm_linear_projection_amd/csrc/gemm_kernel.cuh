@@ -31,14 +31,19 @@
 // round-robin) works on a contiguous block of tiles, grouped GROUP_M tiles
 // tall, which share A and B panels in that XCD's L2.
 //
+// The kernel template lives in this header so that the bf16 and int8 instantiations
+// can be compiled as separate units with different code-generation options.
+//
 // Split-K: with KSPLIT > 1 the grid holds KSPLIT workgroups per tile, each
 // reducing one contiguous range of k-steps and writing a partial tile (fp32 or
 // int32) to slice z of a [KSPLIT, M, N] buffer; the caller reduces the slices.
+#pragma once
+
 #include "common.cuh"
 #include "launch.h"
 
 namespace rnl {
-namespace {
+namespace gemm_detail {
 
 template <typename TIn>
 struct Mfma;
@@ -207,10 +212,10 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
     phase(F1, F0, nslot, 0, kt + NST, slot);  // second half: refill `slot`, read next first half
     slot = nslot;
   }
-  if (nk > 0) {
-    phase(F0, F1, slot, 1, -1, 0);
-    phase(F1, F0, 0, -1, -1, 0);
-  }
+  // last k-step (an empty split range only ever loaded zero-filled stages, so these
+  // MFMAs add nothing and need no guard)
+  phase(F0, F1, slot, 1, -1, 0);
+  phase(F1, F0, 0, -1, -1, 0);
   RNL_WAIT_VM_LGKM0(0);
 
   // epilogue: lane holds C[m][n .. n+3]
@@ -269,7 +274,7 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
 
 #undef RNL_WAIT_VM_LGKM0
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename TIn, int BM, int BN, int NST, int EPI>
 hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws, int64_t M,
@@ -287,7 +292,7 @@ hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, con
 // (3 stages, 144 KiB), 128x128 (4 stages, 128 KiB).
 enum Shape { S256x192, S256x128, S128x256, S128x128 };
 
-Shape pick_shape(int64_t M, int64_t N) {
+inline Shape pick_shape(int64_t M, int64_t N) {
   // Largest tile that still gives every CU at least one workgroup.
   if (cdiv(M, 256) * cdiv(N, 192) >= 256) return S256x192;
   if (cdiv(M, 256) * cdiv(N, 128) >= 256) return S256x128;
@@ -306,42 +311,5 @@ hipError_t launch_shape(Shape sh, const TIn* A, const TIn* B, void* C, const flo
   }
 }
 
-}  // namespace
-
-int gemm_split_plan(int64_t M, int64_t N, int64_t K, int elem_bytes, int* shape) {
-  // For outputs too small to fill the chip, split K so that tiles x splits reaches
-  // at least 256 workgroups with at least 8 k-steps each.
-  const Shape sh = pick_shape(M, N);
-  if (shape != nullptr) *shape = (int)sh;
-  const int64_t bm = (sh == S256x192 || sh == S256x128) ? 256 : 128;
-  const int64_t bn = sh == S256x192 ? 192 : (sh == S128x256 ? 256 : 128);
-  const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
-  const int64_t nk = cdiv(K * elem_bytes, 128);
-  int64_t ks = 1;
-  while (tiles * ks < 256 && nk / (ks * 2) >= 8) ks *= 2;
-  return (int)ks;
-}
-
-hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
-                            int64_t N, int64_t K, hipStream_t s) {
-  const Shape sh = pick_shape(M, N);
-  if (out_kind == OUT_F32) return launch_shape<uint16_t, EPI_F32>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
-  return launch_shape<uint16_t, EPI_BF16>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
-}
-
-hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, float* partial, int64_t M,
-                                   int64_t N, int64_t K, int ksplit, hipStream_t s) {
-  return launch_shape<uint16_t, EPI_PART>(pick_shape(M, N), A, B, partial, nullptr, nullptr, M, N, K,
-                                          ksplit, s);
-}
-
-hipError_t launch_gemm_int8(const int8_t* A, const int8_t* B, void* C, int out_kind,
-                            const float* xs, const float* ws, int64_t M, int64_t N, int64_t K,
-                            hipStream_t s) {
-  const Shape sh = pick_shape(M, N);
-  if (out_kind == OUT_I32) return launch_shape<int8_t, EPI_I32>(sh, A, B, C, xs, ws, M, N, K, 1, s);
-  if (out_kind == OUT_F32) return launch_shape<int8_t, EPI_DEQ_F32>(sh, A, B, C, xs, ws, M, N, K, 1, s);
-  return launch_shape<int8_t, EPI_DEQ_BF16>(sh, A, B, C, xs, ws, M, N, K, 1, s);
-}
-
+}  // namespace gemm_detail
 }  // namespace rnl
