@@ -52,7 +52,7 @@ WORKLOADS = {
 }
 DEFAULT = "preattn_qkv_T4096"
 KERNEL_SOURCES = {
-    "gemm": ["gemm.hip", "common.cuh"],
+    "gemm": ["gemm_kernel.cuh", "gemm_bf16.hip", "gemm_int8.hip", "common.cuh"],
     "decode": ["decode.hip", "common.cuh"],
     "skinny": ["skinny.hip", "common.cuh"],
 }
@@ -180,18 +180,43 @@ class Setup:
         torch.cuda.synchronize()
 
 
-def time_loop(fn, steps, warmup):
+def time_loop(fn, steps, warmup, graph=True):
+    """Average ms per call of fn(i) over `steps` calls after `warmup` calls.
+
+    With graph=True the `steps` calls are captured once into a HIP graph and the
+    timed region is one replay, so host-side launch overhead (Python, ctypes)
+    does not leak into the device time; the captured work is exactly the
+    eager calls' kernels on the same stream.  Events bracket the region on
+    the stream the kernels run on, after a device synchronisation.
+    """
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        fn(warmup + i)
-    end.record()
-    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    fn(warmup + i)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()  # untimed replay: first-touch of the graph's resources
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        del g
+    else:
+        start.record()
+        for i in range(steps):
+            fn(warmup + i)
+        end.record()
+        torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms
 
 
@@ -254,13 +279,13 @@ def cpu_baseline(setup, target_s=8.0):
             "sample": f"first {rows} of {T} token rows, {calls} call(s), {per_call:.3f} s per call"}
 
 
-def bench_one(name, steps, warmup, with_cpu=True):
+def bench_one(name, steps, warmup, with_cpu=True, graph=True):
     import torch
 
     w = WORKLOADS[name]
     s = Setup(name, w)
-    ms = time_loop(s.step, steps, warmup)
-    kms = time_loop(s.kern, steps, warmup) if s.kern is not s.step else ms
+    ms = time_loop(s.step, steps, warmup, graph)
+    kms = time_loop(s.kern, steps, warmup, graph) if s.kern is not s.step else ms
     if w["bound"] == "hbm":
         value, unit = bytes_of(w) / (ms * 1e-3) / 1e9, "GB/s"
     else:
@@ -287,7 +312,8 @@ def bench_one(name, steps, warmup, with_cpu=True):
         "data": "synthetic",
         "config": {"workload": s.case.name, "description": w["desc"],
                    **{k: w[k] for k in ("T", "K", "R", "N") if k in w},
-                   "parallelism": "none (1 GPU)", "input_copies": s.copies},
+                   "parallelism": "none (1 GPU)", "input_copies": s.copies,
+                   "timing": "hip graph of the timed steps" if graph else "eager launches"},
         "roofline": {"bound": bound, "kernel": s.kernel, "achieved": round(achieved, 3), "peak": PEAK[peak_key],
                      "unit": ru, "frac": round(achieved / PEAK[peak_key], 4),
                      "kernel_ms": round(kms, 6),
@@ -308,6 +334,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not supported",
@@ -326,7 +353,8 @@ def main():
         __graft_entry__.build()
     names = sorted(WORKLOADS, key=lambda n: n != DEFAULT) if args.all else [args.workload]
     for n in names:
-        print(json.dumps(bench_one(n, args.steps, args.warmup, with_cpu=not args.no_cpu)), flush=True)
+        print(json.dumps(bench_one(n, args.steps, args.warmup, with_cpu=not args.no_cpu, graph=not args.eager)),
+              flush=True)
 
 
 if __name__ == "__main__":

@@ -87,8 +87,9 @@ extern "C" {
  *   reduction over K is split across workgroups and added in a fixed order,
  *   so repeated calls give identical results.
  *
- * Errors: RNL_ERR_NULL (x, W or y NULL), RNL_ERR_SHAPE, RNL_ERR_DTYPE
- * (w_dtype not BF16/FP32, out_dtype not BF16/FP32), RNL_ERR_ARG,
+ * Errors: RNL_ERR_NULL (x, W or y NULL), RNL_ERR_SHAPE (also N > 2^20 with
+ * fp32 weights), RNL_ERR_DTYPE (w_dtype not BF16/FP32, out_dtype not
+ * BF16/FP32), RNL_ERR_ARG,
  * RNL_ERR_ALIGN, RNL_ERR_WORKSPACE, RNL_ERR_HIP.
  */
 RNL_API int rmsnorm_linear_bf16(const void* x, const void* gamma, float eps, const void* W, int w_dtype,

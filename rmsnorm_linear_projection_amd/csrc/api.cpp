@@ -38,6 +38,7 @@ int hip_status(hipError_t e, const char* what) {
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxK_int8 = 133144;  // K * 127 * 127 <= 2^31 - 1
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 32-bit tile offsets in range
+constexpr int64_t kMaxN_fp32w = int64_t(1) << 20;  // fp32 weights: column blocks of 32 fit one grid axis
 constexpr int64_t kDecodeMaxT = 16;
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -128,6 +129,7 @@ int rmsnorm_linear_bf16(const void* x, const void* gamma, float eps, const void*
   RNL_TRY(check_dims(T, K, N, kMaxK));
   if (w_dtype != RNL_BF16 && w_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "w_dtype must be RNL_BF16 or RNL_FP32");
   if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
+  if (w_dtype == RNL_FP32 && N > kMaxN_fp32w) return fail(RNL_ERR_SHAPE, "fp32 weights need N <= 2^20");
   RNL_TRY(check_eps(eps));
   RNL_ALIGN(x, 16, "x");
   RNL_ALIGN(gamma, 16, "gamma");

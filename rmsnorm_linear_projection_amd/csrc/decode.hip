@@ -7,11 +7,11 @@
 // weight row is consumed by one wavefront in consecutive steps.
 //
 // Per workgroup:
-//   1. the first batch of weight loads is issued;
+//   1. the first batch of weight, x and gamma loads is issued;
 //   2. each wavefront sums x^2 over its quarter of K for the T rows; the four
 //      quarters are combined through LDS and every lane derives rstd for its
 //      token (AT-10 page section 3, variant B, fp32);
-//   3. for each 32-wide k-step, x is re-read (L2 hit), normed in fp32
+//   3. for each 32-wide k-step, x (re-read, an L2 hit) is normed in fp32
 //      (fl(fl(x * rstd) * gamma)), rounded to bf16 and fed with the weight
 //      fragment to v_mfma_f32_16x16x32_bf16 (weight = MFMA A source, 16 rows;
 //      tokens = MFMA B source, 16 columns, rows >= T read as zero);
@@ -23,7 +23,8 @@
 namespace rnl {
 namespace {
 
-constexpr int kU = 8;  // k-steps of weight in flight per wavefront and batch
+constexpr int kU = 4;   // k-steps of weight per prefetch batch
+constexpr int kXS = 32; // x chunks per round trip of the sum-of-squares pass
 
 __device__ __forceinline__ float sumsq8(u32x4 w) {
   float s = 0.f;
@@ -53,7 +54,7 @@ __device__ __forceinline__ u32x4 norm_bf16x8(u32x4 xv, u32x4 gv, float rstd) {
 }
 
 template <bool GAMMA, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma, float eps,
                                                      float inv_k, const uint16_t* __restrict__ W,
                                                      void* __restrict__ y, float* __restrict__ rstd_out,
@@ -72,25 +73,42 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * K, (uint32_t)min(16, N - n0) * kbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, GAMMA ? kbytes : 0u);
-  const uint32_t x_row = (uint32_t)t * kbytes, w_row = (uint32_t)t * kbytes;  // lane & 15 is both
+  const uint32_t row_off = (uint32_t)t * kbytes;  // lane & 15 is the token row and the weight row
+  // byte offset of k-step s inside a row for this lane, or kOOB past the range
   auto koff = [&](int s) -> uint32_t {
     const uint32_t kb = (uint32_t)(s * 32 + g * 8) * 2u;
-    return kb < kbytes ? kb : kOOB;
+    return (s < s_end && kb < kbytes) ? kb : kOOB;
   };
-  auto wload = [&](int s) -> u32x4 {
-    const uint32_t k = koff(s);
-    return (s < s_end) ? buf_load16(rw, k == kOOB ? kOOB : w_row + k) : u32x4{0u, 0u, 0u, 0u};
-  };
+  auto at = [&](uint32_t k, uint32_t base) -> uint32_t { return k == kOOB ? kOOB : base + k; };
 
-  u32x4 wcur[kU];
+  // Operands of a batch of kU k-steps: weight rows, raw x rows and gamma, requested
+  // together one batch ahead of their use (vector memory requests complete in
+  // order, so a use never waits on a later prefetch).
+  struct Batch {
+    u32x4 w[kU], x[kU], g[kU];
+  };
+  auto issue = [&](Batch& b, int s0) {
 #pragma unroll
-  for (int u = 0; u < kU; ++u) wcur[u] = wload(s_beg + u);
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t k = koff(s0 + u);
+      b.w[u] = buf_load16(rw, at(k, row_off));
+      b.x[u] = buf_load16(rx, at(k, row_off));
+      if constexpr (GAMMA) b.g[u] = buf_load16(rg, k);
+      else b.g[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
-  // phase 1: sum of squares of token t over this wavefront's quarter of K
+  // phase 1: first weight batch in flight, then the sum of squares of token t over
+  // this wavefront's quarter of K, kXS x chunks per round trip
+  Batch cur;
+  issue(cur, s_beg);
   float ss = 0.f;
-  for (int s = s_beg; s < s_end; ++s) {
-    const uint32_t k = koff(s);
-    ss += sumsq8(buf_load16(rx, k == kOOB ? kOOB : x_row + k));
+  for (int s0 = s_beg; s0 < s_end; s0 += kXS) {
+    u32x4 xb[kXS];
+#pragma unroll
+    for (int i = 0; i < kXS; ++i) xb[i] = buf_load16(rx, at(koff(s0 + i), row_off));
+#pragma unroll
+    for (int i = 0; i < kXS; ++i) ss += sumsq8(xb[i]);
   }
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
@@ -100,32 +118,31 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   const float rstd = rstd_from_sumsq(S, inv_k, eps);
   if (rstd_out != nullptr && blockIdx.x == 0 && tid < T) rstd_out[tid] = rstd;
 
-  // phase 2: normed bf16 tokens x weight rows on MFMA
+  // phase 2: normed bf16 tokens x weight rows on MFMA.  Two batch buffers alternate
+  // (the loop is unrolled by two) so that no batch is ever copied: a register copy
+  // of a prefetched batch would wait for its loads.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = s_beg; s0 < s_end; s0 += kU) {
-    u32x4 wnext[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) wnext[u] = wload(s0 + kU + u);
-    u32x4 xv[kU], gv[kU];
+  auto consume = [&](const Batch& b) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const uint32_t k = koff(s0 + u);
-      const bool live = s0 + u < s_end;
-      xv[u] = buf_load16(rx, (!live || k == kOOB) ? kOOB : x_row + k);
-      if constexpr (GAMMA) gv[u] = buf_load16(rg, live ? k : kOOB);
-      else gv[u] = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 a = norm_bf16x8<GAMMA>(b.x[u], b.g[u], rstd);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.w[u]),
+                                                    __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (s0 + u < s_end) {
-        const u32x4 a = norm_bf16x8<GAMMA>(xv[u], gv[u], rstd);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wcur[u]),
-                                                      __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) wcur[u] = wnext[u];
+  };
+  Batch alt;
+  int s0 = s_beg;
+  for (; s0 + kU < s_end; s0 += 2 * kU) {
+    issue(alt, s0 + kU);
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the next batch go out first
+    consume(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(cur, s0 + 2 * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(alt);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (s0 < s_end) consume(cur);  // an odd batch count leaves one batch in `cur`
 
   if (wave > 0) red_acc[wave - 1][lane] = acc;
   __syncthreads();

@@ -3,9 +3,9 @@
 // e.g. [B, 28672] x [28672, 24]).
 //
 // The output is tiny, so the only parallelism is along K: the reduction is
-// split into S contiguous ranges, each workgroup producing fp32 partial dot
-// products and partial sums of squares for 64 tokens x 32 output columns; a
-// second kernel adds the S partials in a fixed order (bit-reproducible) and
+// split into S contiguous ranges of 512 k, each workgroup producing fp32 partial
+// dot products and partial sums of squares for 64 tokens x 32 output columns;
+// a second kernel adds the S partials in a fixed order (bit-reproducible) and
 // applies rstd.
 //
 // x is read exactly once.  Without a gamma, n = x * rstd, so
@@ -72,27 +72,46 @@ __device__ __forceinline__ f32x4 mma(u32x4 p, u32x4 q, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
 }
 
+// One workgroup: 64 tokens x 32 output columns x one K range of 4 * kSPW k-steps
+// (32 k each); wavefront w takes kSPW consecutive k-steps.  Each wavefront
+// issues all of its loads (x, weight, gamma) before the first MFMA, so the whole
+// grid's data is requested in one round trip.
+constexpr int kSPW = 4;
+
 template <bool GAMMA>
 __global__ __launch_bounds__(256) void skinny_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, const float* __restrict__ W,
-    float* __restrict__ part, float* __restrict__ ss_part, int T, int K, int N, int Npad,
-    int steps_per_split) {
+    float* __restrict__ part, float* __restrict__ ss_part, int T, int K, int N, int Npad) {
   __shared__ f32x4 red[3][8][64];
   __shared__ float red_ss[4][kTG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kTG, z = blockIdx.y, nc0 = blockIdx.z * kNC;
   const bool do_ss = blockIdx.z == 0;
-
-  const int nsteps = (K + 31) / 32;
-  const int zb = min(nsteps, z * steps_per_split), ze = min(nsteps, zb + steps_per_split);
-  const int per = (ze - zb + 3) / 4;
-  const int s_beg = min(ze, zb + wave * per), s_end = min(ze, s_beg + per);
+  const int s_beg = (z * 4 + wave) * kSPW;  // first k-step of this wavefront
 
   const uint32_t kbytes = (uint32_t)K * 2u, wbytes = (uint32_t)K * 4u;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t0 * K, (uint32_t)min(kTG, T - t0) * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)nc0 * K, (uint32_t)min(kNC, N - nc0) * wbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, GAMMA ? kbytes : 0u);
+
+  u32x4 xv[kSPW][4], w0[kSPW][2], w1[kSPW][2], gv[kSPW];
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) {
+    const int k = (s_beg + u) * 32 + g * 8;
+    const bool in_k = k < K;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      xv[u][tb] = buf_load16(rx, in_k ? (uint32_t)(tb * 16 + r16) * kbytes + (uint32_t)k * 2u : kOOB);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t base = (uint32_t)(nb * 16 + r16) * wbytes + (uint32_t)k * 4u;
+      w0[u][nb] = buf_load16(rw, in_k ? base : kOOB);
+      w1[u][nb] = buf_load16(rw, in_k ? base + 16u : kOOB);
+    }
+    if constexpr (GAMMA) gv[u] = buf_load16(rg, in_k ? (uint32_t)k * 2u : kOOB);
+    else gv[u] = u32x4{0u, 0u, 0u, 0u};
+  }
 
   f32x4 acc[4][2];
 #pragma unroll
@@ -101,47 +120,37 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[4] = {0.f, 0.f, 0.f, 0.f};
 
-  for (int s = s_beg; s < s_end; ++s) {
-    const int k = s * 32 + g * 8;
-    const bool in_k = k < K;
-    u32x4 xv[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      xv[tb] = buf_load16(rx, in_k ? (uint32_t)(tb * 16 + r16) * kbytes + (uint32_t)k * 2u : kOOB);
+  for (int u = 0; u < kSPW; ++u) {
     float wv[2][8];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint32_t base = (uint32_t)(nb * 16 + r16) * wbytes + (uint32_t)k * 4u;
-      const u32x4 w0 = buf_load16(rw, in_k ? base : kOOB);
-      const u32x4 w1 = buf_load16(rw, in_k ? base + 16u : kOOB);
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        wv[nb][j] = __uint_as_float(w0[j]);
-        wv[nb][4 + j] = __uint_as_float(w1[j]);
+        wv[nb][j] = __uint_as_float(w0[u][nb][j]);
+        wv[nb][4 + j] = __uint_as_float(w1[u][nb][j]);
       }
-    }
     if constexpr (GAMMA) {
-      const u32x4 gv = buf_load16(rg, in_k ? (uint32_t)k * 2u : kOOB);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          wv[nb][2 * j] = __fmul_rn(wv[nb][2 * j], bf16lo(gv[j]));
-          wv[nb][2 * j + 1] = __fmul_rn(wv[nb][2 * j + 1], bf16hi(gv[j]));
+          wv[nb][2 * j] = __fmul_rn(wv[nb][2 * j], bf16lo(gv[u][j]));
+          wv[nb][2 * j + 1] = __fmul_rn(wv[nb][2 * j + 1], bf16hi(gv[u][j]));
         }
     }
     if (do_ss) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) ss[tb] += sumsq8(xv[tb]);
+      for (int tb = 0; tb < 4; ++tb) ss[tb] += sumsq8(xv[u][tb]);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const Split3 p = split_w(wv[nb]);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        acc[tb][nb] = mma(p.hi, xv[tb], acc[tb][nb]);
-        acc[tb][nb] = mma(p.mid, xv[tb], acc[tb][nb]);
-        acc[tb][nb] = mma(p.lo, xv[tb], acc[tb][nb]);
+        acc[tb][nb] = mma(p.hi, xv[u][tb], acc[tb][nb]);
+        acc[tb][nb] = mma(p.mid, xv[u][tb], acc[tb][nb]);
+        acc[tb][nb] = mma(p.lo, xv[u][tb], acc[tb][nb]);
       }
     }
   }
@@ -185,21 +194,47 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(
   }
 }
 
+// Finalize: workgroup (t, column block of 64).  Lane c of wavefront w adds the
+// partials z = w, w + 4, w + 8, ... of column c (eight loads in flight per
+// round), then the four wavefront sums are added in wavefront order, so the
+// summation order depends only on S and the result is bit-reproducible.
+constexpr int kFinZ = 8;
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void skinny_finalize_kernel(
     const float* __restrict__ part, const float* __restrict__ ss_part, void* __restrict__ y,
     float* __restrict__ rstd_out, int T, int N, int Npad, int S, float inv_k, float eps) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)T * N) return;
-  const int t = (int)(idx / N), n = (int)(idx % N);
-  float sq = 0.f, acc = 0.f;
-  for (int z = 0; z < S; ++z) {
-    sq += ss_part[(size_t)z * T + t];
-    acc += part[((size_t)z * T + t) * Npad + n];
+  __shared__ float red[2][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x, n = blockIdx.y * 64 + lane;
+  const bool col = n < N;
+  float acc = 0.f, sq = 0.f;
+  for (int z0 = wave; z0 < S; z0 += 4 * kFinZ) {
+    float p[kFinZ], q[kFinZ];
+#pragma unroll
+    for (int i = 0; i < kFinZ; ++i) {
+      const int z = z0 + 4 * i;
+      const bool ok = z < S;
+      p[i] = (ok && col) ? part[((size_t)z * T + t) * Npad + n] : 0.f;
+      q[i] = ok ? ss_part[(size_t)z * T + t] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kFinZ; ++i) {
+      acc += p[i];
+      sq += q[i];
+    }
   }
+  red[0][wave][lane] = acc;
+  red[1][wave][lane] = sq;
+  __syncthreads();
+  if (wave != 0) return;
+  acc = ((red[0][0][lane] + red[0][1][lane]) + red[0][2][lane]) + red[0][3][lane];
+  sq = ((red[1][0][lane] + red[1][1][lane]) + red[1][2][lane]) + red[1][3][lane];
   const float rstd = rstd_from_sumsq(sq, inv_k, eps);
   if (n == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
+  if (!col) return;
   const float v = __fmul_rn(rstd, acc);
+  const size_t idx = (size_t)t * N + n;
   if constexpr (OUT_BF16) {
     static_cast<uint16_t*>(y)[idx] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
   } else {
@@ -217,13 +252,8 @@ Plan plan_of(int64_t T, int64_t K, int64_t N) {
   p.nc = (int)((N + kNC - 1) / kNC);
   p.Npad = p.nc * kNC;
   p.nsteps = (int)((K + 31) / 32);
-  // aim for >= 512 workgroups (two per CU) with at least 4 k-steps each
-  int64_t want = (512 + (int64_t)p.tg * p.nc - 1) / ((int64_t)p.tg * p.nc);
-  int64_t maxs = p.nsteps / 4 > 0 ? p.nsteps / 4 : 1;
-  int64_t S = want < 1 ? 1 : (want > maxs ? maxs : want);
-  if (S > 256) S = 256;
-  p.sps = (int)((p.nsteps + S - 1) / S);
-  p.S = (int)((p.nsteps + p.sps - 1) / p.sps);
+  p.sps = 4 * kSPW;
+  p.S = (p.nsteps + p.sps - 1) / p.sps;
   return p;
 }
 
@@ -246,15 +276,14 @@ hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float e
   dim3 grid((unsigned)p.tg, (unsigned)p.S, (unsigned)p.nc), block(256);
   if (gamma != nullptr)
     hipLaunchKernelGGL((skinny_partial_kernel<true>), grid, block, 0, s, x, gamma, W, part, ss_part,
-                       (int)T, (int)K, (int)N, p.Npad, p.sps);
+                       (int)T, (int)K, (int)N, p.Npad);
   else
     hipLaunchKernelGGL((skinny_partial_kernel<false>), grid, block, 0, s, x, gamma, W, part, ss_part,
-                       (int)T, (int)K, (int)N, p.Npad, p.sps);
+                       (int)T, (int)K, (int)N, p.Npad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float inv_k = 1.0f / (float)K;
-  const int64_t total = T * N;
-  dim3 g2((unsigned)((total + 255) / 256));
+  dim3 g2((unsigned)T, (unsigned)((N + 63) / 64));
   if (out_kind == OUT_BF16)
     hipLaunchKernelGGL((skinny_finalize_kernel<true>), g2, block, 0, s, part, ss_part, y, rstd_out,
                        (int)T, (int)N, p.Npad, p.S, inv_k, eps);

@@ -73,6 +73,7 @@ def bf16_call(lib, x=FAKE, g=NULL, eps=1e-6, W=FAKE, wd=1, y=FAKE, od=1, rstd=NU
     (dict(K=12), "RNL_ERR_SHAPE"),
     (dict(K=(1 << 20) + 8), "RNL_ERR_SHAPE"),
     (dict(T=(1 << 24) + 1), "RNL_ERR_SHAPE"),
+    (dict(wd=2, N=(1 << 20) + 1), "RNL_ERR_SHAPE"),  # fp32 weights: N <= 2^20
     (dict(wd=3), "RNL_ERR_DTYPE"),
     (dict(od=4), "RNL_ERR_DTYPE"),
     (dict(eps=-1.0), "RNL_ERR_ARG"),
