@@ -53,7 +53,7 @@ WORKLOADS = {
 DEFAULT = "preattn_qkv_T4096"
 KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.cuh", "gemm_bf16.hip", "gemm_int8.hip", "common.cuh"],
-    "decode": ["decode.hip", "common.cuh"],
+    "small_m": ["small_m.hip", "common.cuh"],
     "skinny": ["skinny.hip", "common.cuh"],
 }
 
@@ -138,12 +138,14 @@ class Setup:
             ws = torch.empty(max(1, rnl.workspace_bytes("bf16", T, K, N)), dtype=torch.uint8, device=dev)
             Wc = t.get("W_copies", [t["W"]])
             self.step = lambda i: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], y=y, workspace=ws)
+            a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
             if T <= 16:
-                self.kernel, self.kernel_key = "decode_kernel", "decode"
-                self.kern = self.step
-                self.kern_units = ("hbm", bytes_of(w))
+                # weight streaming: the normed activations are re-read from L2,
+                # the weight (rotated) from HBM
+                self.kernel, self.kernel_key = "small_m_kernel", "small_m"
+                self.kern = lambda i: rnl.linear_bf16(a, Wc[i % len(Wc)], y=y)
+                self.kern_units = ("hbm", N * K * 2 + T * K * 2 + T * N * 2)
             else:
-                a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
                 self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
                 self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
                 self.kern_units = ("bf16", flops_of(w))
@@ -326,6 +328,69 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
     return line
 
 
+COPY_BYTES = 256 << 20  # size of the plain device copy that calibrates FETCH_SIZE / WRITE_SIZE
+KERNEL_MATCH = {"gemm": "gemm_nt_kernel", "small_m": "small_m_kernel", "skinny": "skinny_"}
+
+
+def copy_calibration(steps=5):
+    """A plain device-to-device copy of COPY_BYTES, launched `steps` times, for
+    scaling the HBM counters (each dispatch reads and writes COPY_BYTES)."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": steps}), flush=True)
+
+
+def _counter_kib(csv_path, name_part, counter, all_names=False):
+    """Per-dispatch value of `counter` (KiB) from a rocprofv3 counter_collection.csv,
+    averaged over the dispatches of the most frequent kernel whose name contains
+    name_part (the timed kernel), or, with all_names, the sum of those averages
+    over every matching kernel (a kernel pair timed as one unit)."""
+    import csv
+
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                d = per.setdefault(r["Kernel_Name"], {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} records for kernels matching {name_part!r} in {csv_path}")
+    avg = {k: sum(v.values()) / len(v) for k, v in per.items()}
+    if all_names:
+        return sum(avg.values()), min(len(v) for v in per.values())
+    top = max(per, key=lambda k: len(per[k]))
+    return avg[top], len(per[top])
+
+
+def record_counters(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Fold two rocprofv3 --pmc runs of a workload (FETCH_SIZE, then WRITE_SIZE)
+    and the same two counters of the calibration copy into profiles/counters.json."""
+    w = WORKLOADS[name]
+    key = "skinny" if w["kind"] == "fp32w" else ("small_m" if w["kind"] == "bf16" and w["T"] <= 16 else "gemm")
+    pair = key == "skinny"
+    fk, nf = _counter_kib(fetch_csv, KERNEL_MATCH[key], "FETCH_SIZE", pair)
+    wk, nw = _counter_kib(write_csv, KERNEL_MATCH[key], "WRITE_SIZE", pair)
+    cf, _ = _counter_kib(copy_fetch_csv, "", "FETCH_SIZE")
+    cw, _ = _counter_kib(copy_write_csv, "", "WRITE_SIZE")
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    data = {"workloads": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data["copy_calibration"] = {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                                "fetch_scale": COPY_BYTES / 1024.0 / cf, "write_scale": COPY_BYTES / 1024.0 / cw}
+    data["workloads"][name] = {"kernel": KERNEL_MATCH[key], "src_sha": src_sha(KERNEL_SOURCES[key]),
+                               "fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw]}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(data["workloads"][name]))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,7 +400,14 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the plain copy that calibrates the HBM byte counters")
+    ap.add_argument("--record-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="fold rocprofv3 counter_collection.csv files of --workload into profiles/counters.json")
     args = ap.parse_args()
+    if args.record_counters:
+        record_counters(args.workload, *args.record_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not supported",
               file=sys.stderr)
@@ -345,6 +417,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import rmsnorm_linear_projection_amd as rnl
 
     if not os.path.exists(rnl.LIB_PATH):

@@ -8,7 +8,7 @@
  *     ms     = fl( fl(sum_k xf^2) * fl(1/K) )         (fp32 reduction)
  *     rstd   = 1 / sqrt(ms + eps)                      (section 3, variant B)
  *     n[k]   = fl( fl(xf[k] * rstd) * float(gamma[k]) ) (gamma optional)
- *     y[t,:] = matmul(bf16(n), W, b_trans=True)        (W stored [N, K])
+ *     y[t,:] = bf16(n) . W^T                          (W stored [N, K])
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is DEVICE memory, row-major and contiguous, owned by
@@ -32,9 +32,10 @@
  *     *_workspace_bytes() query returns for the same arguments (0 means none
  *     is needed and the pointer may be NULL).  Its contents on entry do not
  *     matter and are undefined afterwards.
- *   - Environment variable RNL_VARIANT (read at every call) may force a kernel
- *     family for testing: "decode" (T <= 16 only) or "gemm"; anything else,
- *     or unset, lets the shape decide.
+ *   - bf16 projections with at most 16 activation rows run a weight-streaming
+ *     kernel, larger ones the tiled GEMM.  Environment variable RNL_VARIANT
+ *     (read at every call) set to "gemm" forces the tiled GEMM for any size,
+ *     for testing; anything else, or unset, lets the shape decide.
  */
 #ifndef RNL_H
 #define RNL_H
@@ -69,10 +70,11 @@ extern "C" {
  * rmsnorm_linear_bf16 -- fused RMSNorm -> Linear (AT-10).
  *
  * AT-10 page, section 2 (compute flow), section 3 (AT-03 RMSNorm: fp32 inside,
- * optional gamma, optional rstd output), section 4 (AT-09 BF16 mode:
- * matmul(x, w, BF16, b_trans=True)).  With w_dtype == RNL_FP32 this is the
- * SK-03 page's mhc_pre variant ("large reduction x tiny output width", FP32
- * compute): the normed rows stay fp32 and are multiplied by an fp32 weight.
+ * optional gamma, optional rstd output), section 4 (AT-09 BF16 mode: bf16
+ * operands, the weight transposed).  With w_dtype == RNL_FP32 this is the
+ * SK-03 page's mhc_pre variant (a very long reduction into a handful of
+ * output columns, computed in fp32): the normed rows stay fp32 and are
+ * multiplied by an fp32 weight.
  *
  *   x         [T, K] bf16 activations.
  *   gamma     [K] bf16 scale, or NULL for no gamma (has_gamma = false).
@@ -104,8 +106,9 @@ RNL_API size_t rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t
  * rmsnorm_linear_int8 -- fused RMSNorm -> per-token int8 quant -> int8 GEMM ->
  * dequant (AT-11 = AT-10 with AT-09's INT8 W8A8 mode).
  *
- * AT-10 page, section 4: x_int8, x_scale = AT-05(normed); y_int32 =
- * matmul(x_int8, w_int8, INT32); y = AT-06(y_int32, x_scale, w_scale).
+ * AT-10 page, section 4: the fp32 normed rows are quantised per token
+ * (AT-05), multiplied by the int8 weight with int32 accumulation, and the
+ * accumulators are dequantised with both scales (AT-06).
  * AT-05 (AT-10 page section 4; SK-03 page quant variant, common.py quant):
  * amax[t] = max_k |n[t,k]|, s = fl(127 / amax), q = saturate_+-127(rint(fl(n*s)))
  * with round-half-to-even, x_scale = fl(amax / 127); an all-zero row gives
@@ -135,10 +138,10 @@ RNL_API size_t rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t
 /*
  * norm_proj_chain -- two-stage low-rank projection q_a_proj -> RMSNorm -> q_b_proj.
  *
- * AT-10 page, section 5 (MLAProlog: q = matmul(x_tile, wq_a, BF16);
- * qr = rms_norm(q) * gamma_cq; qr = cast(qr, BF16); assemble(qr, qr_out);
- * q = matmul(qr, wq_b, BF16)) and SK-14 page section 5, orchestration mode 1
- * (serial pipeline).
+ * AT-10 page, section 5 (MLAProlog query branch: bf16 product with the
+ * down-projection weight, RMSNorm with gamma, bf16 cast, the normed rows
+ * written out, then the bf16 product with the up-projection weight) and
+ * SK-14 page section 5, orchestration mode 1 (serial pipeline).
  *
  *   x       [T, K] bf16.
  *   W_a     [R, K] bf16 (b_trans).   q_a = round_bf16(x . W_a^T)   [T, R]

@@ -14,20 +14,20 @@ Pages this follows (cited by title and section):
   section 5 (MLAProlog: q_a_proj -> norm -> q_b_proj),
   section 9 (golden reference: ``rms_norm_new`` divides x by sqrt).
 * SK-03 page -- "SK-03 Linear Projection (Norm->MatMul)": the skeleton
-  template, the quant variant (``common.py`` ``quant`` / ``quant_tensor``)
+  template, the quant variant (its per-tensor quant helper)
   and the mhc_pre variant (large reduction x tiny width, FP32 compute).
 * SK-14 page -- "SK-14 General Multi-MatMul skeleton": section 5 mode 1
   (serial pipeline, MLA q_a_proj -> norm -> q_b_proj) and the
   QuantMatMulReduceSum example (dequant as acc_fp32 * (x1_scale * x2_scale)).
 * Patterns page -- "PyPTO common coding patterns": section 9.17 table
   (eps is added before the reciprocal square root) and section 9.18 point 5
-  (``b_trans=True`` means ``a @ b.T``).
+  (a transposed second operand multiplies by the weight's rows).
 
 Conventions.  bf16 tensors are passed as ``uint16`` bit patterns, fp32 as
 ``float32``, int8 as ``int8``.  Every fp32 step is one numpy float32 operation,
 which IEEE-754 rounds to nearest even; numpy never contracts a multiply and an
-add.  Readings of points the pages leave open are marked READING and are
-listed, with their reasons, in the design notes of the repository.
+add.  Where the pages leave a point open, the docstring of the function that
+takes it says READING and gives the choice and its reason.
 """
 from __future__ import annotations
 
@@ -159,11 +159,11 @@ def rms_norm_rows_golden_div(x_bits, eps: float):
 # Projections
 # ----------------------------------------------------------------------------
 def project_bf16(n: np.ndarray, W_bits) -> np.ndarray:
-    """y = matmul(cast(n, BF16), W, b_trans=True) as fp32 [T, N].
+    """y = bf16(n) . W^T as fp32 [T, N].
 
     AT-10 page section 2 and 4: the normed rows are cast to BF16 and
-    multiplied by the weight stored [N, K] (``b_trans=True`` is ``a @ b.T``,
-    patterns page 9.18 point 5).  READING: the products of two bf16 values are
+    multiplied by the weight stored [N, K], whose rows are the output columns
+    (patterns page 9.18 point 5).  READING: the products of two bf16 values are
     exact in fp64; they are accumulated in fp64 and the result is rounded once
     to fp32.  A bf16 output is that fp32 value rounded to bf16.
     """
@@ -196,7 +196,7 @@ def quant_values(n: np.ndarray, s: np.ndarray) -> np.ndarray:
 
 
 def quant_rows(n: np.ndarray):
-    """Per-token symmetric dynamic quant (AT-05; SK-03 page ``quant_tensor``).
+    """Per-token symmetric dynamic quant (AT-05; SK-03 page quant variant).
 
     amax[t] = max_k |n[t,k]|; s = fl(127 / amax) (AT-10 page section 4: 127.0 /
     max gives the scale); q = quant_values(n, s); dequant scale x_scale =
@@ -242,7 +242,7 @@ def dequant(acc: np.ndarray, x_scale: np.ndarray, w_scale: np.ndarray) -> np.nda
 # Entry points (same names and argument meanings as the C-ABI library)
 # ----------------------------------------------------------------------------
 def rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd=None):
-    """AT-10: RMSNorm (fp32) -> bf16 cast -> matmul(W[N,K], b_trans).
+    """AT-10: RMSNorm (fp32) -> bf16 cast -> product with W[N,K] transposed.
 
     Returns (y32 fp32 [T,N], y_bf16 bits [T,N], rstd [T]).
     """
@@ -275,8 +275,8 @@ def norm_proj_chain(x_bits, Wa_bits, gamma_bits, eps, Wb_bits, rstd=None, qa_bit
     """MLA q_a_proj -> RMSNorm -> q_b_proj (AT-10 page section 5; SK-14 page
     section 5 mode 1).
 
-    q_a = bf16(matmul(x, W_a, BF16)); qr = bf16(rms_norm(q_a) * gamma) is
-    assembled into ``qr_out``; y = bf16(matmul(qr, W_b, BF16)).  If ``qa_bits``
+    q_a = bf16(x . W_a^T); qr = bf16(RMSNorm(q_a) * gamma) is the second
+    output; y = bf16(qr . W_b^T).  If ``qa_bits``
     is given (the device's q_a) the norm starts from it, and if ``rstd`` is
     given it replaces the recomputed one.  Returns a dict with qa (bits),
     qr (bits), y32 (fp32), y_bf16 (bits), rstd.

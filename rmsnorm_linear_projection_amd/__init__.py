@@ -8,7 +8,7 @@ call raises.
 
 Entry points (same names as the C ABI):
 
-* :func:`rmsnorm_linear_bf16` -- RMSNorm -> bf16 cast -> matmul(W[N,K], b_trans)
+* :func:`rmsnorm_linear_bf16` -- RMSNorm -> bf16 cast -> product with W[N,K]^T
   (fp32 weights: the normed rows stay fp32, the large-reduction split-K path);
 * :func:`rmsnorm_linear_int8` -- RMSNorm -> per-token int8 quant -> int8 GEMM ->
   dequant;
@@ -151,7 +151,7 @@ def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.b
 
 
 def rmsnorm_linear_bf16(x, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=None, y=None, workspace=None):
-    """y[T,N] = matmul(bf16(RMSNorm(x) * gamma), W[N,K], b_trans) -- AT-10.
+    """y[T,N] = bf16(RMSNorm(x) * gamma) . W[N,K]^T -- AT-10.
 
     ``W`` bf16 [N, K], or fp32 [N, K] for the fp32-compute variant.  ``gamma``
     may be None.  ``rstd_out`` (fp32 [T]) receives the per-token rstd.

@@ -39,29 +39,34 @@ constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxK_int8 = 133144;  // K * 127 * 127 <= 2^31 - 1
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 32-bit tile offsets in range
 constexpr int64_t kMaxN_fp32w = int64_t(1) << 20;  // fp32 weights: column blocks of 32 fit one grid axis
-constexpr int64_t kDecodeMaxT = 16;
+constexpr int64_t kSmallM = 16;  // at most this many activation rows: weight-streaming kernel
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-enum Variant { V_AUTO, V_DECODE, V_GEMM };
+enum Variant { V_AUTO, V_GEMM };
 
 Variant forced_variant() {
   const char* v = std::getenv("RNL_VARIANT");
-  if (v == nullptr) return V_AUTO;
-  if (std::strcmp(v, "decode") == 0) return V_DECODE;
-  if (std::strcmp(v, "gemm") == 0) return V_GEMM;
+  if (v != nullptr && std::strcmp(v, "gemm") == 0) return V_GEMM;
   return V_AUTO;
 }
 
-// bf16 weights: T <= 16 streams the weight in one fused launch, larger T runs
-// the norm pre-pass and the tiled GEMM.
-bool use_decode(int64_t T) {
-  const Variant v = forced_variant();
-  if (v == V_DECODE) return T <= kDecodeMaxT;
-  if (v == V_GEMM) return false;
-  return T <= kDecodeMaxT;
+// bf16 projections with at most 16 activation rows stream the weight with the
+// small-M kernel; larger ones use the tiled GEMM.  RNL_VARIANT=gemm forces the
+// tiled GEMM for any M.
+bool use_small_m(int64_t M) { return M <= kSmallM && forced_variant() != V_GEMM; }
+
+hipError_t project_bf16(const uint16_t* A, const uint16_t* W, void* C, int kind, int64_t M, int64_t N,
+                        int64_t K, hipStream_t s) {
+  if (use_small_m(M)) return rnl::launch_small_m_bf16(A, W, C, kind, M, N, K, 0, s);
+  return rnl::launch_gemm_bf16(A, W, C, kind, M, N, K, s);
+}
+
+// K splits of the chain's first projection (1 = none)
+int chain_splits(int64_t T, int64_t R, int64_t K) {
+  return use_small_m(T) ? 1 : rnl::gemm_split_plan(T, R, K, 2, nullptr);
 }
 
 int check_dims(int64_t T, int64_t K, int64_t N, int64_t maxK) {
@@ -91,8 +96,7 @@ int check_eps(float eps) {
 
 size_t bf16_ws(int64_t T, int64_t K, int64_t N, int w_dtype) {
   if (w_dtype == RNL_FP32) return rnl::skinny_workspace_bytes(T, K, N);
-  if (use_decode(T)) return 0;
-  return align256((size_t)T * (size_t)K * 2);
+  return align256((size_t)T * (size_t)K * 2);  // the normed bf16 activations
 }
 
 }  // namespace
@@ -151,14 +155,10 @@ int rmsnorm_linear_bf16(const void* x, const void* gamma, float eps, const void*
                       "skinny split-K launch");
   }
   const uint16_t* wb = static_cast<const uint16_t*>(W);
-  if (use_decode(T)) {
-    return hip_status(rnl::launch_decode_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, K, N, s),
-                      "decode launch");
-  }
   uint16_t* a = static_cast<uint16_t*>(workspace);
   hipError_t e = rnl::launch_norm_rows_bf16(xb, gb, eps, T, K, a, rstd_out, s);
   if (e != hipSuccess) return hip_status(e, "norm pre-pass launch");
-  return hip_status(rnl::launch_gemm_bf16(a, wb, y, ok_kind, T, N, K, s), "bf16 GEMM launch");
+  return hip_status(project_bf16(a, wb, y, ok_kind, T, N, K, s), "bf16 projection launch");
 }
 
 size_t rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype) {
@@ -209,7 +209,7 @@ int rmsnorm_linear_int8(const void* x, const void* gamma, float eps, const int8_
 size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N) {
   (void)N;
   if (T <= 0 || R <= 0 || K <= 0) return 0;
-  const int ks = rnl::gemm_split_plan(T, R, K, 2, nullptr);
+  const int ks = chain_splits(T, R, K);
   if (ks > 1) return align256((size_t)ks * (size_t)T * (size_t)R * 4);  // fp32 split-K partials of q_a
   return align256((size_t)T * (size_t)R * 2);                           // bf16 q_a
 }
@@ -239,7 +239,7 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
   const uint16_t* wa = static_cast<const uint16_t*>(W_a);
   const uint16_t* gb = static_cast<const uint16_t*>(gamma);
   uint16_t* qr = static_cast<uint16_t*>(qr_out);
-  const int ks = rnl::gemm_split_plan(T, R, K, 2, nullptr);
+  const int ks = chain_splits(T, R, K);
   hipError_t e;
   if (ks > 1) {
     // q_a is too small to fill the chip: split its K, then add the partials in split
@@ -251,14 +251,14 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
     if (e != hipSuccess) return hip_status(e, "chain reduce+norm launch");
   } else {
     uint16_t* qa = static_cast<uint16_t*>(workspace);
-    e = rnl::launch_gemm_bf16(xb, wa, qa, rnl::OUT_BF16, T, R, K, s);
-    if (e != hipSuccess) return hip_status(e, "chain stage-1 GEMM launch");
+    e = project_bf16(xb, wa, qa, rnl::OUT_BF16, T, R, K, s);
+    if (e != hipSuccess) return hip_status(e, "chain stage-1 projection launch");
     e = rnl::launch_norm_rows_bf16(qa, gb, eps, T, R, qr, rstd_out, s);
     if (e != hipSuccess) return hip_status(e, "chain norm launch");
   }
-  return hip_status(rnl::launch_gemm_bf16(static_cast<const uint16_t*>(qr_out), static_cast<const uint16_t*>(W_b),
-                                          y, rnl::OUT_BF16, T, N, R, s),
-                    "chain stage-2 GEMM launch");
+  return hip_status(project_bf16(static_cast<const uint16_t*>(qr_out), static_cast<const uint16_t*>(W_b), y,
+                                 rnl::OUT_BF16, T, N, R, s),
+                    "chain stage-2 projection launch");
 }
 
 int rms_norm_bf16(const void* x, const void* gamma, float eps, void* y, float* rstd_out, int64_t T,
@@ -301,10 +301,10 @@ int linear_bf16(const void* a, const void* W, void* y, int out_dtype, int64_t M,
   RNL_ALIGN(a, 16, "a");
   RNL_ALIGN(W, 16, "W");
   RNL_ALIGN(y, 16, "y");
-  return hip_status(rnl::launch_gemm_bf16(static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(W), y,
-                                          out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32, M, N, K,
-                                          static_cast<hipStream_t>(stream)),
-                    "bf16 GEMM launch");
+  return hip_status(project_bf16(static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(W), y,
+                                 out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32, M, N, K,
+                                 static_cast<hipStream_t>(stream)),
+                    "bf16 projection launch");
 }
 
 int linear_int8(const int8_t* xq, const float* x_scale, const int8_t* Wq, const float* w_scale, void* y,

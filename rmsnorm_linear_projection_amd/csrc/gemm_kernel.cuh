@@ -1,7 +1,7 @@
 // Tiled MFMA GEMM for the projection step: C[M,N] = A[M,K] . B[N,K]^T (b_trans).
 //
 // A is the normed activation (bf16, or per-token int8), B the weight stored
-// [N, K] (AT-10 page section 2: the weight enters with b_trans=True).  Both
+// [N, K] (AT-10 page section 2: the weight enters transposed).  Both
 // operands are K-contiguous and staged through LDS identically: a k-step is 128
 // bytes of every tile row (64 bf16 or 128 int8), cut into 16-byte chunks, and
 // one chunk is exactly one lane's MFMA operand:

@@ -42,10 +42,12 @@ hipError_t launch_gemm_int8(const int8_t* A, const int8_t* B, void* C, int out_k
                             const float* xs, const float* ws, int64_t M, int64_t N, int64_t K,
                             hipStream_t s);
 
-// Fused RMSNorm + projection for T <= 16 tokens (weight streaming).
-hipError_t launch_decode_bf16(const uint16_t* x, const uint16_t* gamma, float eps,
-                              const uint16_t* W, void* y, int out_kind, float* rstd_out, int64_t T,
-                              int64_t K, int64_t N, hipStream_t s);
+// C[M,N] = A[M,K] . W[N,K]^T for M <= 16 (weight streaming), bf16 or fp32 out.
+// R = weight rows per workgroup (a multiple of 4, at most 32), or 0 to let
+// small_m_rows(N) spread the rows evenly over the compute units.
+int small_m_rows(int64_t N);
+hipError_t launch_small_m_bf16(const uint16_t* A, const uint16_t* W, void* C, int out_kind, int64_t M,
+                               int64_t N, int64_t K, int R, hipStream_t s);
 
 // fp32-weight projection of the fp32 normed rows, split over K.
 size_t skinny_workspace_bytes(int64_t T, int64_t K, int64_t N);

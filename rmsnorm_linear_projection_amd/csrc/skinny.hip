@@ -1,6 +1,6 @@
 // fp32-weight projection of the fp32 normed rows, split over K: the SK-03
-// page's mhc_pre variant ("large reduction x tiny output width", FP32 compute,
-// e.g. [B, 28672] x [28672, 24]).
+// page's mhc_pre variant (a very long reduction into a few output columns,
+// computed in fp32, e.g. [B, 28672] x [28672, 24]).
 //
 // The output is tiny, so the only parallelism is along K: the reduction is
 // split into S contiguous ranges of 512 k, each workgroup producing fp32 partial

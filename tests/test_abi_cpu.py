@@ -92,8 +92,8 @@ def test_bf16_validation(lib, kw, code):
 
 
 def test_workspace_queries(lib):
-    # decode (T <= 16) needs none; the GEMM path needs the normed activations
-    assert lib.rmsnorm_linear_bf16_workspace_bytes(16, 4096, 6144, 1, 1) == 0
+    # the bf16 path keeps the normed activations in the workspace
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(16, 4096, 6144, 1, 1) >= 16 * 4096 * 2
     assert lib.rmsnorm_linear_bf16_workspace_bytes(4096, 4096, 6144, 1, 1) >= 4096 * 4096 * 2
     assert lib.rmsnorm_linear_bf16_workspace_bytes(512, 28672, 24, 2, 2) > 512 * 24 * 4
     assert lib.rmsnorm_linear_int8_workspace_bytes(2048, 4096, 4096, 1) >= 2048 * 4096 + 2048 * 4
@@ -102,10 +102,11 @@ def test_workspace_queries(lib):
 
 
 def test_forced_variant_changes_workspace(lib, monkeypatch):
+    # few tokens: the chain's first projection is not split; the tiled GEMM splits its K
+    small = lib.norm_proj_chain_workspace_bytes(4, 7168, 1536, 24576)
+    assert small == 4 * 1536 * 2 + (-(4 * 1536 * 2) % 256)
     monkeypatch.setenv("RNL_VARIANT", "gemm")
-    assert lib.rmsnorm_linear_bf16_workspace_bytes(8, 256, 128, 1, 1) == 8 * 256 * 2
-    monkeypatch.setenv("RNL_VARIANT", "decode")
-    assert lib.rmsnorm_linear_bf16_workspace_bytes(8, 256, 128, 1, 1) == 0
+    assert lib.norm_proj_chain_workspace_bytes(4, 7168, 1536, 24576) > small
 
 
 def int8_call(lib, x=FAKE, g=NULL, eps=1e-6, Wq=FAKE, ws=FAKE, y=FAKE, od=1, xq=NULL, xs=NULL, rstd=NULL,

@@ -79,7 +79,8 @@ def assert_rstd(rstd_gpu, rstd_ref, what, ulps=8):
 
 
 # ---------------------------------------------------------------------------
-# bf16 path (decode kernel for T <= 16, norm pre-pass + tiled GEMM otherwise)
+# bf16 path (norm pre-pass, then the weight-streaming kernel for T <= 16 or the
+# tiled GEMM)
 # ---------------------------------------------------------------------------
 def run_bf16(case, out_dtype=torch.bfloat16):
     x, g, W = dev(case["x"]), dev(case["gamma"]), dev(case["W"])
@@ -320,6 +321,8 @@ def check_chain_case(case, rows=None):
     (300, 520, 136, 260, True),
     (64, 4096, 128, 64, True),  # stage 1 split over K (8 slices)
     (50, 2056, 72, 33, False),  # split over K with a K tail
+    (4, 7168, 1536, 520, True),  # few tokens: both stages stream their weights
+    (16, 1032, 264, 6143, False),
 ])
 def test_chain_small(T, K, R, N, gamma):
     check_chain_case(synthetic.chain_case(T, K, R, N, seed=T + R, gamma=gamma))
@@ -370,6 +373,27 @@ def test_atom_linear_bf16(M, K, N):
     rows = sample_rows(M)
     ref = O.project_bf16(O.bf16_bits_to_f32(bits(a)[rows]), bits(W))
     assert_bf16_close(f32(y)[rows], ref, "linear_bf16")
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 4096, 6144),  # 24 weight rows per workgroup (two MFMA row blocks)
+    (16, 4104, 6143),  # K tail of a 32-wide step, ragged N
+    (5, 264, 100),
+    (16, 1032, 1536),
+    (2, 64, 24576),
+    (7, 8, 3),
+])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_atom_linear_bf16_few_rows(M, K, N, out_dtype):
+    a = synthetic.normal((M, K), 1.0, 5, 11)
+    W = synthetic.normal((N, K), 1.0 / np.sqrt(K), 5, 12)
+    y = rnl.linear_bf16(dev(a), dev(W), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = O.project_bf16(O.bf16_bits_to_f32(bits(a)), bits(W))
+    assert_bf16_close(f32(y), ref, "linear_bf16 few rows")
+    y2 = rnl.linear_bf16(dev(a), dev(W), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "not deterministic"
 
 
 @pytest.mark.parametrize("M,K,N", [(33, 64, 17), (257, 4112, 130)])
