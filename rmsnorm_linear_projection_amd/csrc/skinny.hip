@@ -3,10 +3,10 @@
 // computed in fp32, e.g. [B, 28672] x [28672, 24]).
 //
 // The output is tiny, so the only parallelism is along K: the reduction is
-// split into S contiguous ranges of 512 k, each workgroup producing fp32 partial
-// dot products and partial sums of squares for 64 tokens x 32 output columns;
-// a second kernel adds the S partials in a fixed order (bit-reproducible) and
-// applies rstd.
+// split into S contiguous ranges (S chosen so that there is about one
+// workgroup per CU), each workgroup producing fp32 partial dot products and
+// partial sums of squares for 64 tokens x 32 output columns; a second kernel
+// adds the S partials in a fixed order (bit-reproducible) and applies rstd.
 //
 // x is read exactly once.  Without a gamma, n = x * rstd, so
 // sum_k n[k] W[j,k] = rstd * sum_k x[k] W[j,k] in exact arithmetic: the
@@ -20,6 +20,8 @@
 // (v_mfma_f32_16x16x32_bf16, exact products, fp32 accumulation) at three
 // MFMAs per block instead of the much slower fp32 MFMA.  The weight
 // ([N, K] fp32, a few MB) is re-read by every token group and stays in L2.
+#include <algorithm>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -28,17 +30,8 @@ namespace {
 
 constexpr int kTG = 64;  // tokens per workgroup (4 MFMA column blocks)
 constexpr int kNC = 32;  // output columns per workgroup (2 MFMA row blocks)
-
-__device__ __forceinline__ float sumsq8(u32x4 w) {
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float a = bf16lo(w[j]), b = bf16hi(w[j]);
-    s += a * a;
-    s += b * b;
-  }
-  return s;
-}
+constexpr int kKU = 1;   // k-steps per load batch
+constexpr int kNW = 4;   // wavefronts per workgroup of the partial kernel
 
 // high 16 bits of two fp32 words -> one packed bf16 pair (lo word first)
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
@@ -72,104 +65,127 @@ __device__ __forceinline__ f32x4 mma(u32x4 p, u32x4 q, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
 }
 
-// One workgroup: 64 tokens x 32 output columns x one K range of 4 * kSPW k-steps
-// (32 k each); wavefront w takes kSPW consecutive k-steps.  Each wavefront
-// issues all of its loads (x, weight, gamma) before the first MFMA, so the whole
-// grid's data is requested in one round trip.
-constexpr int kSPW = 4;
-
-template <bool GAMMA>
-__global__ __launch_bounds__(256) void skinny_partial_kernel(
+// One workgroup: 64 tokens x 32 output columns x one contiguous range of k-steps
+// (32 k each), split evenly over its NW wavefronts.  The grid holds about one
+// workgroup per CU; each wavefront streams its range with the loads of the next
+// KU k-steps in flight (two alternating register batches) while it splits and
+// multiplies the current ones, and two wavefronts per SIMD hide each other's
+// load latency.  The sum of squares of each token also runs
+// on the MFMA: with the token fragment as both operands, the diagonal of the
+// 16 x 16 product is sum_k x^2 for the 16 tokens (exact bf16 products, fp32
+// accumulation), which spares the vector ALU a squaring pass.
+template <int KU, int NW, bool GAMMA>
+__global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, const float* __restrict__ W,
-    float* __restrict__ part, float* __restrict__ ss_part, int T, int K, int N, int Npad) {
-  __shared__ f32x4 red[3][8][64];
-  __shared__ float red_ss[4][kTG];
+    float* __restrict__ part, float* __restrict__ ss_part, int T, int K, int N, int Npad,
+    int steps_per_wg) {
+  __shared__ f32x4 red[NW - 1][8][64];
+  __shared__ float red_ss[NW][kTG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kTG, z = blockIdx.y, nc0 = blockIdx.z * kNC;
-  const bool do_ss = blockIdx.z == 0;
-  const int s_beg = (z * 4 + wave) * kSPW;  // first k-step of this wavefront
+  const bool do_ss = blockIdx.z == 0;  // uniform: one column block derives the sums of squares
+
+  const int nsteps = (K + 31) / 32;
+  const int wg_beg = min(nsteps, z * steps_per_wg), wg_end = min(nsteps, wg_beg + steps_per_wg);
+  const int per = (wg_end - wg_beg + NW - 1) / NW;
+  const int s_beg = min(wg_end, wg_beg + wave * per), s_end = min(wg_end, s_beg + per);
 
   const uint32_t kbytes = (uint32_t)K * 2u, wbytes = (uint32_t)K * 4u;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t0 * K, (uint32_t)min(kTG, T - t0) * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)nc0 * K, (uint32_t)min(kNC, N - nc0) * wbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, GAMMA ? kbytes : 0u);
 
-  u32x4 xv[kSPW][4], w0[kSPW][2], w1[kSPW][2], gv[kSPW];
+  struct Batch {
+    u32x4 xv[KU][4], w0[KU][2], w1[KU][2], gv[KU];
+  };
+  auto issue = [&](Batch& b, int s0) {
 #pragma unroll
-  for (int u = 0; u < kSPW; ++u) {
-    const int k = (s_beg + u) * 32 + g * 8;
-    const bool in_k = k < K;
+    for (int u = 0; u < KU; ++u) {
+      const int k = (s0 + u) * 32 + g * 8;
+      const bool in_k = (s0 + u) < s_end && k < K;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      xv[u][tb] = buf_load16(rx, in_k ? (uint32_t)(tb * 16 + r16) * kbytes + (uint32_t)k * 2u : kOOB);
+      for (int tb = 0; tb < 4; ++tb)
+        b.xv[u][tb] = buf_load16(rx, in_k ? (uint32_t)(tb * 16 + r16) * kbytes + (uint32_t)k * 2u : kOOB);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint32_t base = (uint32_t)(nb * 16 + r16) * wbytes + (uint32_t)k * 4u;
-      w0[u][nb] = buf_load16(rw, in_k ? base : kOOB);
-      w1[u][nb] = buf_load16(rw, in_k ? base + 16u : kOOB);
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t base = (uint32_t)(nb * 16 + r16) * wbytes + (uint32_t)k * 4u;
+        b.w0[u][nb] = buf_load16(rw, in_k ? base : kOOB);
+        b.w1[u][nb] = buf_load16(rw, in_k ? base + 16u : kOOB);
+      }
+      if constexpr (GAMMA) b.gv[u] = buf_load16(rg, in_k ? (uint32_t)k * 2u : kOOB);
+      else b.gv[u] = u32x4{0u, 0u, 0u, 0u};
     }
-    if constexpr (GAMMA) gv[u] = buf_load16(rg, in_k ? (uint32_t)k * 2u : kOOB);
-    else gv[u] = u32x4{0u, 0u, 0u, 0u};
-  }
+  };
 
-  f32x4 acc[4][2];
+  f32x4 acc[4][2], sq[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 4; ++a) {
+    sq[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int u = 0; u < kSPW; ++u) {
-    float wv[2][8];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wv[nb][j] = __uint_as_float(w0[u][nb][j]);
-        wv[nb][4 + j] = __uint_as_float(w1[u][nb][j]);
-      }
-    if constexpr (GAMMA) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wv[nb][2 * j] = __fmul_rn(wv[nb][2 * j], bf16lo(gv[u][j]));
-          wv[nb][2 * j + 1] = __fmul_rn(wv[nb][2 * j + 1], bf16hi(gv[u][j]));
-        }
-    }
-    if (do_ss) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) ss[tb] += sumsq8(xv[u][tb]);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const Split3 p = split_w(wv[nb]);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        acc[tb][nb] = mma(p.hi, xv[u][tb], acc[tb][nb]);
-        acc[tb][nb] = mma(p.mid, xv[u][tb], acc[tb][nb]);
-        acc[tb][nb] = mma(p.lo, xv[u][tb], acc[tb][nb]);
-      }
-    }
   }
 
-  // combine the four wavefronts in a fixed order
+  auto consume = [&](const Batch& bt) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      if (do_ss) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) sq[tb] = mma(bt.xv[u][tb], bt.xv[u][tb], sq[tb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float wv[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wv[j] = __uint_as_float(bt.w0[u][nb][j]);
+          wv[4 + j] = __uint_as_float(bt.w1[u][nb][j]);
+        }
+        if constexpr (GAMMA) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            wv[2 * j] = __fmul_rn(wv[2 * j], bf16lo(bt.gv[u][j]));
+            wv[2 * j + 1] = __fmul_rn(wv[2 * j + 1], bf16hi(bt.gv[u][j]));
+          }
+        }
+        const Split3 p = split_w(wv);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          acc[tb][nb] = mma(p.hi, bt.xv[u][tb], acc[tb][nb]);
+          acc[tb][nb] = mma(p.mid, bt.xv[u][tb], acc[tb][nb]);
+          acc[tb][nb] = mma(p.lo, bt.xv[u][tb], acc[tb][nb]);
+        }
+      }
+    }
+  };
+
+  Batch b0, b1;
+  issue(b0, s_beg);
+  int s0 = s_beg;
+  for (; s0 + KU < s_end; s0 += 2 * KU) {
+    issue(b1, s0 + KU);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(b0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b0, s0 + 2 * KU);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (s0 < s_end) consume(b0);
+
+  // combine the wavefronts in a fixed order
   if (wave > 0) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) red[wave - 1][tb * 2 + nb][lane] = acc[tb][nb];
   }
-  if (do_ss) {
+  if (do_ss && (r16 >> 2) == g) {
+    // diagonal of the token x token product: lane (r16, g) with r16 / 4 == g holds
+    // token r16's sum of squares in element r16 & 3
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      float v = ss[tb];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (g == 0) red_ss[wave][tb * 16 + r16] = v;
-    }
+    for (int tb = 0; tb < 4; ++tb) red_ss[wave][tb * 16 + r16] = sq[tb][r16 & 3];
   }
   __syncthreads();
   if (wave == 0) {
@@ -179,9 +195,8 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         f32x4 v = acc[tb][nb];
-        v += red[0][tb * 2 + nb][lane];
-        v += red[1][tb * 2 + nb][lane];
-        v += red[2][tb * 2 + nb][lane];
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) v += red[w][tb * 2 + nb][lane];
         if (t < T) {
           const int n = nc0 + nb * 16 + 4 * g;  // < Npad always
           *reinterpret_cast<f32x4*>(part + ((size_t)z * T + t) * Npad + n) = v;
@@ -190,7 +205,10 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(
     }
   }
   if (do_ss && tid < kTG && t0 + tid < T) {
-    ss_part[(size_t)z * T + t0 + tid] = red_ss[0][tid] + red_ss[1][tid] + red_ss[2][tid] + red_ss[3][tid];
+    float v = red_ss[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red_ss[w][tid];
+    ss_part[(size_t)z * T + t0 + tid] = v;
   }
 }
 
@@ -243,17 +261,24 @@ __global__ __launch_bounds__(256) void skinny_finalize_kernel(
 }
 
 struct Plan {
-  int tg, nc, nsteps, S, sps, Npad;
+  int tg, nc, nsteps, S, spw, Npad;
 };
 
+// About one workgroup per CU: the K range is split into S pieces of spw k-steps,
+// spw a power of two (>= 8) so that each piece of a token row starts and ends on
+// a 2^n-byte boundary (unaligned pieces stream measurably slower from HBM), the
+// smallest such that tg * nc * S does not exceed 256.
 Plan plan_of(int64_t T, int64_t K, int64_t N) {
   Plan p;
   p.tg = (int)((T + kTG - 1) / kTG);
   p.nc = (int)((N + kNC - 1) / kNC);
   p.Npad = p.nc * kNC;
   p.nsteps = (int)((K + 31) / 32);
-  p.sps = 4 * kSPW;
-  p.S = (p.nsteps + p.sps - 1) / p.sps;
+  const int64_t tiles = (int64_t)p.tg * p.nc;
+  int64_t spw = 8;
+  while (spw < 4096 && tiles * ((p.nsteps + spw - 1) / spw) > 256) spw *= 2;
+  p.spw = (int)spw;
+  p.S = (int)((p.nsteps + spw - 1) / spw);
   return p;
 }
 
@@ -275,11 +300,11 @@ hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float e
                                             align256((size_t)p.S * (size_t)T * (size_t)p.Npad * 4));
   dim3 grid((unsigned)p.tg, (unsigned)p.S, (unsigned)p.nc), block(256);
   if (gamma != nullptr)
-    hipLaunchKernelGGL((skinny_partial_kernel<true>), grid, block, 0, s, x, gamma, W, part, ss_part,
-                       (int)T, (int)K, (int)N, p.Npad);
+    hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, true>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
+                       (int)T, (int)K, (int)N, p.Npad, p.spw);
   else
-    hipLaunchKernelGGL((skinny_partial_kernel<false>), grid, block, 0, s, x, gamma, W, part, ss_part,
-                       (int)T, (int)K, (int)N, p.Npad);
+    hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, false>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
+                       (int)T, (int)K, (int)N, p.Npad, p.spw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float inv_k = 1.0f / (float)K;
