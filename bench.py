@@ -183,17 +183,22 @@ class Setup:
 
 
 def time_loop(fn, steps, warmup, graph=True):
-    """Average ms per call of fn(i) over `steps` calls after `warmup` calls.
+    """(ms per call, untimed calls made) for fn(i) over `steps` timed calls
+    after about `warmup` untimed ones.
 
-    With graph=True the `steps` calls are captured once into a HIP graph and the
-    timed region is one replay, so host-side launch overhead (Python, ctypes)
-    does not leak into the device time; the captured work is exactly the
-    eager calls' kernels on the same stream.  Events bracket the region on
-    the stream the kernels run on, after a device synchronisation.
+    With graph=True the `steps` calls are captured once into a HIP graph; a few
+    eager calls run before the capture, and the rest of the warm-up is made of
+    untimed replays of the same graph, which keep the GPU busy the way the
+    timed region does (the clocks settle under sustained load).  The timed
+    region is one replay, so host-side launch overhead (Python, ctypes) does
+    not leak into the device time; the captured work is exactly the eager
+    calls' kernels.  Events bracket the region on the stream the kernels run
+    on, after a device synchronisation.
     """
     import torch
 
-    for i in range(warmup):
+    eager = min(warmup, 3) if graph else warmup
+    for i in range(eager):
         fn(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -204,22 +209,26 @@ def time_loop(fn, steps, warmup, graph=True):
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
                 for i in range(steps):
-                    fn(warmup + i)
+                    fn(eager + i)
         torch.cuda.current_stream().wait_stream(s)
-        g.replay()  # untimed replay: first-touch of the graph's resources
+        replays = max(1, -(-(warmup - eager) // steps))
+        for _ in range(replays):
+            g.replay()
         torch.cuda.synchronize()
         start.record()
         g.replay()
         end.record()
         torch.cuda.synchronize()
         del g
+        done = eager + replays * steps
     else:
         start.record()
         for i in range(steps):
-            fn(warmup + i)
+            fn(eager + i)
         end.record()
         torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms
+        done = eager
+    return start.elapsed_time(end) / steps, done  # ms
 
 
 def cpu_baseline(setup, target_s=8.0):
@@ -286,8 +295,8 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
 
     w = WORKLOADS[name]
     s = Setup(name, w)
-    ms = time_loop(s.step, steps, warmup, graph)
-    kms = time_loop(s.kern, steps, warmup, graph) if s.kern is not s.step else ms
+    ms, warm_done = time_loop(s.step, steps, warmup, graph)
+    kms = time_loop(s.kern, steps, warmup, graph)[0] if s.kern is not s.step else ms
     if w["bound"] == "hbm":
         value, unit = bytes_of(w) / (ms * 1e-3) / 1e9, "GB/s"
     else:
@@ -305,7 +314,7 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
         "unit": unit,
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warmup,
+        "warmup": warm_done,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -395,7 +404,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps before the timed ones (graph replays after 3 eager calls)")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")

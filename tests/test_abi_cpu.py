@@ -94,6 +94,7 @@ def test_bf16_validation(lib, kw, code):
 def test_workspace_queries(lib):
     # the bf16 path keeps the normed activations in the workspace
     assert lib.rmsnorm_linear_bf16_workspace_bytes(16, 4096, 6144, 1, 1) >= 16 * 4096 * 2
+    assert lib.rmsnorm_linear_bf16_workspace_bytes(17, 4096, 6144, 1, 1) >= 17 * 4096 * 2
     assert lib.rmsnorm_linear_bf16_workspace_bytes(4096, 4096, 6144, 1, 1) >= 4096 * 4096 * 2
     assert lib.rmsnorm_linear_bf16_workspace_bytes(512, 28672, 24, 2, 2) > 512 * 24 * 4
     assert lib.rmsnorm_linear_int8_workspace_bytes(2048, 4096, 4096, 1) >= 2048 * 4096 + 2048 * 4

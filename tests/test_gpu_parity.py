@@ -115,6 +115,10 @@ BF16_SMALL = [
     (17, 256, 130),
     (300, 1032, 200),  # K tail of a 64-wide k-step
     (129, 64, 33),
+    (16, 8200, 40),  # weight streaming with long rows, K tail
+    (9, 20480, 24),
+    (16, 4096, 24576),  # 32 weight rows per workgroup, three workgroups per CU
+    (2, 2048, 200),
 ]
 
 
