@@ -1,10 +1,11 @@
 // Row-wise RMSNorm pre-pass for the large-T GEMM paths (gfx950).
 //
-// One 256-thread workgroup per token row.  The row is read once with 16-byte
-// coalesced loads (kept in registers when K <= 16384), the fp32 sum of squares
-// is reduced across the wavefront and the workgroup, and the normed row is
-// written either as bf16 (the A operand of the bf16 GEMM) or as per-token
-// symmetric int8 plus its dequant scale (the A operand of the int8 GEMM).
+// Rows of up to 8192 values: one wavefront per row (shuffle reductions only).
+// Longer rows: one 256-thread workgroup per row, the row read once with 16-byte
+// coalesced loads (kept in registers when K <= 16384) and the fp32 sum of
+// squares reduced across the wavefronts.  The normed row is written either as
+// bf16 (the A operand of the bf16 GEMM) or as per-token symmetric int8 plus
+// its dequant scale (the A operand of the int8 GEMM).
 //
 // Arithmetic (AT-10 page, section 3, variant B; AT-10 page section 4, AT-05):
 //   S = sum_k xf^2 (fp32, any order), rstd = 1/sqrt(fl(fl(S*fl(1/K)) + eps)),
@@ -191,6 +192,92 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
   }
 }
 
+// Short rows (K <= 8192): one wavefront per row, four rows per workgroup.  Each
+// lane loads its CPL chunks of x and of gamma in one round trip, the sum of
+// squares and amax are reduced with wavefront shuffles (no barriers), and the
+// normed values stay in registers between the amax and the quantisation.
+template <int CPL, bool INT8>
+__global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps, float inv_k,
+    int64_t T, int64_t K, void* __restrict__ out, float* __restrict__ x_scale_out,
+    float* __restrict__ rstd_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wavefront: no barrier follows
+  const int nch = (int)(K >> 3);
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * K);
+  const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
+  u32x4 v[CPL], gv[CPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int idx = lane + 64 * c;
+    v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+    gv[c] = (gr != nullptr && idx < nch) ? gr[idx] : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) ss += sumsq8(v[c]);
+  const float rstd = rstd_from_sumsq(wave_sum(ss), inv_k, eps);
+  if (lane == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
+
+  float n[CPL][8];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      n[c][2 * j] = __fmul_rn(bf16lo(v[c][j]), rstd);
+      n[c][2 * j + 1] = __fmul_rn(bf16hi(v[c][j]), rstd);
+      if (gr != nullptr) {
+        n[c][2 * j] = __fmul_rn(n[c][2 * j], bf16lo(gv[c][j]));
+        n[c][2 * j + 1] = __fmul_rn(n[c][2 * j + 1], bf16hi(gv[c][j]));
+      }
+    }
+  }
+  if constexpr (!INT8) {
+    u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + t * K);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + 64 * c;
+      if (idx < nch)
+        orow[idx] = u32x4{pack_bf16x2(n[c][0], n[c][1]), pack_bf16x2(n[c][2], n[c][3]),
+                          pack_bf16x2(n[c][4], n[c][5]), pack_bf16x2(n[c][6], n[c][7])};
+    }
+  } else {
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(n[c][j]));  // chunks past K are 0
+    amax = wave_max(amax);
+    const float s = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
+    if (lane == 0 && x_scale_out != nullptr) x_scale_out[t] = __fdiv_rn(amax, 127.0f);
+    u32x2* orow = reinterpret_cast<u32x2*>(static_cast<int8_t*>(out) + t * K);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + 64 * c;
+      if (idx < nch) orow[idx] = u32x2{q4(n[c], 0, s), q4(n[c], 4, s)};
+    }
+  }
+}
+
+template <bool INT8>
+hipError_t launch_norm_wave(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T, int64_t K,
+                            void* out, float* x_scale_out, float* rstd_out, hipStream_t s) {
+  const float inv_k = 1.0f / (float)K;
+  const int64_t per = (K / 8 + 63) / 64;
+  dim3 grid((unsigned)((T + 3) / 4)), block(kThreads);
+#define RNL_NORM_WAVE(C)                                                                                hipLaunchKernelGGL((norm_rows_wave_kernel<C, INT8>), grid, block, 0, s, x, gamma, eps, inv_k, T, K,                      out, x_scale_out, rstd_out)
+  if (per <= 1) RNL_NORM_WAVE(1);
+  else if (per <= 2) RNL_NORM_WAVE(2);
+  else if (per <= 4) RNL_NORM_WAVE(4);
+  else if (per <= 8) RNL_NORM_WAVE(8);
+  else RNL_NORM_WAVE(16);
+#undef RNL_NORM_WAVE
+  return hipGetLastError();
+}
+
+constexpr int64_t kWaveRowMaxK = 8192;
+
 template <bool INT8, class Row>
 hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int64_t K, void* out,
                        float* x_scale_out, float* rstd_out, hipStream_t s) {
@@ -214,12 +301,14 @@ hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int
 
 hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
+  if (K <= kWaveRowMaxK) return launch_norm_wave<false>(x, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
   return launch_norm<false>(RowBf16{x, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
 
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s) {
+  if (K <= kWaveRowMaxK) return launch_norm_wave<true>(x, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
   return launch_norm<true>(RowBf16{x, K}, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
 }
 

@@ -323,7 +323,7 @@ def check_chain_case(case, rows=None):
     (37, 256, 64, 80, True),
     (5, 128, 48, 30, False),
     (300, 520, 136, 260, True),
-    (64, 4096, 128, 64, True),  # stage 1 split over K (8 slices)
+    (64, 4096, 128, 64, True),  # stage 1 split over K (4 slices)
     (50, 2056, 72, 33, False),  # split over K with a K tail
     (4, 7168, 1536, 520, True),  # few tokens: both stages stream their weights
     (16, 1032, 264, 6143, False),
