@@ -74,16 +74,17 @@ __device__ __forceinline__ f32x4 mma(u32x4 p, u32x4 q, f32x4 c) {
 // on the MFMA: with the token fragment as both operands, the diagonal of the
 // 16 x 16 product is sum_k x^2 for the 16 tokens (exact bf16 products, fp32
 // accumulation), which spares the vector ALU a squaring pass.
-template <int KU, int NW, bool GAMMA>
+template <int KU, int NW, int TG, bool GAMMA>
 __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, const float* __restrict__ W,
     float* __restrict__ part, float* __restrict__ ss_part, int T, int K, int N, int Npad,
     int steps_per_wg) {
-  __shared__ f32x4 red[NW - 1][8][64];
-  __shared__ float red_ss[NW][kTG];
+  constexpr int TB = TG / 16;  // MFMA column blocks of tokens
+  __shared__ f32x4 red[NW - 1][2 * TB][64];
+  __shared__ float red_ss[NW][TG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kTG, z = blockIdx.y, nc0 = blockIdx.z * kNC;
+  const int t0 = blockIdx.x * TG, z = blockIdx.y, nc0 = blockIdx.z * kNC;
   const bool do_ss = blockIdx.z == 0;  // uniform: one column block derives the sums of squares
 
   const int nsteps = (K + 31) / 32;
@@ -92,12 +93,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
   const int s_beg = min(wg_end, wg_beg + wave * per), s_end = min(wg_end, s_beg + per);
 
   const uint32_t kbytes = (uint32_t)K * 2u, wbytes = (uint32_t)K * 4u;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t0 * K, (uint32_t)min(kTG, T - t0) * kbytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t0 * K, (uint32_t)min(TG, T - t0) * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)nc0 * K, (uint32_t)min(kNC, N - nc0) * wbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, GAMMA ? kbytes : 0u);
 
   struct Batch {
-    u32x4 xv[KU][4], w0[KU][2], w1[KU][2], gv[KU];
+    u32x4 xv[KU][TB], w0[KU][2], w1[KU][2], gv[KU];
   };
   auto issue = [&](Batch& b, int s0) {
 #pragma unroll
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
       const int k = (s0 + u) * 32 + g * 8;
       const bool in_k = (s0 + u) < s_end && k < K;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < TB; ++tb)
         b.xv[u][tb] = buf_load16(rx, in_k ? (uint32_t)(tb * 16 + r16) * kbytes + (uint32_t)k * 2u : kOOB);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -118,9 +119,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
     }
   };
 
-  f32x4 acc[4][2], sq[4];
+  f32x4 acc[TB][2], sq[TB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < TB; ++a) {
     sq[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
     for (int u = 0; u < KU; ++u) {
       if (do_ss) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) sq[tb] = mma(bt.xv[u][tb], bt.xv[u][tb], sq[tb]);
+        for (int tb = 0; tb < TB; ++tb) sq[tb] = mma(bt.xv[u][tb], bt.xv[u][tb], sq[tb]);
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
         }
         const Split3 p = split_w(wv);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
           acc[tb][nb] = mma(p.hi, bt.xv[u][tb], acc[tb][nb]);
           acc[tb][nb] = mma(p.mid, bt.xv[u][tb], acc[tb][nb]);
           acc[tb][nb] = mma(p.lo, bt.xv[u][tb], acc[tb][nb]);
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
   // combine the wavefronts in a fixed order
   if (wave > 0) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) red[wave - 1][tb * 2 + nb][lane] = acc[tb][nb];
   }
@@ -185,12 +186,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
     // diagonal of the token x token product: lane (r16, g) with r16 / 4 == g holds
     // token r16's sum of squares in element r16 & 3
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) red_ss[wave][tb * 16 + r16] = sq[tb][r16 & 3];
+    for (int tb = 0; tb < TB; ++tb) red_ss[wave][tb * 16 + r16] = sq[tb][r16 & 3];
   }
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < TB; ++tb) {
       const int t = t0 + tb * 16 + r16;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
       }
     }
   }
-  if (do_ss && tid < kTG && t0 + tid < T) {
+  if (do_ss && tid < TG && t0 + tid < T) {
     float v = red_ss[0][tid];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += red_ss[w][tid];
@@ -268,9 +269,9 @@ struct Plan {
 // spw a power of two (>= 8) so that each piece of a token row starts and ends on
 // a 2^n-byte boundary (unaligned pieces stream measurably slower from HBM), the
 // smallest such that tg * nc * S does not exceed 256.
-Plan plan_of(int64_t T, int64_t K, int64_t N) {
+Plan plan_of(int64_t T, int64_t K, int64_t N, int tg_rows = kTG) {
   Plan p;
-  p.tg = (int)((T + kTG - 1) / kTG);
+  p.tg = (int)((T + tg_rows - 1) / tg_rows);
   p.nc = (int)((N + kNC - 1) / kNC);
   p.Npad = p.nc * kNC;
   p.nsteps = (int)((K + 31) / 32);
@@ -300,10 +301,10 @@ hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float e
                                             align256((size_t)p.S * (size_t)T * (size_t)p.Npad * 4));
   dim3 grid((unsigned)p.tg, (unsigned)p.S, (unsigned)p.nc), block(256);
   if (gamma != nullptr)
-    hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, true>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
+    hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, kTG, true>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
                        (int)T, (int)K, (int)N, p.Npad, p.spw);
   else
-    hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, false>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
+    hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, kTG, false>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
                        (int)T, (int)K, (int)N, p.Npad, p.spw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -280,6 +280,18 @@ def test_fp32w_bf16_output():
                      out_dtype=torch.bfloat16)
 
 
+@pytest.mark.parametrize("T,K,N", [(3, 1 << 20, 24), (2, (1 << 20) - 8, 8)])
+def test_max_k(T, K, N):
+    """The largest K the bf16 entry point accepts, with bf16 and with fp32 weights."""
+    check_bf16_case(synthetic.norm_linear_case(T, K, N, seed=5))
+    check_fp32w_case(synthetic.norm_linear_case(T, K, N, seed=6, gamma=False, w_dtype="fp32"))
+
+
+def test_int8_max_k():
+    """The largest K for which an int32 accumulator cannot overflow (a multiple of 16)."""
+    check_int8_case(synthetic.int8_case(2, 133136, 16, seed=7))
+
+
 def test_skinny_fp32_full_size():
     """Large-reduction tiny-width norm + linear, T=512, K=28672, N=24, fp32 W."""
     case = synthetic.skinny_fp32()
