@@ -78,14 +78,31 @@ template <int KU, int NW, int TG, bool GAMMA>
 __global__ __launch_bounds__(NW * 64) void skinny_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, const float* __restrict__ W,
     float* __restrict__ part, float* __restrict__ ss_part, int T, int K, int N, int Npad,
-    int steps_per_wg) {
+    int steps_per_wg, int ntg, int nsplit) {
   constexpr int TB = TG / 16;  // MFMA column blocks of tokens
   __shared__ f32x4 red[NW - 1][2 * TB][64];
   __shared__ float red_ss[NW][TG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * TG, z = blockIdx.y, nc0 = blockIdx.z * kNC;
-  const bool do_ss = blockIdx.z == 0;  // uniform: one column block derives the sums of squares
+  // Work item (token group, K piece, column block).  With a flat grid, the
+  // workgroups that share a K piece (and so read the same weight slice) are
+  // placed on one XCD: dispatch deals workgroup ids round-robin over the 8
+  // XCDs, so id b is remapped to (b % 8) * (n / 8) + b / 8 and consecutive
+  // remapped ids, which differ only in the token group, stay on one L2.
+  int tgi, z, ncb;
+  if (ntg > 0) {
+    const int b = blockIdx.x, n = gridDim.x;
+    const int L = (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+    tgi = L % ntg;
+    z = (L / ntg) % nsplit;
+    ncb = L / ntg / nsplit;
+  } else {
+    tgi = blockIdx.x;
+    z = blockIdx.y;
+    ncb = blockIdx.z;
+  }
+  const int t0 = tgi * TG, nc0 = ncb * kNC;
+  const bool do_ss = ncb == 0;  // uniform: one column block derives the sums of squares
 
   const int nsteps = (K + 31) / 32;
   const int wg_beg = min(nsteps, z * steps_per_wg), wg_end = min(nsteps, wg_beg + steps_per_wg);
@@ -299,13 +316,18 @@ hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float e
   float* part = static_cast<float*>(workspace);
   float* ss_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                             align256((size_t)p.S * (size_t)T * (size_t)p.Npad * 4));
-  dim3 grid((unsigned)p.tg, (unsigned)p.S, (unsigned)p.nc), block(256);
+  // a flat grid (with the XCD placement) whenever the item count fits one axis
+  const int64_t items = (int64_t)p.tg * p.S * p.nc;
+  const bool flat = items <= 0x7fffffff;
+  dim3 grid = flat ? dim3((unsigned)items) : dim3((unsigned)p.tg, (unsigned)p.S, (unsigned)p.nc);
+  const int ntg = flat ? p.tg : 0;
+  dim3 block(256);
   if (gamma != nullptr)
     hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, kTG, true>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
-                       (int)T, (int)K, (int)N, p.Npad, p.spw);
+                       (int)T, (int)K, (int)N, p.Npad, p.spw, ntg, p.S);
   else
     hipLaunchKernelGGL((skinny_partial_kernel<kKU, kNW, kTG, false>), grid, dim3(kNW * 64), 0, s, x, gamma, W, part, ss_part,
-                       (int)T, (int)K, (int)N, p.Npad, p.spw);
+                       (int)T, (int)K, (int)N, p.Npad, p.spw, ntg, p.S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float inv_k = 1.0f / (float)K;
