@@ -24,4 +24,8 @@ from .rmsnorm_linear import (  # noqa: F401
     rmsnorm_linear_fp32w,
     rmsnorm_linear_int8,
     norm_proj_chain,
+    add_residual,
+    add_rmsnorm_linear_bf16,
+    add_rmsnorm_linear_fp32w,
+    add_rmsnorm_linear_int8,
 )

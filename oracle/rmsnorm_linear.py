@@ -111,10 +111,10 @@ def rstd_variant_a(ms: np.ndarray, eps: float) -> np.ndarray:
 def rms_norm_rows(x_bits, gamma_bits, eps: float, rstd=None, variant: str = "B"):
     """Per-row RMSNorm in fp32.  Returns (n [T,K] fp32, rstd [T] fp32).
 
-    AT-10 page section 3: xf = cast(x, FP32); ms = sum(xf^2)/D; var = ms+eps;
-    rstd = 1/sqrt(var); y = xf * rstd; optional y = y * cast(gamma, FP32)
-    (gamma applied after the rstd product, as the MLA caller does in
-    section 5).  If ``rstd`` is given (for instance the device's own), it is
+    AT-10 page section 3: xf = float(x); ms = (sum of xf^2) * (1/D);
+    var = ms + eps; rstd = 1/sqrt(var); n = xf * rstd, then n * float(gamma)
+    when gamma is given (gamma applied after the rstd product, as the MLA
+    caller does in section 5).  If ``rstd`` is given (for instance the device's own), it is
     used instead of recomputing it, so that the normed values can be compared
     bit for bit downstream.
     """
@@ -239,6 +239,25 @@ def dequant(acc: np.ndarray, x_scale: np.ndarray, w_scale: np.ndarray) -> np.nda
 
 
 # ----------------------------------------------------------------------------
+# Residual add before the norm (pre-attention input norm)
+# ----------------------------------------------------------------------------
+def add_residual(x_bits, r_bits) -> np.ndarray:
+    """x_add = x + residual, as bf16 bits [T, K].
+
+    AT-10 page section 6: in the pre-attention operator the input is usually
+    first added to the residual stream and the norm is applied to that sum;
+    the atom table of section 3 lists the in-place add-then-norm variant
+    among the ones that also output rstd.  READING: the two bf16 operands are
+    added in fp32 (one rounding) and the sum is rounded to bf16 (nearest
+    even), which is the bf16 tensor the norm then reads and the new residual
+    stream the caller keeps.
+    """
+    xf = bf16_bits_to_f32(x_bits)
+    rf = bf16_bits_to_f32(r_bits)
+    return f32_to_bf16_bits((xf + rf).astype(F32))
+
+
+# ----------------------------------------------------------------------------
 # Entry points (same names and argument meanings as the C-ABI library)
 # ----------------------------------------------------------------------------
 def rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd=None):
@@ -287,3 +306,27 @@ def norm_proj_chain(x_bits, Wa_bits, gamma_bits, eps, Wb_bits, rstd=None, qa_bit
     qr_bits = f32_to_bf16_bits(n)
     y32 = project_bf16(bf16_bits_to_f32(qr_bits), Wb_bits)
     return {"qa": qa_bits, "qr": qr_bits, "y32": y32, "y_bf16": f32_to_bf16_bits(y32), "rstd": rstd}
+
+
+def add_rmsnorm_linear_bf16(x_bits, r_bits, gamma_bits, eps, W_bits, rstd=None):
+    """Residual add, then AT-10 on the sum.  Returns (x_add bits, y32, y_bf16
+    bits, rstd)."""
+    xa = add_residual(x_bits, r_bits)
+    y32, ybf, rstd = rmsnorm_linear_bf16(xa, gamma_bits, eps, W_bits, rstd)
+    return xa, y32, ybf, rstd
+
+
+def add_rmsnorm_linear_fp32w(x_bits, r_bits, gamma_bits, eps, W, rstd=None):
+    """Residual add, then the fp32-weight variant.  Returns (x_add bits, y32, rstd)."""
+    xa = add_residual(x_bits, r_bits)
+    y32, rstd = rmsnorm_linear_fp32w(xa, gamma_bits, eps, W, rstd)
+    return xa, y32, rstd
+
+
+def add_rmsnorm_linear_int8(x_bits, r_bits, gamma_bits, eps, Wq, w_scale, rstd=None):
+    """Residual add, then AT-11 on the sum.  Returns the dict of
+    rmsnorm_linear_int8 with the x_add bits under "x_add"."""
+    xa = add_residual(x_bits, r_bits)
+    out = rmsnorm_linear_int8(xa, gamma_bits, eps, Wq, w_scale, rstd)
+    out["x_add"] = xa
+    return out

@@ -412,3 +412,74 @@ def test_chain_stage_one_exact():
     assert np.array_equal(r["qa"], O.f32_to_bf16_bits(qa32))
     y = _exact_proj(O.bf16_bits_to_f32(r["qr"]), O.bf16_bits_to_f32(Wb))
     assert np.array_equal(r["y32"], y)
+
+
+# ---------------------------------------------------------------------------
+# residual add before the norm
+# ---------------------------------------------------------------------------
+def _fraction_to_bf16_bits(fr: Fraction) -> int:
+    """Nearest-even bf16 (8 significant bits) of an exact rational, from the
+    definition of the format (normal range only), as a bit pattern."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    m = a / Fraction(2) ** (e - 7)  # in [2^7, 2^8)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    if fl == 256:  # rounded up to the next binade
+        fl, e = 128, e + 1
+    return sign | ((e + 127) << 7) | (fl - 128)
+
+
+def test_add_residual_is_correctly_rounded_sum():
+    """Two bf16 values whose exponents differ by at most 15 add exactly in fp32, so
+    x_add must be the nearest-even bf16 of the exact sum."""
+    x = _rand_bf16_rows(6, 64, seed=21)
+    r = _rand_bf16_rows(6, 64, seed=22, std=0.3)
+    got = O.add_residual(x, r)
+    xf, rf = O.bf16_bits_to_f32(x), O.bf16_bits_to_f32(r)
+    checked = 0
+    for a, b, g in zip(xf.ravel(), rf.ravel(), got.ravel()):
+        if a == 0 or b == 0 or abs(np.frexp(a)[1] - np.frexp(b)[1]) > 15:
+            continue
+        s = Fraction(float(a)) + Fraction(float(b))
+        assert int(g) == _fraction_to_bf16_bits(s), (a, b)
+        checked += 1
+    assert checked > 300
+
+
+def test_add_residual_ties_round_to_even():
+    """1 + 2^-8 and 1 + 3 * 2^-8 are halfway between bf16 neighbours: the first rounds
+    down to 1 (even), the second up to 1 + 2^-6."""
+    one, half_ulp, three_half = (int(O.f32_to_bf16_bits(np.float32(v))[0]) for v in (1.0, 2.0 ** -8, 3 * 2.0 ** -8))
+    got = O.add_residual(np.array([[one, one]], dtype=np.uint16), np.array([[half_ulp, three_half]], dtype=np.uint16))
+    assert O.bf16_bits_to_f32(got).tolist() == [[1.0, 1.0 + 2.0 ** -6]]
+
+
+def test_add_residual_zero_and_negation():
+    case = synthetic.norm_linear_case(5, 96, 7, seed=3)
+    x, g, W = bits(case["x"]), bits(case["gamma"]), bits(case["W"])
+    zero = np.zeros_like(x)
+    xa, y32, ybf, rstd = O.add_rmsnorm_linear_bf16(x, zero, g, 1e-6, W)
+    ref32, refbf, refr = O.rmsnorm_linear_bf16(x, g, 1e-6, W)
+    assert np.array_equal(xa, x) and np.array_equal(y32, ref32) and np.array_equal(rstd, refr)
+    neg = x ^ np.uint16(0x8000)
+    xa, y32, _, _ = O.add_rmsnorm_linear_bf16(x, neg, g, 1e-6, W)
+    assert not np.any(O.bf16_bits_to_f32(xa)) and not np.any(y32)
+    q = O.add_rmsnorm_linear_int8(x, neg, g, 1e-6, synthetic.int8_uniform((7, 96), 0, 3).numpy(),
+                                  np.ones(7, dtype=np.float32))
+    assert not q["q"].any() and not q["x_scale"].any()
+
+
+def test_add_residual_commutes():
+    x = _rand_bf16_rows(4, 32, seed=30)
+    r = _rand_bf16_rows(4, 32, seed=31)
+    assert np.array_equal(O.add_residual(x, r), O.add_residual(r, x))
