@@ -41,6 +41,10 @@ WORKLOADS = {
                             desc="pre-attention norm + QKV, 16 decode tokens"),
     "preattn_qkv_T1": dict(kind="bf16", T=1, K=4096, N=6144, bound="hbm", dtype="bf16",
                            desc="pre-attention norm + QKV, 1 decode token"),
+    "preattn_qkv_add_T4096": dict(kind="bf16", add=True, T=4096, K=4096, N=6144, bound="mfma", dtype="bf16",
+                                  desc="residual add -> pre-attention norm -> fused QKV projection"),
+    "preattn_qkv_add_T16": dict(kind="bf16", add=True, T=16, K=4096, N=6144, bound="hbm", dtype="bf16",
+                                desc="residual add -> pre-attention norm -> QKV, 16 decode tokens"),
     "small_T8": dict(kind="bf16", T=8, K=256, N=128, bound="hbm", dtype="bf16",
                      desc="bf16 RMSNorm + Linear, T=8 K=256 N=128"),
     "int8_w8a8": dict(kind="int8", T=2048, K=4096, N=4096, bound="mfma", dtype="int8",
@@ -68,7 +72,8 @@ def bytes_of(w):
     """Algorithmic bytes: every input read once, every output written once."""
     T, K, N = w["T"], w["K"], w["N"]
     if w["kind"] == "bf16":
-        return T * K * 2 + K * 2 + N * K * 2 + T * N * 2
+        # with the residual add: the residual is read and x_add written as well
+        return T * K * 2 * (3 if w.get("add") else 1) + K * 2 + N * K * 2 + T * N * 2
     if w["kind"] == "int8":
         return T * K * 2 + K * 2 + N * K + N * 4 + T * N * 2
     if w["kind"] == "fp32w":
@@ -120,6 +125,9 @@ class Setup:
             "int8": lambda: synthetic.int8_case(w["T"], w["K"], w["N"], name=name),
             "chain": lambda: synthetic.chain_case(w["T"], w["K"], w["R"], w["N"], name=name),
         }[kind]()
+        if w.get("add"):
+            self.case = synthetic.with_residual(self.case)
+            self.case.name = name
         t = {k: (v.to(dev) if v is not None else None) for k, v in self.case.tensors.items()}
         T, K, N = w["T"], w["K"], w["N"]
         eps = self.case.eps
@@ -135,9 +143,16 @@ class Setup:
         self.kernel_key = None
         if kind == "bf16":
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(1, rnl.workspace_bytes("bf16", T, K, N)), dtype=torch.uint8, device=dev)
+            ws = torch.empty(max(1, rnl.workspace_bytes("add_bf16" if w.get("add") else "bf16", T, K, N)),
+                             dtype=torch.uint8, device=dev)
             Wc = t.get("W_copies", [t["W"]])
-            self.step = lambda i: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], y=y, workspace=ws)
+            if w.get("add"):
+                xa = torch.empty_like(t["x"])
+                self.step = lambda i: rnl.add_rmsnorm_linear_bf16(t["x"], t["residual"], t["gamma"], eps,
+                                                                  Wc[i % len(Wc)], y=y, x_add_out=xa, workspace=ws)
+            else:
+                self.step = lambda i: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], y=y,
+                                                              workspace=ws)
             a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
             if T <= 16:
                 # weight streaming: the normed activations are re-read from L2,
@@ -249,7 +264,9 @@ def cpu_baseline(setup, target_s=8.0):
     def run(rows):
         x = bits(c["x"][:rows])
         g = None if c["gamma"] is None else bits(c["gamma"])
-        if kind == "bf16":
+        if kind == "bf16" and w.get("add"):
+            O.add_rmsnorm_linear_bf16(x, bits(c["residual"][:rows]), g, c.eps, bits(c["W"]))
+        elif kind == "bf16":
             O.rmsnorm_linear_bf16(x, g, c.eps, bits(c["W"]))
         elif kind == "fp32w":
             O.rmsnorm_linear_fp32w(x, g, c.eps, c["W"].numpy())

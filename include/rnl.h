@@ -136,6 +136,41 @@ RNL_API int rmsnorm_linear_int8(const void* x, const void* gamma, float eps, con
 RNL_API size_t rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype);
 
 /*
+ * add_rmsnorm_linear_bf16 / add_rmsnorm_linear_int8 -- residual add in front
+ * of the fused norm and projection.
+ *
+ * AT-10 page, section 6: in the pre-attention operator the layer input is
+ * first added to the residual stream and the norm reads that sum; the atom
+ * table of section 3 lists the add-then-norm variant among those that also
+ * give rstd.  Each call first forms
+ *   x_add[t, k] = round_bf16(float(x[t, k]) + float(residual[t, k]))
+ * (one fp32 addition, round to nearest even), writes it to x_add_out (the
+ * new residual stream), and then computes exactly what rmsnorm_linear_bf16
+ * (resp. rmsnorm_linear_int8) computes with x_add in place of x.
+ *
+ *   x, residual  [T, K] bf16, both required.
+ *   x_add_out    [T, K] bf16 output, required; must not overlap any input
+ *                or output buffer (an overlap with x or residual is
+ *                rejected with RNL_ERR_ARG).
+ *   all other arguments, limits and errors as in the call without the add;
+ *   RNL_ERR_NULL also when residual or x_add_out is NULL.
+ */
+RNL_API int add_rmsnorm_linear_bf16(const void* x, const void* residual, void* x_add_out, const void* gamma,
+                                    float eps, const void* W, int w_dtype, void* y, int out_dtype,
+                                    float* rstd_out, int64_t T, int64_t K, int64_t N, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+RNL_API size_t add_rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t N, int w_dtype,
+                                                       int out_dtype);
+
+RNL_API int add_rmsnorm_linear_int8(const void* x, const void* residual, void* x_add_out, const void* gamma,
+                                    float eps, const int8_t* Wq, const float* w_scale, void* y, int out_dtype,
+                                    int8_t* xq_out, float* x_scale_out, float* rstd_out, int64_t T, int64_t K,
+                                    int64_t N, void* workspace, size_t workspace_bytes, void* stream);
+
+RNL_API size_t add_rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype);
+
+/*
  * norm_proj_chain -- two-stage low-rank projection q_a_proj -> RMSNorm -> q_b_proj.
  *
  * AT-10 page, section 5 (MLAProlog query branch: bf16 product with the

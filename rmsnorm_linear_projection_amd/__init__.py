@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   (fp32 weights: the normed rows stay fp32, the large-reduction split-K path);
 * :func:`rmsnorm_linear_int8` -- RMSNorm -> per-token int8 quant -> int8 GEMM ->
   dequant;
+* :func:`add_rmsnorm_linear_bf16`, :func:`add_rmsnorm_linear_int8` -- the same
+  with the residual add in front (x_add = x + residual, also returned);
 * :func:`norm_proj_chain` -- q_a = x W_a^T -> RMSNorm -> qr -> y = qr W_b^T.
 """
 from __future__ import annotations
@@ -24,6 +26,8 @@ import torch
 __all__ = [
     "rmsnorm_linear_bf16",
     "rmsnorm_linear_int8",
+    "add_rmsnorm_linear_bf16",
+    "add_rmsnorm_linear_int8",
     "norm_proj_chain",
     "rms_norm_bf16",
     "rms_norm_quant_int8",
@@ -89,6 +93,14 @@ def load_library() -> ctypes.CDLL:
     lib.linear_bf16.restype = ctypes.c_int
     lib.linear_int8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
     lib.linear_int8.restype = ctypes.c_int
+    lib.add_rmsnorm_linear_bf16.argtypes = [_c_p, _c_p, _c_p] + lib.rmsnorm_linear_bf16.argtypes[1:]
+    lib.add_rmsnorm_linear_bf16.restype = ctypes.c_int
+    lib.add_rmsnorm_linear_bf16_workspace_bytes.argtypes = lib.rmsnorm_linear_bf16_workspace_bytes.argtypes
+    lib.add_rmsnorm_linear_bf16_workspace_bytes.restype = ctypes.c_size_t
+    lib.add_rmsnorm_linear_int8.argtypes = [_c_p, _c_p, _c_p] + lib.rmsnorm_linear_int8.argtypes[1:]
+    lib.add_rmsnorm_linear_int8.restype = ctypes.c_int
+    lib.add_rmsnorm_linear_int8_workspace_bytes.argtypes = lib.rmsnorm_linear_int8_workspace_bytes.argtypes
+    lib.add_rmsnorm_linear_int8_workspace_bytes.restype = ctypes.c_size_t
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -139,23 +151,33 @@ def _workspace(nbytes: int, dev, given):
 
 
 def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.bfloat16) -> int:
-    """Workspace a call needs: kind 'bf16' (T, K, N), 'int8' (T, K, N) or 'chain' (T, K, R, N)."""
+    """Workspace a call needs: kind 'bf16', 'int8', 'add_bf16', 'add_int8' (T, K, N) or 'chain' (T, K, R, N)."""
     lib = load_library()
     if kind == "bf16":
         return int(lib.rmsnorm_linear_bf16_workspace_bytes(*shape, _DTYPE_CODE[w_dtype], _DTYPE_CODE[out_dtype]))
+    if kind == "add_bf16":
+        return int(lib.add_rmsnorm_linear_bf16_workspace_bytes(*shape, _DTYPE_CODE[w_dtype], _DTYPE_CODE[out_dtype]))
     if kind == "int8":
         return int(lib.rmsnorm_linear_int8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
+    if kind == "add_int8":
+        return int(lib.add_rmsnorm_linear_int8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
     if kind == "chain":
         return int(lib.norm_proj_chain_workspace_bytes(*shape))
     raise ValueError(kind)
 
 
-def rmsnorm_linear_bf16(x, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=None, y=None, workspace=None):
-    """y[T,N] = bf16(RMSNorm(x) * gamma) . W[N,K]^T -- AT-10.
+def _residual(x, residual, x_add_out):
+    """Checks the residual-add operands; returns x_add_out (allocated if None)."""
+    _dev_tensor(residual, "residual", torch.bfloat16, 2)
+    _shape(tuple(residual.shape) == tuple(x.shape), "residual must have the shape of x")
+    if x_add_out is None:
+        x_add_out = torch.empty_like(x)
+    _dev_tensor(x_add_out, "x_add_out", torch.bfloat16, 2)
+    _shape(tuple(x_add_out.shape) == tuple(x.shape), "x_add_out must have the shape of x")
+    return x_add_out
 
-    ``W`` bf16 [N, K], or fp32 [N, K] for the fp32-compute variant.  ``gamma``
-    may be None.  ``rstd_out`` (fp32 [T]) receives the per-token rstd.
-    """
+
+def _bf16_call(x, residual, x_add_out, gamma, eps, W, out_dtype, rstd_out, y, workspace):
     lib = load_library()
     _dev_tensor(x, "x", torch.bfloat16, 2)
     _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
@@ -173,19 +195,40 @@ def rmsnorm_linear_bf16(x, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=Non
     _dev_tensor(y, "y", out_dtype)
     _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
     with torch.cuda.device(x.device):
-        need = int(lib.rmsnorm_linear_bf16_workspace_bytes(T, K, N, wcode, ocode))
+        query = lib.rmsnorm_linear_bf16_workspace_bytes if residual is None else \
+            lib.add_rmsnorm_linear_bf16_workspace_bytes
+        need = int(query(T, K, N, wcode, ocode))
         ws, ws_bytes = _workspace(need, x.device, workspace)
-        rc = lib.rmsnorm_linear_bf16(_ptr(x), _ptr(gamma), float(eps), _ptr(W), wcode, _ptr(y), ocode,
-                                     _ptr(rstd_out), T, K, N, _ptr(ws), ws_bytes, _stream(x.device))
+        tail = (_ptr(gamma), float(eps), _ptr(W), wcode, _ptr(y), ocode, _ptr(rstd_out), T, K, N, _ptr(ws),
+                ws_bytes, _stream(x.device))
+        if residual is None:
+            rc = lib.rmsnorm_linear_bf16(_ptr(x), *tail)
+        else:
+            rc = lib.add_rmsnorm_linear_bf16(_ptr(x), _ptr(residual), _ptr(x_add_out), *tail)
     _check(rc)
     return y
 
 
-def rmsnorm_linear_int8(x, gamma, eps, Wq, w_scale, out_dtype=torch.bfloat16, xq_out=None, x_scale_out=None,
-                        rstd_out=None, y=None, workspace=None):
-    """AT-11: RMSNorm -> per-token symmetric int8 quant -> int8 x int8 -> int32 ->
-    dequant with x_scale and w_scale.  ``out_dtype`` torch.int32 returns the raw
-    accumulators."""
+def rmsnorm_linear_bf16(x, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=None, y=None, workspace=None):
+    """y[T,N] = bf16(RMSNorm(x) * gamma) . W[N,K]^T -- AT-10.
+
+    ``W`` bf16 [N, K], or fp32 [N, K] for the fp32-compute variant.  ``gamma``
+    may be None.  ``rstd_out`` (fp32 [T]) receives the per-token rstd.
+    """
+    return _bf16_call(x, None, None, gamma, eps, W, out_dtype, rstd_out, y, workspace)
+
+
+def add_rmsnorm_linear_bf16(x, residual, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=None, y=None,
+                            x_add_out=None, workspace=None):
+    """x_add = bf16(x + residual), then rmsnorm_linear_bf16 on x_add (the
+    pre-attention input norm).  Returns (y, x_add_out)."""
+    x_add_out = _residual(x, residual, x_add_out)
+    y = _bf16_call(x, residual, x_add_out, gamma, eps, W, out_dtype, rstd_out, y, workspace)
+    return y, x_add_out
+
+
+def _int8_call(x, residual, x_add_out, gamma, eps, Wq, w_scale, out_dtype, xq_out, x_scale_out, rstd_out, y,
+               workspace):
     lib = load_library()
     _dev_tensor(x, "x", torch.bfloat16, 2)
     _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
@@ -208,15 +251,39 @@ def rmsnorm_linear_int8(x, gamma, eps, Wq, w_scale, out_dtype=torch.bfloat16, xq
     _dev_tensor(y, "y", out_dtype)
     _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
     with torch.cuda.device(x.device):
-        need = int(lib.rmsnorm_linear_int8_workspace_bytes(T, K, N, ocode))
+        query = lib.rmsnorm_linear_int8_workspace_bytes if residual is None else \
+            lib.add_rmsnorm_linear_int8_workspace_bytes
+        need = int(query(T, K, N, ocode))
         if xq_out is not None and x_scale_out is not None:
             need = 0
         ws, ws_bytes = _workspace(need, x.device, workspace)
-        rc = lib.rmsnorm_linear_int8(_ptr(x), _ptr(gamma), float(eps), _ptr(Wq), _ptr(w_scale), _ptr(y), ocode,
-                                     _ptr(xq_out), _ptr(x_scale_out), _ptr(rstd_out), T, K, N, _ptr(ws),
-                                     ws_bytes, _stream(x.device))
+        tail = (_ptr(gamma), float(eps), _ptr(Wq), _ptr(w_scale), _ptr(y), ocode, _ptr(xq_out), _ptr(x_scale_out),
+                _ptr(rstd_out), T, K, N, _ptr(ws), ws_bytes, _stream(x.device))
+        if residual is None:
+            rc = lib.rmsnorm_linear_int8(_ptr(x), *tail)
+        else:
+            rc = lib.add_rmsnorm_linear_int8(_ptr(x), _ptr(residual), _ptr(x_add_out), *tail)
     _check(rc)
     return y
+
+
+def rmsnorm_linear_int8(x, gamma, eps, Wq, w_scale, out_dtype=torch.bfloat16, xq_out=None, x_scale_out=None,
+                        rstd_out=None, y=None, workspace=None):
+    """AT-11: RMSNorm -> per-token symmetric int8 quant -> int8 x int8 -> int32 ->
+    dequant with x_scale and w_scale.  ``out_dtype`` torch.int32 returns the raw
+    accumulators."""
+    return _int8_call(x, None, None, gamma, eps, Wq, w_scale, out_dtype, xq_out, x_scale_out, rstd_out, y,
+                      workspace)
+
+
+def add_rmsnorm_linear_int8(x, residual, gamma, eps, Wq, w_scale, out_dtype=torch.bfloat16, xq_out=None,
+                            x_scale_out=None, rstd_out=None, y=None, x_add_out=None, workspace=None):
+    """x_add = bf16(x + residual), then rmsnorm_linear_int8 on x_add.  Returns
+    (y, x_add_out)."""
+    x_add_out = _residual(x, residual, x_add_out)
+    y = _int8_call(x, residual, x_add_out, gamma, eps, Wq, w_scale, out_dtype, xq_out, x_scale_out, rstd_out, y,
+                   workspace)
+    return y, x_add_out
 
 
 def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None, workspace=None):

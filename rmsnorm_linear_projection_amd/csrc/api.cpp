@@ -99,6 +99,114 @@ size_t bf16_ws(int64_t T, int64_t K, int64_t N, int w_dtype) {
   return align256((size_t)T * (size_t)K * 2);  // the normed bf16 activations
 }
 
+// x_add_out must not share a byte with x or the residual: the kernels read
+// both after writing parts of x_add.
+bool add_overlaps(const void* x, const void* residual, const void* x_add, int64_t T, int64_t K) {
+  const uintptr_t n = (uintptr_t)T * (uintptr_t)K * 2u;
+  auto hit = [n](const void* a, const void* b) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + n && pb < pa + n;
+  };
+  return hit(x_add, x) || hit(x_add, residual);
+}
+
+// The bf16 / fp32-weight path, with an optional residual added before the norm
+// (residual and x_add both non-null) -- shared by rmsnorm_linear_bf16 and
+// add_rmsnorm_linear_bf16.
+int bf16_path(const void* x, const void* residual, void* x_add, const void* gamma, float eps, const void* W,
+              int w_dtype, void* y, int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "x, W and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK));
+  if (w_dtype != RNL_BF16 && w_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "w_dtype must be RNL_BF16 or RNL_FP32");
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
+  if (w_dtype == RNL_FP32 && N > kMaxN_fp32w) return fail(RNL_ERR_SHAPE, "fp32 weights need N <= 2^20");
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(residual, 16, "residual");
+  RNL_ALIGN(x_add, 16, "x_add_out");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(W, 16, "W");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  if (residual != nullptr && add_overlaps(x, residual, x_add, T, K))
+    return fail(RNL_ERR_ARG, "x_add_out overlaps x or residual");
+  const size_t need = bf16_ws(T, K, N, w_dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* rb = static_cast<const uint16_t*>(residual);
+  uint16_t* xab = static_cast<uint16_t*>(x_add);
+  const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+  const int ok_kind = out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32;
+  if (w_dtype == RNL_FP32) {
+    if (rb != nullptr) {
+      // the split-K kernel reads x itself: form x_add first and project that
+      const hipError_t e = rnl::launch_add_rows(xb, rb, xab, T, K, s);
+      if (e != hipSuccess) return hip_status(e, "residual add launch");
+      xb = xab;
+    }
+    return hip_status(rnl::launch_skinny_fp32w(xb, gb, eps, static_cast<const float*>(W), y, ok_kind,
+                                               rstd_out, T, K, N, workspace, s),
+                      "skinny split-K launch");
+  }
+  const uint16_t* wb = static_cast<const uint16_t*>(W);
+  uint16_t* a = static_cast<uint16_t*>(workspace);
+  const hipError_t e = rb != nullptr ? rnl::launch_add_norm_rows_bf16(xb, rb, xab, gb, eps, T, K, a, rstd_out, s)
+                                     : rnl::launch_norm_rows_bf16(xb, gb, eps, T, K, a, rstd_out, s);
+  if (e != hipSuccess) return hip_status(e, "norm pre-pass launch");
+  return hip_status(project_bf16(a, wb, y, ok_kind, T, N, K, s), "bf16 projection launch");
+}
+
+// The int8 path, with an optional residual added before the norm.
+int int8_path(const void* x, const void* residual, void* x_add, const void* gamma, float eps, const int8_t* Wq,
+              const float* w_scale, void* y, int out_dtype, int8_t* xq_out, float* x_scale_out, float* rstd_out,
+              int64_t T, int64_t K, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || Wq == nullptr || w_scale == nullptr || y == nullptr)
+    return fail(RNL_ERR_NULL, "x, Wq, w_scale and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK_int8));
+  if (K % 16 != 0) return fail(RNL_ERR_SHAPE, "int8 path needs K %% 16 == 0 (K=%lld)", (long long)K);
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32 && out_dtype != RNL_INT32)
+    return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16, RNL_FP32 or RNL_INT32");
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(residual, 16, "residual");
+  RNL_ALIGN(x_add, 16, "x_add_out");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(Wq, 16, "Wq");
+  RNL_ALIGN(w_scale, 4, "w_scale");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(xq_out, 16, "xq_out");
+  RNL_ALIGN(x_scale_out, 4, "x_scale_out");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  if (residual != nullptr && add_overlaps(x, residual, x_add, T, K))
+    return fail(RNL_ERR_ARG, "x_add_out overlaps x or residual");
+  const size_t q_bytes = xq_out ? 0 : align256((size_t)T * (size_t)K);
+  const size_t s_bytes = x_scale_out ? 0 : align256((size_t)T * 4);
+  const size_t need = q_bytes + s_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* q = xq_out ? xq_out : static_cast<int8_t*>(workspace);
+  float* xs = x_scale_out ? x_scale_out
+                          : reinterpret_cast<float*>(static_cast<char*>(workspace) + q_bytes);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+  const hipError_t e =
+      residual != nullptr
+          ? rnl::launch_add_norm_rows_int8(xb, static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(x_add),
+                                           gb, eps, T, K, q, xs, rstd_out, s)
+          : rnl::launch_norm_rows_int8(xb, gb, eps, T, K, q, xs, rstd_out, s);
+  if (e != hipSuccess) return hip_status(e, "norm+quant pre-pass launch");
+  const int kind = out_dtype == RNL_INT32 ? rnl::OUT_I32 : (out_dtype == RNL_FP32 ? rnl::OUT_F32 : rnl::OUT_BF16);
+  return hip_status(rnl::launch_gemm_int8(q, Wq, y, kind, xs, w_scale, T, N, K, s), "int8 GEMM launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,36 +237,20 @@ size_t rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t N, int 
 int rmsnorm_linear_bf16(const void* x, const void* gamma, float eps, const void* W, int w_dtype,
                         void* y, int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (x == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "x, W and y are required");
-  RNL_TRY(check_dims(T, K, N, kMaxK));
-  if (w_dtype != RNL_BF16 && w_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "w_dtype must be RNL_BF16 or RNL_FP32");
-  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
-  if (w_dtype == RNL_FP32 && N > kMaxN_fp32w) return fail(RNL_ERR_SHAPE, "fp32 weights need N <= 2^20");
-  RNL_TRY(check_eps(eps));
-  RNL_ALIGN(x, 16, "x");
-  RNL_ALIGN(gamma, 16, "gamma");
-  RNL_ALIGN(W, 16, "W");
-  RNL_ALIGN(y, 16, "y");
-  RNL_ALIGN(rstd_out, 4, "rstd_out");
-  RNL_ALIGN(workspace, 256, "workspace");
-  const size_t need = bf16_ws(T, K, N, w_dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+  return bf16_path(x, nullptr, nullptr, gamma, eps, W, w_dtype, y, out_dtype, rstd_out, T, K, N, workspace,
+                   workspace_bytes, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  const uint16_t* gb = static_cast<const uint16_t*>(gamma);
-  const int ok_kind = out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32;
-  if (w_dtype == RNL_FP32) {
-    return hip_status(rnl::launch_skinny_fp32w(xb, gb, eps, static_cast<const float*>(W), y, ok_kind,
-                                               rstd_out, T, K, N, workspace, s),
-                      "skinny split-K launch");
-  }
-  const uint16_t* wb = static_cast<const uint16_t*>(W);
-  uint16_t* a = static_cast<uint16_t*>(workspace);
-  hipError_t e = rnl::launch_norm_rows_bf16(xb, gb, eps, T, K, a, rstd_out, s);
-  if (e != hipSuccess) return hip_status(e, "norm pre-pass launch");
-  return hip_status(project_bf16(a, wb, y, ok_kind, T, N, K, s), "bf16 projection launch");
+size_t add_rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t N, int w_dtype, int out_dtype) {
+  return rmsnorm_linear_bf16_workspace_bytes(T, K, N, w_dtype, out_dtype);
+}
+
+int add_rmsnorm_linear_bf16(const void* x, const void* residual, void* x_add_out, const void* gamma, float eps,
+                            const void* W, int w_dtype, void* y, int out_dtype, float* rstd_out, int64_t T,
+                            int64_t K, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  if (residual == nullptr || x_add_out == nullptr) return fail(RNL_ERR_NULL, "residual and x_add_out are required");
+  return bf16_path(x, residual, x_add_out, gamma, eps, W, w_dtype, y, out_dtype, rstd_out, T, K, N, workspace,
+                   workspace_bytes, stream);
 }
 
 size_t rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype) {
@@ -172,38 +264,21 @@ int rmsnorm_linear_int8(const void* x, const void* gamma, float eps, const int8_
                         const float* w_scale, void* y, int out_dtype, int8_t* xq_out,
                         float* x_scale_out, float* rstd_out, int64_t T, int64_t K, int64_t N,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (x == nullptr || Wq == nullptr || w_scale == nullptr || y == nullptr)
-    return fail(RNL_ERR_NULL, "x, Wq, w_scale and y are required");
-  RNL_TRY(check_dims(T, K, N, kMaxK_int8));
-  if (K % 16 != 0) return fail(RNL_ERR_SHAPE, "int8 path needs K %% 16 == 0 (K=%lld)", (long long)K);
-  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32 && out_dtype != RNL_INT32)
-    return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16, RNL_FP32 or RNL_INT32");
-  RNL_TRY(check_eps(eps));
-  RNL_ALIGN(x, 16, "x");
-  RNL_ALIGN(gamma, 16, "gamma");
-  RNL_ALIGN(Wq, 16, "Wq");
-  RNL_ALIGN(w_scale, 4, "w_scale");
-  RNL_ALIGN(y, 16, "y");
-  RNL_ALIGN(xq_out, 16, "xq_out");
-  RNL_ALIGN(x_scale_out, 4, "x_scale_out");
-  RNL_ALIGN(rstd_out, 4, "rstd_out");
-  RNL_ALIGN(workspace, 256, "workspace");
-  const size_t q_bytes = xq_out ? 0 : align256((size_t)T * (size_t)K);
-  const size_t s_bytes = x_scale_out ? 0 : align256((size_t)T * 4);
-  const size_t need = q_bytes + s_bytes;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+  return int8_path(x, nullptr, nullptr, gamma, eps, Wq, w_scale, y, out_dtype, xq_out, x_scale_out, rstd_out, T,
+                   K, N, workspace, workspace_bytes, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int8_t* q = xq_out ? xq_out : static_cast<int8_t*>(workspace);
-  float* xs = x_scale_out ? x_scale_out
-                          : reinterpret_cast<float*>(static_cast<char*>(workspace) + q_bytes);
-  hipError_t e = rnl::launch_norm_rows_int8(static_cast<const uint16_t*>(x),
-                                            static_cast<const uint16_t*>(gamma), eps, T, K, q, xs,
-                                            rstd_out, s);
-  if (e != hipSuccess) return hip_status(e, "norm+quant pre-pass launch");
-  const int kind = out_dtype == RNL_INT32 ? rnl::OUT_I32 : (out_dtype == RNL_FP32 ? rnl::OUT_F32 : rnl::OUT_BF16);
-  return hip_status(rnl::launch_gemm_int8(q, Wq, y, kind, xs, w_scale, T, N, K, s), "int8 GEMM launch");
+size_t add_rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype) {
+  return rmsnorm_linear_int8_workspace_bytes(T, K, N, out_dtype);
+}
+
+int add_rmsnorm_linear_int8(const void* x, const void* residual, void* x_add_out, const void* gamma, float eps,
+                            const int8_t* Wq, const float* w_scale, void* y, int out_dtype, int8_t* xq_out,
+                            float* x_scale_out, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (residual == nullptr || x_add_out == nullptr) return fail(RNL_ERR_NULL, "residual and x_add_out are required");
+  return int8_path(x, residual, x_add_out, gamma, eps, Wq, w_scale, y, out_dtype, xq_out, x_scale_out, rstd_out, T,
+                   K, N, workspace, workspace_bytes, stream);
 }
 
 size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N) {

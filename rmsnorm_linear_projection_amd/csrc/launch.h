@@ -19,6 +19,17 @@ hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s);
+// The same, applied to x_add = bf16(x + residual) (sum in fp32), which is also
+// written to x_add.
+hipError_t launch_add_norm_rows_bf16(const uint16_t* x, const uint16_t* residual, uint16_t* x_add,
+                                     const uint16_t* gamma, float eps, int64_t T, int64_t K, uint16_t* a_out,
+                                     float* rstd_out, hipStream_t s);
+hipError_t launch_add_norm_rows_int8(const uint16_t* x, const uint16_t* residual, uint16_t* x_add,
+                                     const uint16_t* gamma, float eps, int64_t T, int64_t K, int8_t* q_out,
+                                     float* x_scale_out, float* rstd_out, hipStream_t s);
+// x_add = bf16(x + residual) alone.
+hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t* x_add, int64_t T, int64_t K,
+                           hipStream_t s);
 // Same norm (bf16 out) applied to rows that are the bf16 rounding of the sum of S
 // fp32 split-K partials part[S, T, K], added in split order.
 hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,

@@ -16,6 +16,8 @@
 // The row may also be the bf16 rounding of the sum of split-K partial rows of
 // a preceding projection (the q_a -> norm step of the low-rank chain): the
 // partials are added in split order, so the result does not depend on timing.
+#include <algorithm>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -83,13 +85,36 @@ __device__ __forceinline__ uint32_t q4(const float n[8], int base, float s) {
   return r;
 }
 
+// x + residual for 8 packed bf16 pairs: each sum in fp32 (one rounding), then
+// rounded to bf16 (nearest even) -- the residual-add reading of the AT-10 page,
+// section 6 (the norm reads the bf16 sum, which is also written back).
+__device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = pack_bf16x2(__fadd_rn(bf16lo(a[j]), bf16lo(b[j])), __fadd_rn(bf16hi(a[j]), bf16hi(b[j])));
+  return r;
+}
+
 // Row sources: chunk idx (8 consecutive elements, packed bf16) of row t.
+// keep(t, idx, v) is called once per chunk in the first pass over the row.
 struct RowBf16 {
   const uint16_t* x;  // [T, K] bf16
   int64_t K;
   __device__ u32x4 operator()(int64_t t, int idx) const {
     return reinterpret_cast<const u32x4*>(x + t * K)[idx];
   }
+  __device__ void keep(int64_t, int, u32x4) const {}
+};
+struct RowAddBf16 {
+  const uint16_t* x;  // [T, K] bf16
+  const uint16_t* r;  // [T, K] bf16 residual
+  uint16_t* x_add;    // [T, K] bf16: x + r, written in the first pass
+  int64_t K;
+  __device__ u32x4 operator()(int64_t t, int idx) const {
+    return add_bf16x8(reinterpret_cast<const u32x4*>(x + t * K)[idx], reinterpret_cast<const u32x4*>(r + t * K)[idx]);
+  }
+  __device__ void keep(int64_t t, int idx, u32x4 v) const { reinterpret_cast<u32x4*>(x_add + t * K)[idx] = v; }
 };
 struct RowPartials {
   const float* part;  // [S, T, K] fp32
@@ -106,6 +131,7 @@ struct RowPartials {
     return u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
                  pack_bf16x2(hi[2], hi[3])};
   }
+  __device__ void keep(int64_t, int, u32x4) const {}
 };
 
 // CPT > 0: each thread keeps CPT 16-byte chunks of the row in registers.
@@ -128,10 +154,15 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * kThreads;
       v[c] = idx < nch ? row(t, idx) : u32x4{0u, 0u, 0u, 0u};
+      if (idx < nch) row.keep(t, idx, v[c]);
       ss += sumsq8(v[c]);
     }
   } else {
-    for (int idx = tid; idx < nch; idx += kThreads) ss += sumsq8(row(t, idx));
+    for (int idx = tid; idx < nch; idx += kThreads) {
+      const u32x4 w = row(t, idx);
+      row.keep(t, idx, w);
+      ss += sumsq8(w);
+    }
   }
   const float S = block_sum(ss, red);
   const float rstd = rstd_from_sumsq(S, inv_k, eps);
@@ -196,11 +227,11 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 // lane loads its CPL chunks of x and of gamma in one round trip, the sum of
 // squares and amax are reduced with wavefront shuffles (no barriers), and the
 // normed values stay in registers between the amax and the quantisation.
-template <int CPL, bool INT8>
+template <int CPL, bool INT8, bool ADD>
 __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps, float inv_k,
-    int64_t T, int64_t K, void* __restrict__ out, float* __restrict__ x_scale_out,
-    float* __restrict__ rstd_out) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual, uint16_t* __restrict__ x_add,
+    const uint16_t* __restrict__ gamma, float eps, float inv_k, int64_t T, int64_t K,
+    void* __restrict__ out, float* __restrict__ x_scale_out, float* __restrict__ rstd_out) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront: no barrier follows
@@ -214,6 +245,23 @@ __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
     const int idx = lane + 64 * c;
     v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
     gv[c] = (gr != nullptr && idx < nch) ? gr[idx] : u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (ADD) {
+    // x + residual: the sum is what the norm reads, and is written back
+    const u32x4* rr = reinterpret_cast<const u32x4*>(residual + t * K);
+    u32x4* xa = reinterpret_cast<u32x4*>(x_add + t * K);
+    u32x4 rv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + 64 * c;
+      rv[c] = idx < nch ? rr[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + 64 * c;
+      v[c] = add_bf16x8(v[c], rv[c]);
+      if (idx < nch) xa[idx] = v[c];
+    }
   }
 #pragma unroll
   for (int c = 0; c < CPL; ++c) ss += sumsq8(v[c]);
@@ -260,13 +308,16 @@ __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
   }
 }
 
-template <bool INT8>
-hipError_t launch_norm_wave(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T, int64_t K,
-                            void* out, float* x_scale_out, float* rstd_out, hipStream_t s) {
+template <bool INT8, bool ADD>
+hipError_t launch_norm_wave(const uint16_t* x, const uint16_t* residual, uint16_t* x_add, const uint16_t* gamma,
+                            float eps, int64_t T, int64_t K, void* out, float* x_scale_out, float* rstd_out,
+                            hipStream_t s) {
   const float inv_k = 1.0f / (float)K;
   const int64_t per = (K / 8 + 63) / 64;
   dim3 grid((unsigned)((T + 3) / 4)), block(kThreads);
-#define RNL_NORM_WAVE(C)                                                                                hipLaunchKernelGGL((norm_rows_wave_kernel<C, INT8>), grid, block, 0, s, x, gamma, eps, inv_k, T, K,                      out, x_scale_out, rstd_out)
+#define RNL_NORM_WAVE(C)                                                                                     \
+  hipLaunchKernelGGL((norm_rows_wave_kernel<C, INT8, ADD>), grid, block, 0, s, x, residual, x_add, gamma, eps, \
+                     inv_k, T, K, out, x_scale_out, rstd_out)
   if (per <= 1) RNL_NORM_WAVE(1);
   else if (per <= 2) RNL_NORM_WAVE(2);
   else if (per <= 4) RNL_NORM_WAVE(4);
@@ -301,15 +352,51 @@ hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int
 
 hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
-  if (K <= kWaveRowMaxK) return launch_norm_wave<false>(x, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
+  if (K <= kWaveRowMaxK)
+    return launch_norm_wave<false, false>(x, nullptr, nullptr, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
   return launch_norm<false>(RowBf16{x, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
 
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s) {
-  if (K <= kWaveRowMaxK) return launch_norm_wave<true>(x, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+  if (K <= kWaveRowMaxK)
+    return launch_norm_wave<true, false>(x, nullptr, nullptr, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
   return launch_norm<true>(RowBf16{x, K}, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+}
+
+hipError_t launch_add_norm_rows_bf16(const uint16_t* x, const uint16_t* residual, uint16_t* x_add,
+                                     const uint16_t* gamma, float eps, int64_t T, int64_t K, uint16_t* a_out,
+                                     float* rstd_out, hipStream_t s) {
+  if (K <= kWaveRowMaxK)
+    return launch_norm_wave<false, true>(x, residual, x_add, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
+  return launch_norm<false>(RowAddBf16{x, residual, x_add, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
+}
+
+hipError_t launch_add_norm_rows_int8(const uint16_t* x, const uint16_t* residual, uint16_t* x_add,
+                                     const uint16_t* gamma, float eps, int64_t T, int64_t K, int8_t* q_out,
+                                     float* x_scale_out, float* rstd_out, hipStream_t s) {
+  if (K <= kWaveRowMaxK)
+    return launch_norm_wave<true, true>(x, residual, x_add, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+  return launch_norm<true>(RowAddBf16{x, residual, x_add, K}, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
+}
+
+namespace {
+__global__ __launch_bounds__(kThreads) void add_rows_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ r,
+                                                            u32x4* __restrict__ out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    out[i] = add_bf16x8(x[i], r[i]);
+}
+}  // namespace
+
+hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t* x_add, int64_t T, int64_t K,
+                           hipStream_t s) {
+  const int64_t n = T * K / 8;
+  const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL(add_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(residual),
+                     reinterpret_cast<u32x4*>(x_add), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,

@@ -27,7 +27,7 @@ import torch
 EPS = 1e-6
 
 # stream ids: one per tensor role, so that adding a tensor never shifts another
-_S_X, _S_GAMMA, _S_W, _S_WSCALE, _S_WA, _S_WB = 1, 2, 3, 4, 5, 6
+_S_X, _S_GAMMA, _S_W, _S_WSCALE, _S_WA, _S_WB, _S_RES = 1, 2, 3, 4, 5, 6, 7
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -92,6 +92,15 @@ def int8_case(T: int, K: int, N: int, seed: int = 0, gamma: bool = True, name: s
     return Case(name or f"int8_T{T}_K{K}_N{N}", t, EPS, {"T": T, "K": K, "N": N})
 
 
+def with_residual(case: Case, seed: int = 0, std: float = 2.0) -> Case:
+    """Adds residual[T,K] bf16 ~ N(0, std^2) (the residual stream the layer input
+    is added to before the norm); the other tensors are unchanged."""
+    T, K = case["x"].shape
+    t = dict(case.tensors)
+    t["residual"] = normal((T, K), std, seed, _S_RES)
+    return Case(case.name.replace("_T", "_add_T", 1), t, case.eps, dict(case.dims))
+
+
 def chain_case(T: int, K: int, R: int, N: int, seed: int = 0, gamma: bool = True,
                name: str | None = None) -> Case:
     """x[T,K] -> W_a[R,K] -> RMSNorm(R, gamma) -> W_b[N,R]; all bf16."""
@@ -113,6 +122,11 @@ def small_norm_linear(seed: int = 0) -> Case:
 def preattn_qkv(T: int = 4096, seed: int = 0) -> Case:
     """Pre-attention norm + fused QKV projection, K=4096, N=6144 (Q 4096 + K 1024 + V 1024)."""
     return norm_linear_case(T, 4096, 6144, seed, name=f"preattn_qkv_bf16_T{T}_K4096_N6144")
+
+
+def preattn_qkv_add(T: int = 4096, seed: int = 0) -> Case:
+    """Residual add -> pre-attention norm -> fused QKV projection, K=4096, N=6144."""
+    return with_residual(preattn_qkv(T, seed), seed)
 
 
 def int8_w8a8(seed: int = 0) -> Case:

@@ -110,6 +110,42 @@ def test_forced_variant_changes_workspace(lib, monkeypatch):
     assert lib.norm_proj_chain_workspace_bytes(4, 7168, 1536, 24576) > small
 
 
+def add_bf16_call(lib, x=FAKE, r=ctypes.c_void_p(0x20000), xa=ctypes.c_void_p(0x30000), g=NULL, eps=1e-6, W=FAKE,
+                  wd=1, y=FAKE, od=1, rstd=NULL, T=4, K=64, N=8, ws=FAKE, wsb=1 << 30):
+    return lib.add_rmsnorm_linear_bf16(x, r, xa, g, eps, W, wd, y, od, rstd, T, K, N, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(r=NULL), "RNL_ERR_NULL"),
+    (dict(xa=NULL), "RNL_ERR_NULL"),
+    (dict(x=NULL), "RNL_ERR_NULL"),
+    (dict(r=ctypes.c_void_p(0x20008)), "RNL_ERR_ALIGN"),
+    (dict(xa=ctypes.c_void_p(0x30004)), "RNL_ERR_ALIGN"),
+    (dict(xa=FAKE), "RNL_ERR_ARG"),                      # x_add_out is x
+    (dict(xa=ctypes.c_void_p(0x20000 + 496)), "RNL_ERR_ARG"),  # overlaps the residual's last row
+    (dict(wd=2, xa=ctypes.c_void_p(0x20000)), "RNL_ERR_ARG"),
+    (dict(K=12), "RNL_ERR_SHAPE"),
+    (dict(T=64, ws=NULL), "RNL_ERR_WORKSPACE"),
+])
+def test_add_bf16_validation(lib, kw, code):
+    assert add_bf16_call(lib, **kw) == E[code]
+
+
+def test_add_bf16_accepts_adjacent_buffers(lib):
+    # x_add_out right after the residual's last byte passes the overlap check; the call then
+    # fails only on the missing workspace, which is checked after it
+    assert add_bf16_call(lib, xa=ctypes.c_void_p(0x20000 + 64 * 64 * 2 - 16), T=64, ws=NULL) == E["RNL_ERR_ARG"]
+    assert add_bf16_call(lib, xa=ctypes.c_void_p(0x20000 + 64 * 64 * 2), T=64, ws=NULL) == E["RNL_ERR_WORKSPACE"]
+
+
+def test_add_workspace_queries_match(lib):
+    for T, K, N, wd in ((16, 4096, 6144, 1), (4096, 4096, 6144, 1), (512, 28672, 24, 2)):
+        assert lib.add_rmsnorm_linear_bf16_workspace_bytes(T, K, N, wd, 1) == \
+            lib.rmsnorm_linear_bf16_workspace_bytes(T, K, N, wd, 1)
+    assert lib.add_rmsnorm_linear_int8_workspace_bytes(2048, 4096, 4096, 1) == \
+        lib.rmsnorm_linear_int8_workspace_bytes(2048, 4096, 4096, 1)
+
+
 def int8_call(lib, x=FAKE, g=NULL, eps=1e-6, Wq=FAKE, ws=FAKE, y=FAKE, od=1, xq=NULL, xs=NULL, rstd=NULL,
               T=4, K=64, N=8, wsp=FAKE, wsb=1 << 30):
     return lib.rmsnorm_linear_int8(x, g, eps, Wq, ws, y, od, xq, xs, rstd, T, K, N, wsp, wsb, NULL)
@@ -127,6 +163,24 @@ def int8_call(lib, x=FAKE, g=NULL, eps=1e-6, Wq=FAKE, ws=FAKE, y=FAKE, od=1, xq=
 ])
 def test_int8_validation(lib, kw, code):
     assert int8_call(lib, **kw) == E[code]
+
+
+def add_int8_call(lib, x=FAKE, r=ctypes.c_void_p(0x20000), xa=ctypes.c_void_p(0x30000), g=NULL, eps=1e-6,
+                  Wq=FAKE, ws=FAKE, y=FAKE, od=1, xq=NULL, xs=NULL, rstd=NULL, T=4, K=64, N=8, wsp=FAKE,
+                  wsb=1 << 30):
+    return lib.add_rmsnorm_linear_int8(x, r, xa, g, eps, Wq, ws, y, od, xq, xs, rstd, T, K, N, wsp, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(r=NULL), "RNL_ERR_NULL"),
+    (dict(xa=NULL), "RNL_ERR_NULL"),
+    (dict(Wq=NULL), "RNL_ERR_NULL"),
+    (dict(xa=ctypes.c_void_p(0x20000)), "RNL_ERR_ARG"),
+    (dict(K=24), "RNL_ERR_SHAPE"),
+    (dict(wsp=NULL), "RNL_ERR_WORKSPACE"),
+])
+def test_add_int8_validation(lib, kw, code):
+    assert add_int8_call(lib, **kw) == E[code]
 
 
 def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, T=4, K=64, R=32,

@@ -425,3 +425,150 @@ def test_atom_linear_int8(M, K, N):
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
     y_ref = O.dequant(acc_ref, xs.numpy(), ws.numpy())
     assert np.array_equal(y.cpu().numpy(), y_ref)
+
+
+# ---------------------------------------------------------------------------
+# residual add before the norm: x_add bit-exact against the oracle's add, then
+# the same checks as the paths without the add, on x_add; and the call must
+# give the same bits as the call without the add made on the device's x_add
+# ---------------------------------------------------------------------------
+def run_add_bf16(case, out_dtype=torch.bfloat16):
+    x, r, g, W = dev(case["x"]), dev(case["residual"]), dev(case["gamma"]), dev(case["W"])
+    T = x.shape[0]
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y, xa = rnl.add_rmsnorm_linear_bf16(x, r, g, EPS, W, out_dtype=out_dtype, rstd_out=rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), xa.cpu(), rstd.cpu().numpy()
+
+
+def check_add_bf16_case(case, rows=None, out_dtype=torch.bfloat16):
+    y, xa, rstd = run_add_bf16(case, out_dtype)
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb, rb = bits(case["x"])[rows], bits(case["residual"])[rows]
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    xa_ref = O.add_residual(xb, rb)
+    assert np.array_equal(bits(xa)[rows], xa_ref), \
+        f"{case.name}: x_add not bit-exact ({int((bits(xa)[rows] != xa_ref).sum())} differ)"
+    _, rstd_own = O.rms_norm_rows(xa_ref, gb, EPS)
+    assert_rstd(rstd[rows], rstd_own, case.name)
+    if case["W"].dtype == torch.float32:
+        _, y_ref, _ = O.add_rmsnorm_linear_fp32w(xb, rb, gb, EPS, case["W"].numpy(), rstd=rstd[rows])
+        if out_dtype == torch.float32:
+            scale = max(float(np.sqrt(np.mean(y_ref.astype(np.float64) ** 2))), 1e-30)
+            err = np.abs(y.numpy()[rows].astype(np.float64) - y_ref)
+            assert (err <= 1e-5 * np.maximum(np.abs(y_ref), scale)).all(), f"{case.name}: max err {err.max():.3g}"
+        else:
+            assert_bf16_close(f32(y)[rows], y_ref, case.name)
+    else:
+        _, y32, _, _ = O.add_rmsnorm_linear_bf16(xb, rb, gb, EPS, bits(case["W"]), rstd=rstd[rows])
+        assert_bf16_close(f32(y)[rows], y32, case.name)
+    # the add path computes exactly the plain path on x_add
+    y_plain = rnl.rmsnorm_linear_bf16(xa.cuda(), dev(case["gamma"]), EPS, dev(case["W"]), out_dtype=out_dtype)
+    assert torch.equal(y_plain.cpu().view(torch.uint8), y.view(torch.uint8)), f"{case.name}: differs from plain path"
+    return y
+
+
+ADD_BF16 = [
+    (8, 256, 128),     # weight streaming, one wavefront per row
+    (16, 4104, 40),
+    (300, 1032, 200),  # tiled GEMM, ragged tiles
+    (5, 12296, 40),    # rows held in registers across a workgroup
+    (40, 20488, 100),  # rows re-read for each pass
+    (3, 72, 5),
+]
+
+
+@pytest.mark.parametrize("T,K,N", ADD_BF16)
+@pytest.mark.parametrize("gamma", [True, False])
+def test_add_bf16_small(T, K, N, gamma):
+    base = synthetic.norm_linear_case(T, K, N, seed=T + 2 * N, gamma=gamma)
+    check_add_bf16_case(synthetic.with_residual(base, seed=T + 2 * N))
+
+
+def test_add_bf16_fp32_output():
+    case = synthetic.with_residual(synthetic.norm_linear_case(17, 256, 130, seed=4), seed=4)
+    check_add_bf16_case(case, out_dtype=torch.float32)
+
+
+def test_add_bf16_cancelling_residual():
+    # residual = -x on some rows: x_add is exactly zero there, and so is y
+    case = synthetic.with_residual(synthetic.norm_linear_case(24, 512, 64, seed=8), seed=8)
+    r = case.tensors["residual"].clone()
+    r[2] = -case["x"][2]
+    r[5] = 0
+    case.tensors["residual"] = r
+    y = check_add_bf16_case(case)
+    assert (f32(y)[2] == 0).all()
+
+
+@pytest.mark.parametrize("T,K,N,gamma", [(70, 4104, 33, False), (16, 28672, 24, True), (3, 64, 5, False)])
+def test_add_fp32w(T, K, N, gamma):
+    base = synthetic.norm_linear_case(T, K, N, seed=T + N, gamma=gamma, w_dtype="fp32")
+    check_add_bf16_case(synthetic.with_residual(base, seed=T + N), out_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("T", [4096, 16])
+def test_add_preattn_qkv_full_size(T):
+    """Residual add -> pre-attention norm -> fused QKV projection, K=4096, N=6144, at full size."""
+    case = synthetic.preattn_qkv_add(T)
+    y1 = check_add_bf16_case(case, rows=sample_rows(T, 40))
+    y2, _, _ = run_add_bf16(case)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+
+
+def run_add_int8(case, out_dtype):
+    x, r, g = dev(case["x"]), dev(case["residual"]), dev(case["gamma"])
+    Wq, ws = dev(case["Wq"]), dev(case["w_scale"])
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(T, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y, xa = rnl.add_rmsnorm_linear_int8(x, r, g, EPS, Wq, ws, out_dtype=out_dtype, xq_out=xq, x_scale_out=xs,
+                                        rstd_out=rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), xa.cpu(), xq.cpu().numpy(), xs.cpu().numpy(), rstd.cpu().numpy()
+
+
+def check_add_int8_case(case, rows=None):
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb, rb = bits(case["x"])[rows], bits(case["residual"])[rows]
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    Wq, wsc = case["Wq"].numpy(), case["w_scale"].numpy()
+
+    acc, xa, xq, xs, rstd = run_add_int8(case, torch.int32)
+    xa_ref = O.add_residual(xb, rb)
+    assert np.array_equal(bits(xa)[rows], xa_ref), f"{case.name}: x_add not bit-exact"
+    _, rstd_own = O.rms_norm_rows(xa_ref, gb, EPS)
+    assert_rstd(rstd[rows], rstd_own, case.name)
+    ref = O.add_rmsnorm_linear_int8(xb, rb, gb, EPS, Wq, wsc, rstd=rstd[rows])
+    assert np.array_equal(ref["x_add"], xa_ref)
+    assert np.array_equal(xq[rows], ref["q"]), f"{case.name}: xq not bit-exact"
+    assert np.array_equal(xs[rows], ref["x_scale"]), f"{case.name}: x_scale not bit-exact"
+    assert np.array_equal(acc.numpy()[rows].astype(np.int64), ref["acc"]), f"{case.name}: int32 acc not bit-exact"
+
+    yf, _, _, _, _ = run_add_int8(case, torch.float32)
+    rel = np.abs(yf.numpy()[rows] - ref["y32"]) / np.maximum(np.abs(ref["y32"]), 1e-30)
+    assert (rel <= 1e-5).all(), f"{case.name}: fp32 dequant off by {rel.max():.3g}"
+    yb, _, _, _, _ = run_add_int8(case, torch.bfloat16)
+    assert_bf16_close(f32(yb)[rows], ref["y32"], case.name)
+    y_plain = rnl.rmsnorm_linear_int8(xa.cuda(), dev(case["gamma"]), EPS, dev(case["Wq"]), dev(case["w_scale"]))
+    assert torch.equal(y_plain.cpu().view(torch.int16), yb.view(torch.int16)), f"{case.name}: differs from plain path"
+
+
+@pytest.mark.parametrize("T,K,N,gamma", [
+    (37, 256, 72, True),
+    (130, 4112, 100, False),  # K tail of a 128-byte k-step
+    (9, 12304, 40, True),     # rows held in registers across a workgroup
+    (4, 20480, 16, False),    # rows re-read for each pass
+])
+def test_add_int8(T, K, N, gamma):
+    base = synthetic.int8_case(T, K, N, seed=T + N, gamma=gamma)
+    check_add_int8_case(synthetic.with_residual(base, seed=T + N))
+
+
+def test_add_int8_w8a8_full_size():
+    """Residual add, then INT8 W8A8 norm + linear, T=2048, K=4096, N=4096, at full size."""
+    case = synthetic.with_residual(synthetic.int8_w8a8())
+    check_add_int8_case(case, rows=sample_rows(2048, 32))
