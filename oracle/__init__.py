@@ -28,4 +28,7 @@ from .rmsnorm_linear import (  # noqa: F401
     add_rmsnorm_linear_bf16,
     add_rmsnorm_linear_fp32w,
     add_rmsnorm_linear_int8,
+    rope_rotate_half,
+    head_rms_norm,
+    preattn_qkv,
 )

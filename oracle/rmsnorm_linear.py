@@ -258,6 +258,84 @@ def add_residual(x_bits, r_bits) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Post-projection V stage: per-head RMSNorm and rotary embedding
+# ----------------------------------------------------------------------------
+def rope_rotate_half(n: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotary embedding of fp32 head vectors n [R, D] by the angles whose
+    cosines and sines are cos, sin [R, D/2] (fp32).
+
+    AT-10 page section 6 and the SK-03 page (key features: the optional V
+    stage after the projection) name RoPE after the per-head norm but do not
+    define it.  READING: the rotate-half pairing of the Qwen3 family the AT-10
+    page names -- element i is rotated together with element i + D/2 -- with
+    the angles supplied per row and pair by the caller, in fp32 on the normed
+    values before the bf16 cast, every product and sum rounded once:
+        out[i]       = fl( fl(n[i] c[i])       - fl(n[i + D/2] s[i]) )
+        out[i + D/2] = fl( fl(n[i + D/2] c[i]) + fl(n[i] s[i]) )
+    """
+    n = np.asarray(n, dtype=F32)
+    h = n.shape[-1] // 2
+    c = np.asarray(cos, dtype=F32)
+    s = np.asarray(sin, dtype=F32)
+    lo, hi = n[..., :h], n[..., h:]
+    out = np.empty_like(n)
+    out[..., :h] = ((lo * c).astype(F32) - (hi * s).astype(F32)).astype(F32)
+    out[..., h:] = ((hi * c).astype(F32) + (lo * s).astype(F32)).astype(F32)
+    return out
+
+
+def head_rms_norm(y_bits, col0: int, H: int, D: int, gamma_bits, eps: float, cos=None, sin=None, rstd=None):
+    """Per-head RMSNorm of the H heads of D columns that start at column col0
+    of y [T, N] (bf16 bits), optionally followed by RoPE; columns outside the
+    heads are returned unchanged.  Returns (out bits [T, N], rstd [T, H]).
+
+    AT-10 page section 6: after the fused QKV projection the output is split
+    into Q, K and V and a norm is applied per head; section 9's golden chain
+    likewise reshapes the q_b output to (heads, head_dim) and applies RMSNorm
+    again.  READING: each head is one AT-03 row of D values read from the
+    bf16 projection output (the tensor the split takes apart), normed as in
+    rms_norm_rows with gamma [D] shared by the heads, rotated by RoPE when
+    cos/sin [T, D/2] are given (the same angles for every head of a token),
+    and rounded to bf16.
+    """
+    y = np.asarray(y_bits, dtype=np.uint16)
+    T = y.shape[0]
+    seg = y[:, col0:col0 + H * D].reshape(T * H, D)
+    n, r = rms_norm_rows(seg, gamma_bits, eps, None if rstd is None else np.asarray(rstd, dtype=F32).reshape(-1))
+    if cos is not None:
+        c = np.repeat(np.asarray(cos, dtype=F32), H, axis=0)  # row t*H + h takes the angles of token t
+        sn = np.repeat(np.asarray(sin, dtype=F32), H, axis=0)
+        n = rope_rotate_half(n, c, sn)
+    out = y.copy()
+    out[:, col0:col0 + H * D] = f32_to_bf16_bits(n).reshape(T, H * D)
+    return out, r.reshape(T, H)
+
+
+def preattn_qkv(x_bits, r_bits, gamma_bits, eps, W_bits, Hq, Hkv, D, gq_bits, gk_bits, head_eps,
+                cos=None, sin=None, rstd=None, head_rstd=None):
+    """Pre-attention block of the AT-10 page section 6: optional residual add,
+    input RMSNorm, fused QKV projection (W [(Hq + 2 Hkv) D, K], columns Q | K |
+    V), split into Hq query heads, Hkv key heads and Hkv value heads of D
+    columns, per-head RMSNorm of Q (gamma_q) and K (gamma_k) with RoPE on both,
+    V as projected.
+
+    Returns a dict: x_add (bits or None), y_proj (bf16 bits of the projection),
+    y (bf16 bits after the head stage), rstd [T], head_rstd [T, Hq + Hkv].
+    ``rstd`` / ``head_rstd`` replace the computed values when given (the
+    device's own), so that downstream values can be compared bit for bit.
+    """
+    xa = None
+    if r_bits is not None:
+        xa = add_residual(x_bits, r_bits)
+        x_bits = xa
+    _, yb, rstd = rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd)
+    hr = None if head_rstd is None else np.asarray(head_rstd, dtype=F32)
+    y, rq = head_rms_norm(yb, 0, Hq, D, gq_bits, head_eps, cos, sin, None if hr is None else hr[:, :Hq])
+    y, rk = head_rms_norm(y, Hq * D, Hkv, D, gk_bits, head_eps, cos, sin, None if hr is None else hr[:, Hq:])
+    return {"x_add": xa, "y_proj": yb, "y": y, "rstd": rstd, "head_rstd": np.concatenate([rq, rk], axis=1)}
+
+
+# ----------------------------------------------------------------------------
 # Entry points (same names and argument meanings as the C-ABI library)
 # ----------------------------------------------------------------------------
 def rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd=None):

@@ -483,3 +483,126 @@ def test_add_residual_commutes():
     x = _rand_bf16_rows(4, 32, seed=30)
     r = _rand_bf16_rows(4, 32, seed=31)
     assert np.array_equal(O.add_residual(x, r), O.add_residual(r, x))
+
+
+# ---------------------------------------------------------------------------
+# post-projection stage: per-head RMSNorm and rotary embedding
+# ---------------------------------------------------------------------------
+def _angles(T, half, seed):
+    phi = np.random.default_rng(seed).uniform(0.0, 2.0 * np.pi, size=(T, half))
+    return np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
+
+
+def test_head_norm_matches_per_head_loop():
+    """Head (t, h) is the norm of its own D columns, rotated by token t's angles, and
+    nothing else: a loop over tokens and heads gives the same bits."""
+    T, D, H, col0, N = 5, 16, 3, 8, 64
+    y = _rand_bf16_rows(T, N, seed=40, std=3.0)
+    g = bits(synthetic.uniform((D,), 0.5, 1.5, 4, 2))
+    c, s = _angles(T, D // 2, 41)
+    out, r = O.head_rms_norm(y, col0, H, D, g, 1e-6, c, s)
+    assert r.shape == (T, H)
+    for t in range(T):
+        for h in range(H):
+            a = col0 + h * D
+            n, rr = O.rms_norm_rows(y[t:t + 1, a:a + D], g, 1e-6)
+            want = O.f32_to_bf16_bits(O.rope_rotate_half(n, c[t:t + 1], s[t:t + 1]))[0]
+            assert np.array_equal(out[t, a:a + D], want), (t, h)
+            assert r[t, h] == rr[0]
+
+
+def test_head_norm_leaves_other_columns():
+    T, D, H, col0, N = 4, 32, 2, 32, 128
+    y = _rand_bf16_rows(T, N, seed=42)
+    out, _ = O.head_rms_norm(y, col0, H, D, None, 1e-6)
+    assert np.array_equal(out[:, :col0], y[:, :col0])
+    assert np.array_equal(out[:, col0 + H * D:], y[:, col0 + H * D:])
+    assert not np.array_equal(out[:, col0:col0 + H * D], y[:, col0:col0 + H * D])
+
+
+def test_head_norm_heads_are_independent():
+    """eps = 0: scaling one head by 2^p changes no output bit; zeroing a head zeroes
+    that head only."""
+    T, D, H = 6, 64, 4
+    y = _rand_bf16_rows(T, H * D, seed=43)
+    out0, _ = O.head_rms_norm(y, 0, H, D, None, 0.0)
+    yf = O.bf16_bits_to_f32(y).copy()
+    yf[:, 2 * D:3 * D] *= np.float32(2.0 ** 5)
+    out1, _ = O.head_rms_norm(O.f32_to_bf16_bits(yf), 0, H, D, None, 0.0)
+    assert np.array_equal(out0, out1)
+    yz = y.copy()
+    yz[3, D:2 * D] = 0
+    out2, _ = O.head_rms_norm(yz, 0, H, D, None, 1e-6)
+    assert not O.bf16_bits_to_f32(out2[3, D:2 * D]).any()
+    mask = np.ones_like(y, dtype=bool)
+    mask[3, D:2 * D] = False
+    out3, _ = O.head_rms_norm(y, 0, H, D, None, 1e-6)
+    assert np.array_equal(out2[mask], out3[mask])
+
+
+def test_head_norm_constant_head_closed_form():
+    """A head of constant c normed with eps: every value is c / sqrt(c^2 + eps), times gamma."""
+    D = 32
+    c = 0.75
+    y = np.full((1, 2 * D), O.f32_to_bf16_bits(np.float32(c))[0], dtype=np.uint16)
+    g = O.f32_to_bf16_bits(np.full(D, 2.0, dtype=np.float32))
+    out, _ = O.head_rms_norm(y, 0, 2, D, g, 0.25)
+    want = 2.0 * c / np.sqrt(c * c + 0.25)  # 1.5 / sqrt(0.8125) = 1.664..., bf16 1.6640625
+    assert O.bf16_bits_to_f32(out).tolist() == [[float(O.bf16_bits_to_f32(O.f32_to_bf16_bits(np.float32(want)))[0])] * (2 * D)]
+
+
+def test_rope_identity_and_half_turn():
+    n = O.bf16_bits_to_f32(_rand_bf16_rows(3, 16, seed=44)).astype(np.float32)
+    one, zero = np.ones((3, 8), np.float32), np.zeros((3, 8), np.float32)
+    assert np.array_equal(O.rope_rotate_half(n, one, zero), n)
+    assert np.array_equal(O.rope_rotate_half(n, -one, zero), -n)
+
+
+def test_rope_quarter_turn_pairs_i_with_i_plus_half():
+    """cos = 0, sin = 1 maps (a_i, b_i) = (n[i], n[i + D/2]) to (-b_i, a_i): this fixes
+    both the pairing and the sign."""
+    n = np.arange(1, 17, dtype=np.float32).reshape(1, 16)
+    out = O.rope_rotate_half(n, np.zeros((1, 8), np.float32), np.ones((1, 8), np.float32))
+    assert out.tolist() == [[-9, -10, -11, -12, -13, -14, -15, -16, 1, 2, 3, 4, 5, 6, 7, 8]]
+
+
+def test_rope_is_a_rotation():
+    """Each pair keeps its length, and rotating by phi then by -phi returns the input,
+    within a few fp32 roundings."""
+    n = O.bf16_bits_to_f32(_rand_bf16_rows(8, 64, seed=45)).astype(np.float32)
+    c, s = _angles(8, 32, 46)
+    out = O.rope_rotate_half(n, c, s)
+    len_in = n[:, :32].astype(np.float64) ** 2 + n[:, 32:].astype(np.float64) ** 2
+    len_out = out[:, :32].astype(np.float64) ** 2 + out[:, 32:].astype(np.float64) ** 2
+    assert np.max(np.abs(len_out / len_in - 1.0)) < 4e-7
+    back = O.rope_rotate_half(out, c, -s)
+    assert np.max(np.abs(back - n)) <= 4e-7 * np.max(np.abs(n))
+    # two rotations add their angles
+    phi = np.random.default_rng(47).uniform(0, 2 * np.pi, size=(8, 32))
+    c1, s1 = np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
+    c2, s2 = np.cos(2 * phi).astype(np.float32), np.sin(2 * phi).astype(np.float32)
+    twice = O.rope_rotate_half(O.rope_rotate_half(n, c1, s1), c1, s1)
+    assert np.max(np.abs(twice - O.rope_rotate_half(n, c2, s2))) <= 2e-6 * np.max(np.abs(n))
+
+
+def test_preattn_split_and_gammas():
+    """V columns are the projection output; gamma_q acts on the query heads only and
+    gamma_k on the key heads only (gamma_k = 2 doubles the key heads exactly)."""
+    T, K, Hq, Hkv, D = 4, 64, 4, 2, 16
+    N = (Hq + 2 * Hkv) * D
+    case = synthetic.norm_linear_case(T, K, N, seed=48)
+    x, g, W = bits(case["x"]), bits(case["gamma"]), bits(case["W"])
+    ones = O.f32_to_bf16_bits(np.ones(D, np.float32))
+    twos = O.f32_to_bf16_bits(np.full(D, 2.0, np.float32))
+    a = O.preattn_qkv(x, None, g, 1e-6, W, Hq, Hkv, D, ones, ones, 1e-6)
+    b = O.preattn_qkv(x, None, g, 1e-6, W, Hq, Hkv, D, ones, twos, 1e-6)
+    q, k = slice(0, Hq * D), slice(Hq * D, (Hq + Hkv) * D)
+    v = slice((Hq + Hkv) * D, N)
+    assert np.array_equal(a["y"][:, v], a["y_proj"][:, v])
+    assert np.array_equal(a["y"][:, q], b["y"][:, q])
+    assert np.array_equal(O.bf16_bits_to_f32(b["y"][:, k]), 2 * O.bf16_bits_to_f32(a["y"][:, k]))
+    _, ybf, _ = O.rmsnorm_linear_bf16(x, g, 1e-6, W)
+    assert np.array_equal(a["y_proj"], ybf)
+    # a zero residual changes nothing
+    z = O.preattn_qkv(x, np.zeros_like(x), g, 1e-6, W, Hq, Hkv, D, ones, twos, 1e-6)
+    assert np.array_equal(z["y"], b["y"]) and np.array_equal(z["x_add"], x)
