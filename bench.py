@@ -45,6 +45,10 @@ WORKLOADS = {
                                   desc="residual add -> pre-attention norm -> fused QKV projection"),
     "preattn_qkv_add_T16": dict(kind="bf16", add=True, T=16, K=4096, N=6144, bound="hbm", dtype="bf16",
                                 desc="residual add -> pre-attention norm -> QKV, 16 decode tokens"),
+    "preattn_block_T4096": dict(kind="preattn", T=4096, K=4096, N=6144, Hq=32, Hkv=8, D=128, bound="mfma",
+                                dtype="bf16", desc="residual add -> norm -> fused QKV -> per-head norm of Q, K -> RoPE"),
+    "preattn_block_T16": dict(kind="preattn", T=16, K=4096, N=6144, Hq=32, Hkv=8, D=128, bound="hbm",
+                              dtype="bf16", desc="pre-attention block, 16 decode tokens"),
     "small_T8": dict(kind="bf16", T=8, K=256, N=128, bound="hbm", dtype="bf16",
                      desc="bf16 RMSNorm + Linear, T=8 K=256 N=128"),
     "int8_w8a8": dict(kind="int8", T=2048, K=4096, N=4096, bound="mfma", dtype="int8",
@@ -71,6 +75,9 @@ def flops_of(w):
 def bytes_of(w):
     """Algorithmic bytes: every input read once, every output written once."""
     T, K, N = w["T"], w["K"], w["N"]
+    if w["kind"] == "preattn":
+        # x, residual read, x_add written; gamma, W, both head gammas and the angle tables read; y written once
+        return T * K * 2 * 3 + K * 2 + N * K * 2 + 2 * w["D"] * 2 + 2 * T * (w["D"] // 2) * 4 + T * N * 2
     if w["kind"] == "bf16":
         # with the residual add: the residual is read and x_add written as well
         return T * K * 2 * (3 if w.get("add") else 1) + K * 2 + N * K * 2 + T * N * 2
@@ -124,6 +131,7 @@ class Setup:
             "fp32w": lambda: synthetic.norm_linear_case(w["T"], w["K"], w["N"], gamma=False, w_dtype="fp32", name=name),
             "int8": lambda: synthetic.int8_case(w["T"], w["K"], w["N"], name=name),
             "chain": lambda: synthetic.chain_case(w["T"], w["K"], w["R"], w["N"], name=name),
+            "preattn": lambda: synthetic.preattn_block(w["T"]),
         }[kind]()
         if w.get("add"):
             self.case = synthetic.with_residual(self.case)
@@ -134,7 +142,7 @@ class Setup:
         # rotate copies of the streamed operand when the path is bound by HBM
         self.copies = 1
         if w["bound"] == "hbm":
-            rot = "W" if kind == "bf16" else "x"
+            rot = "W" if kind in ("bf16", "preattn") else "x"
             nbytes = t[rot].numel() * t[rot].element_size()
             self.copies = max(1, math.ceil(640e6 / nbytes)) if nbytes > 1e6 else 1
             t[rot + "_copies"] = [t[rot]] + [t[rot].clone() for _ in range(self.copies - 1)]
@@ -157,6 +165,24 @@ class Setup:
             if T <= 16:
                 # weight streaming: the normed activations are re-read from L2,
                 # the weight (rotated) from HBM
+                self.kernel, self.kernel_key = "small_m_kernel", "small_m"
+                self.kern = lambda i: rnl.linear_bf16(a, Wc[i % len(Wc)], y=y)
+                self.kern_units = ("hbm", N * K * 2 + T * K * 2 + T * N * 2)
+            else:
+                self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
+                self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
+                self.kern_units = ("bf16", flops_of(w))
+        elif kind == "preattn":
+            Hq, Hkv, D = w["Hq"], w["Hkv"], w["D"]
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            xa = torch.empty_like(t["x"])
+            ws = torch.empty(max(1, rnl.workspace_bytes("preattn", T, K, Hq, Hkv, D)), dtype=torch.uint8, device=dev)
+            Wc = t.get("W_copies", [t["W"]])
+            self.step = lambda i: rnl.preattn_qkv_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], Hq, Hkv, D,
+                                                       t["gamma_q"], t["gamma_k"], eps, t["cos"], t["sin"],
+                                                       residual=t["residual"], x_add_out=xa, y=y, workspace=ws)
+            a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
+            if T <= 16:
                 self.kernel, self.kernel_key = "small_m_kernel", "small_m"
                 self.kern = lambda i: rnl.linear_bf16(a, Wc[i % len(Wc)], y=y)
                 self.kern_units = ("hbm", N * K * 2 + T * K * 2 + T * N * 2)
@@ -264,7 +290,11 @@ def cpu_baseline(setup, target_s=8.0):
     def run(rows):
         x = bits(c["x"][:rows])
         g = None if c["gamma"] is None else bits(c["gamma"])
-        if kind == "bf16" and w.get("add"):
+        if kind == "preattn":
+            O.preattn_qkv(x, bits(c["residual"][:rows]), g, c.eps, bits(c["W"]), w["Hq"], w["Hkv"], w["D"],
+                          bits(c["gamma_q"]), bits(c["gamma_k"]), c.eps, c["cos"][:rows].numpy(),
+                          c["sin"][:rows].numpy())
+        elif kind == "bf16" and w.get("add"):
             O.add_rmsnorm_linear_bf16(x, bits(c["residual"][:rows]), g, c.eps, bits(c["W"]))
         elif kind == "bf16":
             O.rmsnorm_linear_bf16(x, g, c.eps, bits(c["W"]))
@@ -339,7 +369,7 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
         "dtype": w["dtype"],
         "data": "synthetic",
         "config": {"workload": s.case.name, "description": w["desc"],
-                   **{k: w[k] for k in ("T", "K", "R", "N") if k in w},
+                   **{k: w[k] for k in ("T", "K", "R", "N", "Hq", "Hkv", "D") if k in w},
                    "parallelism": "none (1 GPU)", "input_copies": s.copies,
                    "timing": "hip graph of the timed steps" if graph else "eager launches"},
         "roofline": {"bound": bound, "kernel": s.kernel, "achieved": round(achieved, 3), "peak": PEAK[peak_key],
@@ -397,7 +427,8 @@ def record_counters(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Fold two rocprofv3 --pmc runs of a workload (FETCH_SIZE, then WRITE_SIZE)
     and the same two counters of the calibration copy into profiles/counters.json."""
     w = WORKLOADS[name]
-    key = "skinny" if w["kind"] == "fp32w" else ("small_m" if w["kind"] == "bf16" and w["T"] <= 16 else "gemm")
+    key = "skinny" if w["kind"] == "fp32w" else ("small_m" if w["kind"] in ("bf16", "preattn") and w["T"] <= 16
+                                                 else "gemm")
     pair = key == "skinny"
     fk, nf = _counter_kib(fetch_csv, KERNEL_MATCH[key], "FETCH_SIZE", pair)
     wk, nw = _counter_kib(write_csv, KERNEL_MATCH[key], "WRITE_SIZE", pair)

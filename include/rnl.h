@@ -194,6 +194,48 @@ RNL_API int norm_proj_chain(const void* x, const void* W_a, const void* gamma, f
 RNL_API size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N);
 
 /*
+ * preattn_qkv_bf16 -- the pre-attention block around the fused norm and
+ * projection: optional residual add, input RMSNorm, fused QKV projection,
+ * split into heads, per-head RMSNorm of the query and key heads, optional
+ * rotary embedding of both.
+ *
+ * AT-10 page, section 6: in the non-quantised Qwen3 pre-attention the norm of
+ * x_add is followed by the bf16 product with the fused QKV weight, whose output
+ * is split into Q, K and V, and Q and K get a per-head norm and RoPE.  The
+ * steps, in order:
+ *   x_add = round_bf16(float(x) + float(residual))   (only with a residual)
+ *   p     = rmsnorm_linear_bf16(x_add or x, gamma, eps, W)       [T, N] bf16
+ *   heads: columns [0, Hq D) are Hq query heads, [Hq D, (Hq+Hkv) D) Hkv key
+ *          heads, the last Hkv D columns value heads, D columns each;
+ *   each query / key head: n = fl(fl(float(p) * rstd_h) * gamma_q / gamma_k)
+ *          with rstd_h the AT-03 rstd of its D values (head_eps);
+ *   RoPE (cos, sin given): element i < D/2 of a head and element i + D/2 are
+ *          rotated together by the angle of (t, i):
+ *          out[i]       = fl(fl(n[i] c) - fl(n[i+D/2] s)),
+ *          out[i + D/2] = fl(fl(n[i+D/2] c) + fl(n[i] s)),  c, s = cos[t,i], sin[t,i];
+ *   y     = round_bf16 of that; value heads are p unchanged.
+ *
+ *   x, residual, x_add_out, gamma, eps, rstd_out  as in add_rmsnorm_linear_bf16
+ *             (residual and x_add_out together, or both NULL for no add).
+ *   W         [(Hq + 2 Hkv) D, K] bf16 fused QKV weight (b_trans).
+ *   y         [T, (Hq + 2 Hkv) D] bf16 output, columns Q | K | V.
+ *   gamma_q, gamma_k  [D] bf16 head-norm scales, or NULL; head_eps.
+ *   cos, sin  [T, D/2] fp32 rotation tables, both or neither (no RoPE).
+ *   head_rstd_out [T, Hq + Hkv] fp32 rstd of every normed head, or NULL.
+ *   D must be a multiple of 16 and at most 512.
+ *
+ * Errors: as rmsnorm_linear_bf16; RNL_ERR_NULL also when only one of
+ * residual / x_add_out or of cos / sin is given; RNL_ERR_SHAPE for D.
+ */
+RNL_API int preattn_qkv_bf16(const void* x, const void* residual, void* x_add_out, const void* gamma, float eps,
+                             const void* W, void* y, float* rstd_out, const void* gamma_q, const void* gamma_k,
+                             float head_eps, const float* cos, const float* sin, float* head_rstd_out, int64_t T,
+                             int64_t K, int64_t Hq, int64_t Hkv, int64_t D, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+RNL_API size_t preattn_qkv_bf16_workspace_bytes(int64_t T, int64_t K, int64_t Hq, int64_t Hkv, int64_t D);
+
+/*
  * The atoms the fused entry points are built from.  They run the same kernels
  * and follow the same conventions (device pointers, asynchronous on `stream`,
  * validation before any HIP call, status codes); none needs a workspace.
@@ -215,6 +257,21 @@ RNL_API int rms_norm_bf16(const void* x, const void* gamma, float eps, void* y, 
 RNL_API int rms_norm_quant_int8(const void* x, const void* gamma, float eps, int8_t* xq,
                                 float* x_scale, float* rstd_out, int64_t T, int64_t K,
                                 void* stream);
+
+/*
+ * head_rms_norm_bf16 -- the per-head stage alone (AT-10 page section 6; the
+ * section 9 golden chain re-norms the q_b output per head the same way):
+ * the H heads of D columns starting at column col0 of every row of
+ * y_in [T, ld] are normed (gamma [D] or NULL, eps) and, with cos/sin
+ * [T, D/2] fp32, rotated as in preattn_qkv_bf16; the results go to the same
+ * places of y_out, the other columns of y_out are not written.  y_out may be
+ * y_in (in place) but may not overlap it otherwise (RNL_ERR_ARG).
+ * rstd_out [T, H] or NULL.  ld and col0 multiples of 8; D a multiple of 16,
+ * at most 512; col0 + H D <= ld.
+ */
+RNL_API int head_rms_norm_bf16(const void* y_in, void* y_out, const void* gamma, float eps, const float* cos,
+                               const float* sin, float* rstd_out, int64_t T, int64_t ld, int64_t col0, int64_t H,
+                               int64_t D, void* stream);
 
 /*
  * linear_bf16 -- AT-09 Linear Projection, BF16 mode (AT-10 page section 4):

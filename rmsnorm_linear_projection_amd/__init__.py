@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   dequant;
 * :func:`add_rmsnorm_linear_bf16`, :func:`add_rmsnorm_linear_int8` -- the same
   with the residual add in front (x_add = x + residual, also returned);
+* :func:`preattn_qkv_bf16` -- (residual add ->) RMSNorm -> fused QKV projection ->
+  per-head RMSNorm of the query and key heads (-> RoPE);
 * :func:`norm_proj_chain` -- q_a = x W_a^T -> RMSNorm -> qr -> y = qr W_b^T.
 """
 from __future__ import annotations
@@ -29,6 +31,8 @@ __all__ = [
     "add_rmsnorm_linear_bf16",
     "add_rmsnorm_linear_int8",
     "norm_proj_chain",
+    "preattn_qkv_bf16",
+    "head_rms_norm_bf16",
     "rms_norm_bf16",
     "rms_norm_quant_int8",
     "linear_bf16",
@@ -101,6 +105,15 @@ def load_library() -> ctypes.CDLL:
     lib.add_rmsnorm_linear_int8.restype = ctypes.c_int
     lib.add_rmsnorm_linear_int8_workspace_bytes.argtypes = lib.rmsnorm_linear_int8_workspace_bytes.argtypes
     lib.add_rmsnorm_linear_int8_workspace_bytes.restype = ctypes.c_size_t
+    lib.preattn_qkv_bf16.argtypes = [_c_p, _c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                     ctypes.c_float, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                     _c_p, ctypes.c_size_t, _c_p]
+    lib.preattn_qkv_bf16.restype = ctypes.c_int
+    lib.preattn_qkv_bf16_workspace_bytes.argtypes = [_c_i64] * 5
+    lib.preattn_qkv_bf16_workspace_bytes.restype = ctypes.c_size_t
+    lib.head_rms_norm_bf16.argtypes = [_c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                       _c_i64, _c_i64, _c_p]
+    lib.head_rms_norm_bf16.restype = ctypes.c_int
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -151,7 +164,8 @@ def _workspace(nbytes: int, dev, given):
 
 
 def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.bfloat16) -> int:
-    """Workspace a call needs: kind 'bf16', 'int8', 'add_bf16', 'add_int8' (T, K, N) or 'chain' (T, K, R, N)."""
+    """Workspace a call needs: kind 'bf16', 'int8', 'add_bf16', 'add_int8' (T, K, N), 'chain' (T, K, R, N)
+    or 'preattn' (T, K, Hq, Hkv, D)."""
     lib = load_library()
     if kind == "bf16":
         return int(lib.rmsnorm_linear_bf16_workspace_bytes(*shape, _DTYPE_CODE[w_dtype], _DTYPE_CODE[out_dtype]))
@@ -163,6 +177,8 @@ def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.b
         return int(lib.add_rmsnorm_linear_int8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
     if kind == "chain":
         return int(lib.norm_proj_chain_workspace_bytes(*shape))
+    if kind == "preattn":
+        return int(lib.preattn_qkv_bf16_workspace_bytes(*shape))
     raise ValueError(kind)
 
 
@@ -316,6 +332,77 @@ def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None,
                                  _ptr(rstd_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
     _check(rc)
     return y, qr_out
+
+
+def _rope_tables(cos, sin, T, D):
+    _dev_tensor(cos, "cos", torch.float32, 2)
+    _dev_tensor(sin, "sin", torch.float32, 2)
+    _shape((cos is None) == (sin is None), "cos and sin go together")
+    _shape(cos is None or (tuple(cos.shape) == (T, D // 2) and tuple(sin.shape) == (T, D // 2)),
+           "cos and sin must be [T, D/2]")
+
+
+def preattn_qkv_bf16(x, gamma, eps, W, Hq, Hkv, D, gamma_q=None, gamma_k=None, head_eps=1e-6, cos=None, sin=None,
+                     residual=None, x_add_out=None, y=None, rstd_out=None, head_rstd_out=None, workspace=None):
+    """Pre-attention block (AT-10 page section 6): optional residual add, RMSNorm,
+    fused QKV projection with W [(Hq + 2 Hkv) D, K], per-head RMSNorm of the query
+    (gamma_q) and key (gamma_k) heads, RoPE with cos/sin [T, D/2] when given.
+    Returns (y [T, (Hq + 2 Hkv) D] with columns Q | K | V, x_add_out or None)."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(W, "W", torch.bfloat16, 2)
+    _dev_tensor(gamma_q, "gamma_q", torch.bfloat16, 1)
+    _dev_tensor(gamma_k, "gamma_k", torch.bfloat16, 1)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    _dev_tensor(head_rstd_out, "head_rstd_out", torch.float32)
+    T, K = x.shape
+    N = (Hq + 2 * Hkv) * D
+    _shape(tuple(W.shape) == (N, K), "W must be [(Hq + 2 Hkv) D, K]")
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(gamma_q is None or gamma_q.numel() == D, "gamma_q must be [D]")
+    _shape(gamma_k is None or gamma_k.numel() == D, "gamma_k must be [D]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    _shape(head_rstd_out is None or head_rstd_out.numel() >= T * (Hq + Hkv), "head_rstd_out must be [T, Hq + Hkv]")
+    _rope_tables(cos, sin, T, D)
+    if residual is not None:
+        x_add_out = _residual(x, residual, x_add_out)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _dev_tensor(y, "y", torch.bfloat16)
+    _shape(tuple(y.shape) == (T, N), "y must be [T, (Hq + 2 Hkv) D]")
+    with torch.cuda.device(x.device):
+        need = int(lib.preattn_qkv_bf16_workspace_bytes(T, K, Hq, Hkv, D))
+        ws, ws_bytes = _workspace(need, x.device, workspace)
+        rc = lib.preattn_qkv_bf16(_ptr(x), _ptr(residual), _ptr(x_add_out if residual is not None else None),
+                                  _ptr(gamma), float(eps), _ptr(W), _ptr(y), _ptr(rstd_out), _ptr(gamma_q),
+                                  _ptr(gamma_k), float(head_eps), _ptr(cos), _ptr(sin), _ptr(head_rstd_out), T, K,
+                                  Hq, Hkv, D, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(rc)
+    return y, (x_add_out if residual is not None else None)
+
+
+def head_rms_norm_bf16(y, col0, H, D, gamma=None, eps=1e-6, cos=None, sin=None, out=None, rstd_out=None):
+    """Per-head RMSNorm (+ RoPE with cos/sin [T, D/2]) of the H heads of D columns
+    from column col0 of y [T, ld].  Writes into ``out`` (same shape as y), or into
+    y itself when ``out`` is None; returns the tensor written."""
+    lib = load_library()
+    _dev_tensor(y, "y", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, ld = y.shape
+    _shape(gamma is None or gamma.numel() == D, "gamma must be [D]")
+    _shape(rstd_out is None or rstd_out.numel() >= T * H, "rstd_out must be [T, H]")
+    _rope_tables(cos, sin, T, D)
+    if out is None:
+        out = y
+    _dev_tensor(out, "out", torch.bfloat16, 2)
+    _shape(tuple(out.shape) == (T, ld), "out must have the shape of y")
+    with torch.cuda.device(y.device):
+        rc = lib.head_rms_norm_bf16(_ptr(y), _ptr(out), _ptr(gamma), float(eps), _ptr(cos), _ptr(sin),
+                                    _ptr(rstd_out), T, ld, col0, H, D, _stream(y.device))
+    _check(rc)
+    return out
 
 
 def rms_norm_bf16(x, gamma, eps, y=None, rstd_out=None):

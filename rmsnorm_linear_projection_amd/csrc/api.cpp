@@ -207,6 +207,22 @@ int int8_path(const void* x, const void* residual, void* x_add, const void* gamm
   return hip_status(rnl::launch_gemm_int8(q, Wq, y, kind, xs, w_scale, T, N, K, s), "int8 GEMM launch");
 }
 
+constexpr int64_t kMaxHeadDim = 512;  // a head fits one wavefront (64 lanes x 8 values)
+
+int check_head_dim(int64_t D) {
+  if (D < 16 || D > kMaxHeadDim || D % 16 != 0)
+    return fail(RNL_ERR_SHAPE, "head size D=%lld must be a multiple of 16 in [16, 512]", (long long)D);
+  return RNL_OK;
+}
+
+// y_out either is y_in (in place) or shares no byte with rows [0, T) of it
+bool partial_overlap(const void* a, const void* b, int64_t T, int64_t ld) {
+  if (a == b) return false;
+  const uintptr_t n = (uintptr_t)T * (uintptr_t)ld * 2u;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + n && pb < pa + n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -334,6 +350,67 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
   return hip_status(project_bf16(static_cast<const uint16_t*>(qr_out), static_cast<const uint16_t*>(W_b), y,
                                  rnl::OUT_BF16, T, N, R, s),
                     "chain stage-2 projection launch");
+}
+
+size_t preattn_qkv_bf16_workspace_bytes(int64_t T, int64_t K, int64_t Hq, int64_t Hkv, int64_t D) {
+  if (T <= 0 || K <= 0 || Hq <= 0 || Hkv < 0 || D <= 0) return 0;
+  return bf16_ws(T, K, (Hq + 2 * Hkv) * D, RNL_BF16);
+}
+
+int preattn_qkv_bf16(const void* x, const void* residual, void* x_add_out, const void* gamma, float eps,
+                     const void* W, void* y, float* rstd_out, const void* gamma_q, const void* gamma_k,
+                     float head_eps, const float* cos_t, const float* sin_t, float* head_rstd_out, int64_t T,
+                     int64_t K, int64_t Hq, int64_t Hkv, int64_t D, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if ((residual == nullptr) != (x_add_out == nullptr))
+    return fail(RNL_ERR_NULL, "residual and x_add_out are given together or not at all");
+  if ((cos_t == nullptr) != (sin_t == nullptr)) return fail(RNL_ERR_NULL, "cos and sin are given together or not at all");
+  if (T <= 0 || K <= 0 || Hq <= 0 || Hkv < 0)
+    return fail(RNL_ERR_SHAPE, "need T, K, Hq >= 1 and Hkv >= 0 (T=%lld K=%lld Hq=%lld Hkv=%lld)", (long long)T,
+                (long long)K, (long long)Hq, (long long)Hkv);
+  RNL_TRY(check_head_dim(D));
+  if (Hq + 2 * Hkv > kMaxDim / D) return fail(RNL_ERR_SHAPE, "(Hq + 2 Hkv) * D must be <= 2^24");
+  RNL_TRY(check_eps(head_eps));
+  RNL_ALIGN(gamma_q, 16, "gamma_q");
+  RNL_ALIGN(gamma_k, 16, "gamma_k");
+  RNL_ALIGN(cos_t, 16, "cos");
+  RNL_ALIGN(sin_t, 16, "sin");
+  RNL_ALIGN(head_rstd_out, 4, "head_rstd_out");
+  const int64_t N = (Hq + 2 * Hkv) * D;
+  RNL_TRY(bf16_path(x, residual, x_add_out, gamma, eps, W, RNL_BF16, y, RNL_BF16, rstd_out, T, K, N, workspace,
+                    workspace_bytes, stream));
+  uint16_t* yb = static_cast<uint16_t*>(y);
+  return hip_status(rnl::launch_head_norm_bf16(yb, yb, T, N, 0, Hq + Hkv, D, Hq,
+                                               static_cast<const uint16_t*>(gamma_q),
+                                               static_cast<const uint16_t*>(gamma_k), head_eps, cos_t, sin_t,
+                                               head_rstd_out, static_cast<hipStream_t>(stream)),
+                    "per-head norm launch");
+}
+
+int head_rms_norm_bf16(const void* y_in, void* y_out, const void* gamma, float eps, const float* cos_t,
+                       const float* sin_t, float* rstd_out, int64_t T, int64_t ld, int64_t col0, int64_t H,
+                       int64_t D, void* stream) {
+  if (y_in == nullptr || y_out == nullptr) return fail(RNL_ERR_NULL, "y_in and y_out are required");
+  if ((cos_t == nullptr) != (sin_t == nullptr)) return fail(RNL_ERR_NULL, "cos and sin are given together or not at all");
+  if (T <= 0 || H <= 0 || col0 < 0 || ld <= 0)
+    return fail(RNL_ERR_SHAPE, "need T, H, ld >= 1 and col0 >= 0");
+  RNL_TRY(check_head_dim(D));
+  if (T > kMaxDim || ld > kMaxDim) return fail(RNL_ERR_SHAPE, "T and ld must be <= 2^24");
+  if (ld % 8 != 0 || col0 % 8 != 0) return fail(RNL_ERR_SHAPE, "ld and col0 must be multiples of 8");
+  if (H > (ld - col0) / D) return fail(RNL_ERR_SHAPE, "col0 + H * D exceeds the row length ld");
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(y_in, 16, "y_in");
+  RNL_ALIGN(y_out, 16, "y_out");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(cos_t, 16, "cos");
+  RNL_ALIGN(sin_t, 16, "sin");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  if (partial_overlap(y_in, y_out, T, ld)) return fail(RNL_ERR_ARG, "y_out overlaps y_in without being y_in");
+  const uint16_t* gb = static_cast<const uint16_t*>(gamma);
+  return hip_status(rnl::launch_head_norm_bf16(static_cast<const uint16_t*>(y_in), static_cast<uint16_t*>(y_out),
+                                               T, ld, col0, H, D, H, gb, gb, eps, cos_t, sin_t, rstd_out,
+                                               static_cast<hipStream_t>(stream)),
+                    "per-head norm launch");
 }
 
 int rms_norm_bf16(const void* x, const void* gamma, float eps, void* y, float* rstd_out, int64_t T,

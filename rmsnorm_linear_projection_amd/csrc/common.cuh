@@ -54,11 +54,15 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // rstd = 1 / sqrt(fl(fl(S * inv_k) + eps)) with IEEE-rounded multiply, add,
 // square root and division (sqrtf and '/' are correctly rounded under the
-// default HIP floating-point options; __fsqrt_rn is not).
+// default HIP floating-point options; __fsqrt_rn is not).  The operators are
+// written out under contract(off): under the default options __fmul_rn and
+// __fadd_rn are plain '*' and '+' from a header where contraction into an FMA
+// (one rounding instead of two) stays allowed.
 __device__ __forceinline__ float rstd_from_sumsq(float S, float inv_k, float eps) {
-  float ms = __fmul_rn(S, inv_k);
-  float var = __fadd_rn(ms, eps);
-  return __fdiv_rn(1.0f, sqrtf(var));
+#pragma clang fp contract(off)
+  const float ms = S * inv_k;
+  const float var = ms + eps;
+  return 1.0f / sqrtf(var);
 }
 
 }  // namespace rnl

@@ -35,6 +35,16 @@ hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t
 hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,
                                    int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s);
 
+// Per-head RMSNorm (+ rotate-half RoPE when cos_t/sin_t are given) of the H
+// heads of D columns that start at column col0 of y_in[T, ld] (bf16), written
+// to the same places of y_out (which may be y_in).  Heads h < H1 take gamma1,
+// the rest gamma2 (either may be null); cos_t/sin_t are [T, D/2] fp32;
+// rstd_out [T, H] may be null.  D is a multiple of 16, at most 512.
+hipError_t launch_head_norm_bf16(const uint16_t* y_in, uint16_t* y_out, int64_t T, int64_t ld, int64_t col0,
+                                 int64_t H, int64_t D, int64_t H1, const uint16_t* gamma1, const uint16_t* gamma2,
+                                 float eps, const float* cos_t, const float* sin_t, float* rstd_out,
+                                 hipStream_t s);
+
 // C[M,N] = A[M,K] . B[N,K]^T on bf16 MFMA, fp32 accumulation, C bf16 or fp32.
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);

@@ -18,8 +18,8 @@
 // partials are added in split order, so the result does not depend on timing.
 #include <algorithm>
 
-#include "common.cuh"
 #include "launch.h"
+#include "rows.cuh"
 
 namespace rnl {
 namespace {
@@ -44,34 +44,6 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   return r;
-}
-
-__device__ __forceinline__ float sumsq8(u32x4 w) {
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float a = bf16lo(w[j]), b = bf16hi(w[j]);
-    s += a * a;
-    s += b * b;
-  }
-  return s;
-}
-
-// normed values of one 8-element chunk: n = fl(fl(xf * rstd) * g)
-__device__ __forceinline__ void normed8(u32x4 w, const u32x4* gr, int idx, float rstd, float n[8]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    n[2 * j] = __fmul_rn(bf16lo(w[j]), rstd);
-    n[2 * j + 1] = __fmul_rn(bf16hi(w[j]), rstd);
-  }
-  if (gr != nullptr) {
-    u32x4 g = gr[idx];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      n[2 * j] = __fmul_rn(n[2 * j], bf16lo(g[j]));
-      n[2 * j + 1] = __fmul_rn(n[2 * j + 1], bf16hi(g[j]));
-    }
-  }
 }
 
 __device__ __forceinline__ uint32_t q4(const float n[8], int base, float s) {

@@ -28,6 +28,7 @@ EPS = 1e-6
 
 # stream ids: one per tensor role, so that adding a tensor never shifts another
 _S_X, _S_GAMMA, _S_W, _S_WSCALE, _S_WA, _S_WB, _S_RES = 1, 2, 3, 4, 5, 6, 7
+_S_GQ, _S_GK, _S_ANGLE = 8, 9, 10
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -101,6 +102,31 @@ def with_residual(case: Case, seed: int = 0, std: float = 2.0) -> Case:
     return Case(case.name.replace("_T", "_add_T", 1), t, case.eps, dict(case.dims))
 
 
+def rope_tables(T: int, half: int, seed: int = 0):
+    """cos and sin [T, half] fp32 of angles drawn uniformly in [0, 2 pi): the
+    rotation tables a caller hands to the rotary embedding (random angles stand
+    in for positions times frequencies)."""
+    phi = uniform((T, half), 0.0, 2.0 * math.pi, seed, _S_ANGLE, dtype=torch.float32)
+    return torch.cos(phi).contiguous(), torch.sin(phi).contiguous()
+
+
+def preattn_case(T: int, K: int, Hq: int, Hkv: int, D: int, seed: int = 0, residual: bool = False,
+                 rope: bool = True, head_gamma: bool = True, name: str | None = None) -> Case:
+    """Pre-attention block: x[T,K] bf16, gamma[K], fused QKV weight W[(Hq+2Hkv)D, K],
+    head-norm scales gamma_q, gamma_k [D] ~ U(0.5, 1.5), optional residual, and
+    rotation tables cos/sin [T, D/2]."""
+    N = (Hq + 2 * Hkv) * D
+    case = norm_linear_case(T, K, N, seed, name=name or f"preattn_T{T}_K{K}_Hq{Hq}_Hkv{Hkv}_D{D}")
+    t = case.tensors
+    t["gamma_q"] = uniform((D,), 0.5, 1.5, seed, _S_GQ) if head_gamma else None
+    t["gamma_k"] = uniform((D,), 0.5, 1.5, seed, _S_GK) if head_gamma else None
+    t["cos"], t["sin"] = rope_tables(T, D // 2, seed) if rope else (None, None)
+    case.dims.update({"Hq": Hq, "Hkv": Hkv, "D": D})
+    if residual:
+        t["residual"] = normal((T, K), 2.0, seed, _S_RES)
+    return case
+
+
 def chain_case(T: int, K: int, R: int, N: int, seed: int = 0, gamma: bool = True,
                name: str | None = None) -> Case:
     """x[T,K] -> W_a[R,K] -> RMSNorm(R, gamma) -> W_b[N,R]; all bf16."""
@@ -127,6 +153,12 @@ def preattn_qkv(T: int = 4096, seed: int = 0) -> Case:
 def preattn_qkv_add(T: int = 4096, seed: int = 0) -> Case:
     """Residual add -> pre-attention norm -> fused QKV projection, K=4096, N=6144."""
     return with_residual(preattn_qkv(T, seed), seed)
+
+
+def preattn_block(T: int = 4096, seed: int = 0) -> Case:
+    """Residual add -> norm -> fused QKV (32 query heads, 8 key/value heads of 128)
+    -> per-head norm of Q and K -> RoPE; K = 4096, N = 6144."""
+    return preattn_case(T, 4096, 32, 8, 128, seed, residual=True, name=f"preattn_block_T{T}_K4096_Hq32_Hkv8_D128")
 
 
 def int8_w8a8(seed: int = 0) -> Case:

@@ -183,6 +183,62 @@ def test_add_int8_validation(lib, kw, code):
     assert add_int8_call(lib, **kw) == E[code]
 
 
+def preattn_call(lib, x=FAKE, r=NULL, xa=NULL, g=NULL, eps=1e-6, W=FAKE, y=FAKE, rstd=NULL, gq=NULL, gk=NULL,
+                 heps=1e-6, cos=NULL, sin=NULL, hrstd=NULL, T=4, K=64, Hq=4, Hkv=2, D=128, ws=FAKE, wsb=1 << 30):
+    return lib.preattn_qkv_bf16(x, r, xa, g, eps, W, y, rstd, gq, gk, heps, cos, sin, hrstd, T, K, Hq, Hkv, D, ws,
+                                wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(r=ctypes.c_void_p(0x20000)), "RNL_ERR_NULL"),   # residual without x_add_out
+    (dict(xa=ctypes.c_void_p(0x30000)), "RNL_ERR_NULL"),  # x_add_out without residual
+    (dict(cos=ctypes.c_void_p(0x40000)), "RNL_ERR_NULL"),  # cos without sin
+    (dict(W=NULL), "RNL_ERR_NULL"),
+    (dict(D=24), "RNL_ERR_SHAPE"),
+    (dict(D=528), "RNL_ERR_SHAPE"),
+    (dict(D=8), "RNL_ERR_SHAPE"),
+    (dict(Hq=0), "RNL_ERR_SHAPE"),
+    (dict(Hkv=-1), "RNL_ERR_SHAPE"),
+    (dict(Hq=1 << 20), "RNL_ERR_SHAPE"),
+    (dict(heps=-1.0), "RNL_ERR_ARG"),
+    (dict(gq=ODD), "RNL_ERR_ALIGN"),
+    (dict(cos=ctypes.c_void_p(0x40004), sin=ctypes.c_void_p(0x50000)), "RNL_ERR_ALIGN"),
+    (dict(T=64, ws=NULL), "RNL_ERR_WORKSPACE"),
+])
+def test_preattn_validation(lib, kw, code):
+    assert preattn_call(lib, **kw) == E[code]
+
+
+def test_preattn_workspace_is_the_projection_workspace(lib):
+    assert lib.preattn_qkv_bf16_workspace_bytes(4096, 4096, 32, 8, 128) == \
+        lib.rmsnorm_linear_bf16_workspace_bytes(4096, 4096, 6144, 1, 1)
+    assert lib.preattn_qkv_bf16_workspace_bytes(0, 4096, 32, 8, 128) == 0
+
+
+def head_call(lib, yi=FAKE, yo=FAKE, g=NULL, eps=1e-6, cos=NULL, sin=NULL, rstd=NULL, T=4, ld=512, col0=0, H=4,
+              D=128):
+    return lib.head_rms_norm_bf16(yi, yo, g, eps, cos, sin, rstd, T, ld, col0, H, D, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(yi=NULL), "RNL_ERR_NULL"),
+    (dict(yo=NULL), "RNL_ERR_NULL"),
+    (dict(sin=ctypes.c_void_p(0x40000)), "RNL_ERR_NULL"),
+    (dict(H=5), "RNL_ERR_SHAPE"),            # col0 + H * D > ld
+    (dict(col0=8), "RNL_ERR_SHAPE"),
+    (dict(col0=4, H=1), "RNL_ERR_SHAPE"),    # col0 not a multiple of 8
+    (dict(ld=516, H=1), "RNL_ERR_SHAPE"),    # ld not a multiple of 8
+    (dict(D=40, H=1), "RNL_ERR_SHAPE"),      # D not a multiple of 16
+    (dict(T=0), "RNL_ERR_SHAPE"),
+    (dict(eps=float("nan")), "RNL_ERR_ARG"),
+    (dict(yo=ctypes.c_void_p(0x10000 + 1024)), "RNL_ERR_ARG"),  # overlaps y_in without being it
+    (dict(g=ODD), "RNL_ERR_ALIGN"),
+    (dict(rstd=ctypes.c_void_p(0x10002)), "RNL_ERR_ALIGN"),
+])
+def test_head_norm_validation(lib, kw, code):
+    assert head_call(lib, **kw) == E[code]
+
+
 def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, T=4, K=64, R=32,
                N=8, ws=FAKE, wsb=1 << 30):
     return lib.norm_proj_chain(x, Wa, g, eps, Wb, qr, y, rstd, T, K, R, N, ws, wsb, NULL)

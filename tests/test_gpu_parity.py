@@ -572,3 +572,126 @@ def test_add_int8_w8a8_full_size():
     """Residual add, then INT8 W8A8 norm + linear, T=2048, K=4096, N=4096, at full size."""
     case = synthetic.with_residual(synthetic.int8_w8a8())
     check_add_int8_case(case, rows=sample_rows(2048, 32))
+
+
+# ---------------------------------------------------------------------------
+# per-head stage after the projection: per-head RMSNorm (+ RoPE).  The heads
+# are bit-exact against the oracle given the device's head rstd; the rstd is
+# within 8 ulps of the oracle's own.
+# ---------------------------------------------------------------------------
+def _np(t):
+    return None if t is None else t.numpy()
+
+
+@pytest.mark.parametrize("T,ld,col0,H,D", [
+    (5, 64, 0, 4, 16),
+    (7, 256, 64, 3, 64),
+    (33, 6144, 0, 40, 128),    # query and key heads of the pre-attention layout
+    (3, 24576, 0, 128, 192),   # 24 lanes per head, padded to 32
+    (2, 1536, 512, 2, 512),    # one head per wavefront
+    (1, 136, 8, 1, 128),
+])
+@pytest.mark.parametrize("gamma,rope,inplace", [(True, True, True), (False, True, False), (True, False, False),
+                                                (False, False, True)])
+def test_head_norm_atom(T, ld, col0, H, D, gamma, rope, inplace):
+    seed = T + H + D
+    y = synthetic.normal((T, ld), 2.0, seed, 1)
+    g = synthetic.uniform((D,), 0.5, 1.5, seed, 2) if gamma else None
+    c, s = synthetic.rope_tables(T, D // 2, seed) if rope else (None, None)
+    yd = y.cuda()
+    rstd = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    if inplace:
+        out = rnl.head_rms_norm_bf16(yd, col0, H, D, dev(g), EPS, dev(c), dev(s), rstd_out=rstd)
+    else:
+        out = torch.full_like(yd, 7.0)
+        rnl.head_rms_norm_bf16(yd, col0, H, D, dev(g), EPS, dev(c), dev(s), out=out, rstd_out=rstd)
+    torch.cuda.synchronize()
+    r = rstd.cpu().numpy()
+    yb, gb = bits(y), (None if g is None else bits(g))
+    _, r_own = O.head_rms_norm(yb, col0, H, D, gb, EPS, _np(c), _np(s))
+    assert_rstd(r, r_own, f"heads T{T} D{D}")
+    ref, _ = O.head_rms_norm(yb, col0, H, D, gb, EPS, _np(c), _np(s), rstd=r)
+    ob = bits(out.cpu())
+    heads = slice(col0, col0 + H * D)
+    bad = ob[:, heads] != ref[:, heads]
+    assert not bad.any(), f"{int(bad.sum())} head values differ"
+    outside = np.ones(ld, dtype=bool)
+    outside[heads] = False
+    if inplace:
+        assert np.array_equal(ob[:, outside], yb[:, outside])
+    else:
+        assert (f32(out)[:, outside] == 7.0).all(), "columns outside the heads were written"
+
+
+def run_preattn(case, rows=None):
+    t = {k: dev(v) for k, v in case.tensors.items()}
+    d = case.dims
+    T, Hq, Hkv, D = d["T"], d["Hq"], d["Hkv"], d["D"]
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    hr = torch.empty((T, Hq + Hkv), dtype=torch.float32, device="cuda")
+    y, xa = rnl.preattn_qkv_bf16(t["x"], t["gamma"], EPS, t["W"], Hq, Hkv, D, t["gamma_q"], t["gamma_k"], EPS,
+                                 t["cos"], t["sin"], residual=t.get("residual"), rstd_out=rstd, head_rstd_out=hr)
+    # the projection alone, through the same kernels, on what the norm read
+    p = rnl.rmsnorm_linear_bf16(xa if xa is not None else t["x"], t["gamma"], EPS, t["W"])
+    torch.cuda.synchronize()
+    return y.cpu(), (None if xa is None else xa.cpu()), p.cpu(), rstd.cpu().numpy(), hr.cpu().numpy()
+
+
+def check_preattn_case(case, rows=None):
+    y, xa, p, rstd, hr = run_preattn(case)
+    d = case.dims
+    T, Hq, Hkv, D = d["T"], d["Hq"], d["Hkv"], d["D"]
+    rows = np.arange(T) if rows is None else rows
+    qk = slice(0, (Hq + Hkv) * D)
+    v = slice((Hq + Hkv) * D, (Hq + 2 * Hkv) * D)
+    c = None if case["cos"] is None else case["cos"].numpy()[rows]
+    s = None if case["sin"] is None else case["sin"].numpy()[rows]
+    gq = None if case["gamma_q"] is None else bits(case["gamma_q"])
+    gk = None if case["gamma_k"] is None else bits(case["gamma_k"])
+    yb, pb = bits(y)[rows], bits(p)[rows]
+    # value heads are the projection; query / key heads the head stage of it, bit for bit
+    assert np.array_equal(yb[:, v], pb[:, v]), f"{case.name}: value heads differ from the projection"
+    hq, _ = O.head_rms_norm(pb, 0, Hq, D, gq, EPS, c, s, rstd=hr[rows, :Hq])
+    hk, _ = O.head_rms_norm(hq, Hq * D, Hkv, D, gk, EPS, c, s, rstd=hr[rows, Hq:])
+    assert np.array_equal(yb[:, qk], hk[:, qk]), f"{case.name}: {int((yb[:, qk] != hk[:, qk]).sum())} head values differ"
+    _, hq_own = O.head_rms_norm(pb, 0, Hq, D, gq, EPS)
+    _, hk_own = O.head_rms_norm(pb, Hq * D, Hkv, D, gk, EPS)
+    assert_rstd(hr[rows], np.concatenate([hq_own, hk_own], axis=1), case.name)
+    # end to end against the oracle's own projection (device input rstd)
+    xb = bits(case["x"])[rows]
+    rb = None if "residual" not in case.tensors else bits(case["residual"])[rows]
+    ref = O.preattn_qkv(xb, rb, bits(case["gamma"]), EPS, bits(case["W"]), Hq, Hkv, D, gq, gk, EPS, c, s,
+                        rstd=rstd[rows])
+    if rb is not None:
+        assert np.array_equal(bits(xa)[rows], ref["x_add"]), f"{case.name}: x_add not bit-exact"
+    assert_rstd(rstd[rows], O.rms_norm_rows(ref["x_add"] if rb is not None else xb, bits(case["gamma"]), EPS)[1],
+                case.name)
+    yf, rf = O.bf16_bits_to_f32(yb).astype(np.float64), O.bf16_bits_to_f32(ref["y"]).astype(np.float64)
+    err = np.abs(yf[:, qk] - rf[:, qk])
+    assert (err <= (np.abs(rf[:, qk]) + 1.0) / 64).all(), f"{case.name}: head values off by {err.max():.3g}"
+    ry32, _, _ = O.rmsnorm_linear_bf16(ref["x_add"] if rb is not None else xb, bits(case["gamma"]), EPS,
+                                       bits(case["W"]), rstd=rstd[rows])
+    assert_bf16_close(yf[:, v], ry32[:, v], case.name)
+    return y
+
+
+@pytest.mark.parametrize("T,K,Hq,Hkv,D,residual,rope,head_gamma", [
+    (8, 256, 4, 2, 64, False, True, True),
+    (8, 256, 4, 2, 64, True, False, False),
+    (40, 1032, 6, 1, 128, True, True, True),   # tiled GEMM, ragged tiles
+    (3, 64, 2, 0, 16, False, True, False),     # no key / value heads
+    (20, 512, 3, 3, 192, False, True, True),
+])
+def test_preattn_small(T, K, Hq, Hkv, D, residual, rope, head_gamma):
+    case = synthetic.preattn_case(T, K, Hq, Hkv, D, seed=T + Hq, residual=residual, rope=rope,
+                                  head_gamma=head_gamma)
+    check_preattn_case(case)
+
+
+@pytest.mark.parametrize("T", [4096, 16])
+def test_preattn_block_full_size(T):
+    """Residual add -> norm -> fused QKV -> per-head norm -> RoPE, K=4096, 32 + 8 + 8 heads of 128."""
+    case = synthetic.preattn_block(T)
+    y1 = check_preattn_case(case, rows=sample_rows(T, 24))
+    y2 = run_preattn(case)[0]
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
