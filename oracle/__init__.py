@@ -31,4 +31,5 @@ from .rmsnorm_linear import (  # noqa: F401
     rope_rotate_half,
     head_rms_norm,
     preattn_qkv,
+    mla_prolog,
 )

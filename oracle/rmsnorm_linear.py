@@ -386,6 +386,25 @@ def norm_proj_chain(x_bits, Wa_bits, gamma_bits, eps, Wb_bits, rstd=None, qa_bit
     return {"qa": qa_bits, "qr": qr_bits, "y32": y32, "y_bf16": f32_to_bf16_bits(y32), "rstd": rstd}
 
 
+def mla_prolog(x_bits, Wa_bits, gq_bits, eps, Wb_bits, Wkv_bits, gkv_bits, rstd=None, rstd_kv=None):
+    """The query chain and the KV branch of the MLA prolog on one x (AT-10 page
+    section 5: besides q_a_proj -> norm -> q_b_proj, the KV path projects the
+    same x with the KV weight in BF16, applies RMSNorm, multiplies by
+    gamma_ckv and casts to BF16 -- a second AT-10 instance in parallel).
+
+    kv = bf16(x . W_kv^T); kv_out = bf16(RMSNorm(kv) * gamma_ckv).  READING: the
+    whole kv row is normed (the pages norm the KV projection as one row; a
+    rotary slice of it is not part of this step).  Returns norm_proj_chain's
+    dict plus kv (bits), kv_out (bits) and rstd_kv; ``rstd`` / ``rstd_kv``
+    replace the computed values when given.
+    """
+    out = norm_proj_chain(x_bits, Wa_bits, gq_bits, eps, Wb_bits, rstd)
+    kv = f32_to_bf16_bits(project_bf16(bf16_bits_to_f32(x_bits), Wkv_bits))
+    n, rkv = rms_norm_rows(kv, gkv_bits, eps, rstd_kv)
+    out.update(kv=kv, kv_out=f32_to_bf16_bits(n), rstd_kv=rkv)
+    return out
+
+
 def add_rmsnorm_linear_bf16(x_bits, r_bits, gamma_bits, eps, W_bits, rstd=None):
     """Residual add, then AT-10 on the sum.  Returns (x_add bits, y32, y_bf16
     bits, rstd)."""

@@ -606,3 +606,53 @@ def test_preattn_split_and_gammas():
     # a zero residual changes nothing
     z = O.preattn_qkv(x, np.zeros_like(x), g, 1e-6, W, Hq, Hkv, D, ones, twos, 1e-6)
     assert np.array_equal(z["y"], b["y"]) and np.array_equal(z["x_add"], x)
+
+
+# ---------------------------------------------------------------------------
+# MLA prolog: the KV branch beside the query chain
+# ---------------------------------------------------------------------------
+def _mla_inputs(T, K, R, Rkv, N, seed):
+    x = _rand_bf16_rows(T, K, seed=seed)
+    Wa = bits(synthetic.normal((R, K), K ** -0.5, seed, 5))
+    Wb = bits(synthetic.normal((N, R), R ** -0.5, seed, 6))
+    gq = bits(synthetic.uniform((R,), 0.5, 1.5, seed, 2))
+    gkv = bits(synthetic.uniform((Rkv,), 0.5, 1.5, seed, 8))
+    return x, Wa, Wb, gq, gkv
+
+
+def test_mla_kv_branch_selection_weight():
+    """W_kv = [I | 0] selects the first Rkv columns of x exactly (products with 1 and
+    0 are exact), so kv is x[:, :Rkv] and kv_out is the norm of those columns."""
+    T, K, R, Rkv, N = 6, 96, 32, 48, 40
+    x, Wa, Wb, gq, gkv = _mla_inputs(T, K, R, Rkv, N, 50)
+    sel = np.zeros((Rkv, K), dtype=np.float32)
+    sel[np.arange(Rkv), np.arange(Rkv)] = 1.0
+    out = O.mla_prolog(x, Wa, gq, 1e-6, Wb, O.f32_to_bf16_bits(sel), gkv)
+    assert np.array_equal(out["kv"], x[:, :Rkv])
+    n, r = O.rms_norm_rows(x[:, :Rkv], gkv, 1e-6)
+    assert np.array_equal(out["kv_out"], O.f32_to_bf16_bits(n)) and np.array_equal(out["rstd_kv"], r)
+
+
+def test_mla_kv_branch_permuted_weight():
+    """A permutation weight permutes the kv columns; with gamma_ckv permuted the same
+    way the normed row is the permutation of the unpermuted one."""
+    T, K, R, N = 4, 64, 16, 8
+    x, Wa, Wb, gq, _ = _mla_inputs(T, K, R, K, N, 51)
+    perm = np.random.default_rng(52).permutation(K)
+    P = np.zeros((K, K), dtype=np.float32)
+    P[np.arange(K), perm] = 1.0
+    g = bits(synthetic.uniform((K,), 0.5, 1.5, 51, 9))
+    a = O.mla_prolog(x, Wa, gq, 1e-6, Wb, O.f32_to_bf16_bits(P), g[perm])
+    n, _ = O.rms_norm_rows(x, g, 1e-6)
+    assert np.array_equal(a["kv"], x[:, perm])
+    assert np.array_equal(a["kv_out"], O.f32_to_bf16_bits(n)[:, perm])
+
+
+def test_mla_query_outputs_unchanged_by_kv_branch():
+    T, K, R, Rkv, N = 5, 128, 32, 24, 20
+    x, Wa, Wb, gq, gkv = _mla_inputs(T, K, R, Rkv, N, 53)
+    Wkv = bits(synthetic.normal((Rkv, K), K ** -0.5, 53, 7))
+    out = O.mla_prolog(x, Wa, gq, 1e-6, Wb, Wkv, gkv)
+    ref = O.norm_proj_chain(x, Wa, gq, 1e-6, Wb)
+    for k in ("qa", "qr", "y_bf16", "rstd"):
+        assert np.array_equal(out[k], ref[k]), k
