@@ -55,6 +55,8 @@ WORKLOADS = {
                       desc="RMSNorm -> per-token int8 quant -> int8 GEMM -> dequant"),
     "mla_q_chain": dict(kind="chain", T=1024, K=7168, R=1536, N=24576, bound="mfma", dtype="bf16",
                         desc="x -> W_a[1536,7168] -> RMSNorm -> W_b[24576,1536]"),
+    "mla_prolog": dict(kind="mla", T=1024, K=7168, R=1536, Rkv=512, N=24576, bound="mfma", dtype="bf16",
+                       desc="x -> [W_a; W_kv] -> RMSNorm of q_a and of kv -> W_b[24576,1536]"),
     "skinny_fp32": dict(kind="fp32w", T=512, K=28672, N=24, bound="hbm", dtype="f32",
                         desc="large-reduction tiny-width norm + linear, fp32 weight, no gamma"),
 }
@@ -67,6 +69,8 @@ KERNEL_SOURCES = {
 
 
 def flops_of(w):
+    if w["kind"] == "mla":
+        return 2.0 * w["T"] * (w["K"] * (w["R"] + w["Rkv"]) + w["R"] * w["N"])
     if w["kind"] == "chain":
         return 2.0 * w["T"] * (w["K"] * w["R"] + w["R"] * w["N"])
     return 2.0 * w["T"] * w["K"] * w["N"]
@@ -85,8 +89,8 @@ def bytes_of(w):
         return T * K * 2 + K * 2 + N * K + N * 4 + T * N * 2
     if w["kind"] == "fp32w":
         return T * K * 2 + N * K * 4 + T * N * 4
-    R = w["R"]
-    return T * K * 2 + R * K * 2 + R * 2 + N * R * 2 + T * R * 2 + T * N * 2
+    R = w["R"] + w.get("Rkv", 0)  # the KV branch adds its weight rows, gamma and normed outputs
+    return T * K * 2 + R * K * 2 + R * 2 + w["R"] * N * 2 + T * R * 2 + T * N * 2
 
 
 def src_sha(names):
@@ -132,6 +136,7 @@ class Setup:
             "int8": lambda: synthetic.int8_case(w["T"], w["K"], w["N"], name=name),
             "chain": lambda: synthetic.chain_case(w["T"], w["K"], w["R"], w["N"], name=name),
             "preattn": lambda: synthetic.preattn_block(w["T"]),
+            "mla": lambda: synthetic.mla_prolog(),
         }[kind]()
         if w.get("add"):
             self.case = synthetic.with_residual(self.case)
@@ -209,6 +214,19 @@ class Setup:
             self.kernel, self.kernel_key = "gemm_nt_kernel<int8>", "gemm"
             self.kern = lambda i: rnl.linear_int8(xq, xs, t["Wq"], t["w_scale"], y=y)
             self.kern_units = ("int8", flops_of(w))
+        elif kind == "mla":
+            R, Rkv = w["R"], w["Rkv"]
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            qr = torch.empty((T, R), dtype=torch.bfloat16, device=dev)
+            kvo = torch.empty((T, Rkv), dtype=torch.bfloat16, device=dev)
+            W_akv = torch.cat([t["W_a"], t["W_kv"]], dim=0).contiguous()
+            ws = torch.empty(rnl.workspace_bytes("mla", T, K, R, Rkv, N), dtype=torch.uint8, device=dev)
+            self.step = lambda i: rnl.mla_prolog_bf16(t["x"], W_akv, R, t["gamma"], t["gamma_ckv"], eps, t["W_b"],
+                                                      qr_out=qr, kv_out=kvo, y=y, workspace=ws)
+            self.step(0)
+            self.kernel, self.kernel_key = "gemm_nt_kernel<bf16> (stage 2, qr . W_b^T)", "gemm"
+            self.kern = lambda i: rnl.linear_bf16(qr, t["W_b"], y=y)
+            self.kern_units = ("bf16", 2.0 * T * R * N)
         else:
             R = w["R"]
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
@@ -302,6 +320,8 @@ def cpu_baseline(setup, target_s=8.0):
             O.rmsnorm_linear_fp32w(x, g, c.eps, c["W"].numpy())
         elif kind == "int8":
             O.rmsnorm_linear_int8(x, g, c.eps, c["Wq"].numpy(), c["w_scale"].numpy())
+        elif kind == "mla":
+            O.mla_prolog(x, bits(c["W_a"]), g, c.eps, bits(c["W_b"]), bits(c["W_kv"]), bits(c["gamma_ckv"]))
         else:
             O.norm_proj_chain(x, bits(c["W_a"]), g, c.eps, bits(c["W_b"]))
 
@@ -369,7 +389,7 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
         "dtype": w["dtype"],
         "data": "synthetic",
         "config": {"workload": s.case.name, "description": w["desc"],
-                   **{k: w[k] for k in ("T", "K", "R", "N", "Hq", "Hkv", "D") if k in w},
+                   **{k: w[k] for k in ("T", "K", "R", "Rkv", "N", "Hq", "Hkv", "D") if k in w},
                    "parallelism": "none (1 GPU)", "input_copies": s.copies,
                    "timing": "hip graph of the timed steps" if graph else "eager launches"},
         "roofline": {"bound": bound, "kernel": s.kernel, "achieved": round(achieved, 3), "peak": PEAK[peak_key],

@@ -194,6 +194,34 @@ RNL_API int norm_proj_chain(const void* x, const void* W_a, const void* gamma, f
 RNL_API size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N);
 
 /*
+ * mla_prolog_bf16 -- the query chain of norm_proj_chain and the KV branch of the
+ * MLA prolog, with one pass over x for both first projections.
+ *
+ * AT-10 page, section 5: beside q_a_proj -> norm -> q_b_proj, the KV path
+ * projects the same x with the KV weight (bf16 out), applies RMSNorm, multiplies
+ * by gamma_ckv and casts to bf16: a second AT-10 instance sharing x.
+ *
+ *   x         [T, K] bf16.
+ *   W_akv     [R + Rkv, K] bf16: rows [0, R) the query down-projection W_a,
+ *             rows [R, R + Rkv) the KV projection W_kv (stacked by the caller).
+ *   [q_a | kv] = round_bf16(x . W_akv^T)                       [T, R + Rkv]
+ *   qr_out    [T, R]   = round_bf16(RMSNorm(q_a) * gamma_cq)     (required)
+ *   kv_out    [T, Rkv] = round_bf16(RMSNorm(kv) * gamma_ckv)     (required)
+ *   y         [T, N]   = round_bf16(qr . W_b^T), W_b [N, R] bf16.
+ *   gamma_cq [R], gamma_ckv [Rkv] bf16 or NULL; one eps for both norms.
+ *   rstd_q_out, rstd_kv_out [T] fp32 or NULL.
+ *   R and Rkv must be multiples of 8.  Outputs must not overlap inputs.
+ *
+ * Errors: as norm_proj_chain.
+ */
+RNL_API int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, const void* gamma_ckv, float eps,
+                            const void* W_b, void* qr_out, void* kv_out, void* y, float* rstd_q_out,
+                            float* rstd_kv_out, int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+RNL_API size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N);
+
+/*
  * preattn_qkv_bf16 -- the pre-attention block around the fused norm and
  * projection: optional residual add, input RMSNorm, fused QKV projection,
  * split into heads, per-head RMSNorm of the query and key heads, optional

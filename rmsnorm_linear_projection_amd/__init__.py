@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
   with the residual add in front (x_add = x + residual, also returned);
 * :func:`preattn_qkv_bf16` -- (residual add ->) RMSNorm -> fused QKV projection ->
   per-head RMSNorm of the query and key heads (-> RoPE);
+* :func:`mla_prolog_bf16` -- the chain plus the KV branch (kv = x W_kv^T -> RMSNorm),
+  one pass over x for both first projections;
 * :func:`norm_proj_chain` -- q_a = x W_a^T -> RMSNorm -> qr -> y = qr W_b^T.
 """
 from __future__ import annotations
@@ -31,6 +33,7 @@ __all__ = [
     "add_rmsnorm_linear_bf16",
     "add_rmsnorm_linear_int8",
     "norm_proj_chain",
+    "mla_prolog_bf16",
     "preattn_qkv_bf16",
     "head_rms_norm_bf16",
     "rms_norm_bf16",
@@ -114,6 +117,11 @@ def load_library() -> ctypes.CDLL:
     lib.head_rms_norm_bf16.argtypes = [_c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
                                        _c_i64, _c_i64, _c_p]
     lib.head_rms_norm_bf16.restype = ctypes.c_int
+    lib.mla_prolog_bf16.argtypes = [_c_p, _c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                    _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+    lib.mla_prolog_bf16.restype = ctypes.c_int
+    lib.mla_prolog_bf16_workspace_bytes.argtypes = [_c_i64] * 5
+    lib.mla_prolog_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -165,7 +173,7 @@ def _workspace(nbytes: int, dev, given):
 
 def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.bfloat16) -> int:
     """Workspace a call needs: kind 'bf16', 'int8', 'add_bf16', 'add_int8' (T, K, N), 'chain' (T, K, R, N)
-    or 'preattn' (T, K, Hq, Hkv, D)."""
+    'preattn' (T, K, Hq, Hkv, D) or 'mla' (T, K, R, Rkv, N)."""
     lib = load_library()
     if kind == "bf16":
         return int(lib.rmsnorm_linear_bf16_workspace_bytes(*shape, _DTYPE_CODE[w_dtype], _DTYPE_CODE[out_dtype]))
@@ -179,6 +187,8 @@ def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.b
         return int(lib.norm_proj_chain_workspace_bytes(*shape))
     if kind == "preattn":
         return int(lib.preattn_qkv_bf16_workspace_bytes(*shape))
+    if kind == "mla":
+        return int(lib.mla_prolog_bf16_workspace_bytes(*shape))
     raise ValueError(kind)
 
 
@@ -332,6 +342,45 @@ def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None,
                                  _ptr(rstd_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
     _check(rc)
     return y, qr_out
+
+
+def mla_prolog_bf16(x, W_akv, R, gamma_cq, gamma_ckv, eps, W_b, qr_out=None, kv_out=None, y=None, rstd_q_out=None,
+                    rstd_kv_out=None, workspace=None):
+    """MLA prolog query chain + KV branch (AT-10 page section 5).  W_akv stacks the
+    query down-projection (rows [0, R)) and the KV projection (rows [R, R + Rkv)).
+    Returns (y [T, N], qr [T, R], kv [T, Rkv])."""
+    lib = load_library()
+    for t, n in ((x, "x"), (W_akv, "W_akv"), (W_b, "W_b")):
+        _dev_tensor(t, n, torch.bfloat16, 2)
+    _dev_tensor(gamma_cq, "gamma_cq", torch.bfloat16, 1)
+    _dev_tensor(gamma_ckv, "gamma_ckv", torch.bfloat16, 1)
+    _dev_tensor(rstd_q_out, "rstd_q_out", torch.float32)
+    _dev_tensor(rstd_kv_out, "rstd_kv_out", torch.float32)
+    T, K = x.shape
+    Rkv = W_akv.shape[0] - R
+    N = W_b.shape[0]
+    _shape(W_akv.shape[1] == K and Rkv > 0, "W_akv must be [R + Rkv, K] with Rkv > 0")
+    _shape(W_b.shape[1] == R, "W_b must be [N, R]")
+    _shape(gamma_cq is None or gamma_cq.numel() == R, "gamma_cq must be [R]")
+    _shape(gamma_ckv is None or gamma_ckv.numel() == Rkv, "gamma_ckv must be [Rkv]")
+    _shape(rstd_q_out is None or rstd_q_out.numel() >= T, "rstd_q_out must hold T values")
+    _shape(rstd_kv_out is None or rstd_kv_out.numel() >= T, "rstd_kv_out must hold T values")
+    outs = []
+    for t, shp, n in ((qr_out, (T, R), "qr_out"), (kv_out, (T, Rkv), "kv_out"), (y, (T, N), "y")):
+        if t is None:
+            t = torch.empty(shp, dtype=torch.bfloat16, device=x.device)
+        _dev_tensor(t, n, torch.bfloat16)
+        _shape(tuple(t.shape) == shp, f"{n} must be {list(shp)}")
+        outs.append(t)
+    qr_out, kv_out, y = outs
+    with torch.cuda.device(x.device):
+        need = int(lib.mla_prolog_bf16_workspace_bytes(T, K, R, Rkv, N))
+        ws, ws_bytes = _workspace(need, x.device, workspace)
+        rc = lib.mla_prolog_bf16(_ptr(x), _ptr(W_akv), _ptr(gamma_cq), _ptr(gamma_ckv), float(eps), _ptr(W_b),
+                                 _ptr(qr_out), _ptr(kv_out), _ptr(y), _ptr(rstd_q_out), _ptr(rstd_kv_out), T, K, R,
+                                 Rkv, N, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(rc)
+    return y, qr_out, kv_out
 
 
 def _rope_tables(cos, sin, T, D):

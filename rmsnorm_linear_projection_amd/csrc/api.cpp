@@ -338,7 +338,7 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
     float* part = static_cast<float*>(workspace);
     e = rnl::launch_gemm_bf16_splitk(xb, wa, part, T, R, K, ks, s);
     if (e != hipSuccess) return hip_status(e, "chain stage-1 split-K GEMM launch");
-    e = rnl::launch_reduce_norm_bf16(part, ks, gb, eps, T, R, qr, rstd_out, s);
+    e = rnl::launch_reduce_norm_bf16(part, ks, R, gb, eps, T, R, qr, rstd_out, s);
     if (e != hipSuccess) return hip_status(e, "chain reduce+norm launch");
   } else {
     uint16_t* qa = static_cast<uint16_t*>(workspace);
@@ -350,6 +350,74 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
   return hip_status(project_bf16(static_cast<const uint16_t*>(qr_out), static_cast<const uint16_t*>(W_b), y,
                                  rnl::OUT_BF16, T, N, R, s),
                     "chain stage-2 projection launch");
+}
+
+size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N) {
+  (void)N;
+  if (T <= 0 || R <= 0 || Rkv <= 0 || K <= 0) return 0;
+  const int64_t Rt = R + Rkv;
+  const int ks = chain_splits(T, Rt, K);
+  if (ks > 1) return align256((size_t)ks * (size_t)T * (size_t)Rt * 4);  // fp32 split-K partials of [q_a | kv]
+  return align256((size_t)T * (size_t)Rt * 2);                           // bf16 [q_a | kv]
+}
+
+int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, const void* gamma_ckv, float eps,
+                    const void* W_b, void* qr_out, void* kv_out, void* y, float* rstd_q_out, float* rstd_kv_out,
+                    int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (x == nullptr || W_akv == nullptr || W_b == nullptr || qr_out == nullptr || kv_out == nullptr || y == nullptr)
+    return fail(RNL_ERR_NULL, "x, W_akv, W_b, qr_out, kv_out and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK));
+  RNL_TRY(check_dims(T, R, N, kMaxK));
+  RNL_TRY(check_dims(T, Rkv, N, kMaxK));
+  RNL_TRY(check_dims(T, K, R + Rkv, kMaxK));
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(W_akv, 16, "W_akv");
+  RNL_ALIGN(gamma_cq, 16, "gamma_cq");
+  RNL_ALIGN(gamma_ckv, 16, "gamma_ckv");
+  RNL_ALIGN(W_b, 16, "W_b");
+  RNL_ALIGN(qr_out, 16, "qr_out");
+  RNL_ALIGN(kv_out, 16, "kv_out");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(rstd_q_out, 4, "rstd_q_out");
+  RNL_ALIGN(rstd_kv_out, 4, "rstd_kv_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  const size_t need = mla_prolog_bf16_workspace_bytes(T, K, R, Rkv, N);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* w = static_cast<const uint16_t*>(W_akv);
+  const uint16_t* gq = static_cast<const uint16_t*>(gamma_cq);
+  const uint16_t* gkv = static_cast<const uint16_t*>(gamma_ckv);
+  uint16_t* qr = static_cast<uint16_t*>(qr_out);
+  uint16_t* kvo = static_cast<uint16_t*>(kv_out);
+  const int64_t Rt = R + Rkv;
+  const int ks = chain_splits(T, Rt, K);
+  hipError_t e;
+  // one pass over x for both branches: [q_a | kv] = x . [W_a; W_kv]^T, then each
+  // part of the row is normed with its own gamma
+  if (ks > 1) {
+    float* part = static_cast<float*>(workspace);
+    e = rnl::launch_gemm_bf16_splitk(xb, w, part, T, Rt, K, ks, s);
+    if (e != hipSuccess) return hip_status(e, "stage-1 split-K GEMM launch");
+    e = rnl::launch_reduce_norm_bf16(part, ks, Rt, gq, eps, T, R, qr, rstd_q_out, s);
+    if (e != hipSuccess) return hip_status(e, "query reduce+norm launch");
+    e = rnl::launch_reduce_norm_bf16(part + R, ks, Rt, gkv, eps, T, Rkv, kvo, rstd_kv_out, s);
+    if (e != hipSuccess) return hip_status(e, "kv reduce+norm launch");
+  } else {
+    uint16_t* qakv = static_cast<uint16_t*>(workspace);
+    e = project_bf16(xb, w, qakv, rnl::OUT_BF16, T, Rt, K, s);
+    if (e != hipSuccess) return hip_status(e, "stage-1 projection launch");
+    e = rnl::launch_norm_rows_bf16_strided(qakv, Rt, gq, eps, T, R, qr, rstd_q_out, s);
+    if (e != hipSuccess) return hip_status(e, "query norm launch");
+    e = rnl::launch_norm_rows_bf16_strided(qakv + R, Rt, gkv, eps, T, Rkv, kvo, rstd_kv_out, s);
+    if (e != hipSuccess) return hip_status(e, "kv norm launch");
+  }
+  return hip_status(project_bf16(qr, static_cast<const uint16_t*>(W_b), y, rnl::OUT_BF16, T, N, R, s),
+                    "stage-2 projection launch");
 }
 
 size_t preattn_qkv_bf16_workspace_bytes(int64_t T, int64_t K, int64_t Hq, int64_t Hkv, int64_t D) {

@@ -31,9 +31,14 @@ hipError_t launch_add_norm_rows_int8(const uint16_t* x, const uint16_t* residual
 hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t* x_add, int64_t T, int64_t K,
                            hipStream_t s);
 // Same norm (bf16 out) applied to rows that are the bf16 rounding of the sum of S
-// fp32 split-K partials part[S, T, K], added in split order.
-hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,
+// fp32 split-K partials, added in split order: row t of slice z starts at
+// part + z * T * ld + t * ld (ld >= K, a multiple of 8); out is [T, K].
+hipError_t launch_reduce_norm_bf16(const float* part, int S, int64_t ld, const uint16_t* gamma, float eps,
                                    int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s);
+// The bf16 norm of K values of rows with stride ld (x + t * ld; ld a multiple of
+// 8); out is [T, K].
+hipError_t launch_norm_rows_bf16_strided(const uint16_t* x, int64_t ld, const uint16_t* gamma, float eps, int64_t T,
+                                         int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s);
 
 // Per-head RMSNorm (+ rotate-half RoPE when cos_t/sin_t are given) of the H
 // heads of D columns that start at column col0 of y_in[T, ld] (bf16), written

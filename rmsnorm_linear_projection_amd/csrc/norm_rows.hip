@@ -71,10 +71,10 @@ __device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
 // Row sources: chunk idx (8 consecutive elements, packed bf16) of row t.
 // keep(t, idx, v) is called once per chunk in the first pass over the row.
 struct RowBf16 {
-  const uint16_t* x;  // [T, K] bf16
-  int64_t K;
+  const uint16_t* x;  // row t at x + t * ld, K bf16 values
+  int64_t ld;
   __device__ u32x4 operator()(int64_t t, int idx) const {
-    return reinterpret_cast<const u32x4*>(x + t * K)[idx];
+    return reinterpret_cast<const u32x4*>(x + t * ld)[idx];
   }
   __device__ void keep(int64_t, int, u32x4) const {}
 };
@@ -89,14 +89,14 @@ struct RowAddBf16 {
   __device__ void keep(int64_t t, int idx, u32x4 v) const { reinterpret_cast<u32x4*>(x_add + t * K)[idx] = v; }
 };
 struct RowPartials {
-  const float* part;  // [S, T, K] fp32
-  int64_t TK;         // T * K
-  int64_t K;
+  const float* part;  // slice z, row t at part + z * TK + t * ld
+  int64_t TK;         // slice stride
+  int64_t ld;         // row stride
   int S;
   __device__ u32x4 operator()(int64_t t, int idx) const {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
     for (int z = 0; z < S; ++z) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)z * (size_t)TK + (size_t)t * (size_t)K) + 2 * idx;
+      const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)z * (size_t)TK + (size_t)t * (size_t)ld) + 2 * idx;
       lo += p[0];
       hi += p[1];
     }
@@ -329,6 +329,11 @@ hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float
   return launch_norm<false>(RowBf16{x, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
 
+hipError_t launch_norm_rows_bf16_strided(const uint16_t* x, int64_t ld, const uint16_t* gamma, float eps, int64_t T,
+                                         int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
+  return launch_norm<false>(RowBf16{x, ld}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
+}
+
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s) {
@@ -371,9 +376,9 @@ hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_norm_bf16(const float* part, int S, const uint16_t* gamma, float eps,
+hipError_t launch_reduce_norm_bf16(const float* part, int S, int64_t ld, const uint16_t* gamma, float eps,
                                    int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s) {
-  return launch_norm<false>(RowPartials{part, T * K, K, S}, gamma, eps, T, K, out, nullptr, rstd_out, s);
+  return launch_norm<false>(RowPartials{part, T * ld, ld, S}, gamma, eps, T, K, out, nullptr, rstd_out, s);
 }
 
 }  // namespace rnl

@@ -28,7 +28,7 @@ EPS = 1e-6
 
 # stream ids: one per tensor role, so that adding a tensor never shifts another
 _S_X, _S_GAMMA, _S_W, _S_WSCALE, _S_WA, _S_WB, _S_RES = 1, 2, 3, 4, 5, 6, 7
-_S_GQ, _S_GK, _S_ANGLE = 8, 9, 10
+_S_GQ, _S_GK, _S_ANGLE, _S_WKV, _S_GKV = 8, 9, 10, 11, 12
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -139,6 +139,16 @@ def chain_case(T: int, K: int, R: int, N: int, seed: int = 0, gamma: bool = True
     return Case(name or f"chain_T{T}_K{K}_R{R}_N{N}", t, EPS, {"T": T, "K": K, "R": R, "N": N})
 
 
+def mla_case(T: int, K: int, R: int, Rkv: int, N: int, seed: int = 0, gamma: bool = True,
+             name: str | None = None) -> Case:
+    """The chain of chain_case plus the KV branch: W_kv[Rkv, K] ~ N(0, 1/K), gamma_ckv[Rkv]."""
+    case = chain_case(T, K, R, N, seed, gamma, name=name or f"mla_T{T}_K{K}_R{R}_Rkv{Rkv}_N{N}")
+    case.tensors["W_kv"] = normal((Rkv, K), 1.0 / math.sqrt(K), seed, _S_WKV)
+    case.tensors["gamma_ckv"] = uniform((Rkv,), 0.5, 1.5, seed, _S_GKV) if gamma else None
+    case.dims["Rkv"] = Rkv
+    return case
+
+
 # The five workloads, by what they are.
 def small_norm_linear(seed: int = 0) -> Case:
     """bf16 RMSNorm + Linear, T=8 tokens, K=256, N=128."""
@@ -169,6 +179,11 @@ def int8_w8a8(seed: int = 0) -> Case:
 def mla_q_chain(seed: int = 0) -> Case:
     """Low-rank query chain x[1024,7168] -> W_a[1536,7168] -> norm -> W_b[24576,1536]."""
     return chain_case(1024, 7168, 1536, 24576, seed, name="mla_q_chain_T1024_K7168_R1536_N24576")
+
+
+def mla_prolog(seed: int = 0) -> Case:
+    """Low-rank query chain plus the KV branch (kv_lora_rank 512) on the same x."""
+    return mla_case(1024, 7168, 1536, 512, 24576, seed, name="mla_prolog_T1024_K7168_R1536_Rkv512_N24576")
 
 
 def skinny_fp32(seed: int = 0) -> Case:

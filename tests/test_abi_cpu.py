@@ -239,6 +239,32 @@ def test_head_norm_validation(lib, kw, code):
     assert head_call(lib, **kw) == E[code]
 
 
+def mla_call(lib, x=FAKE, W=FAKE, gq=NULL, gkv=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, kv=FAKE, y=FAKE, rq=NULL, rkv=NULL,
+             T=4, K=64, R=32, Rkv=16, N=8, ws=FAKE, wsb=1 << 30):
+    return lib.mla_prolog_bf16(x, W, gq, gkv, eps, Wb, qr, kv, y, rq, rkv, T, K, R, Rkv, N, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=NULL), "RNL_ERR_NULL"),
+    (dict(W=NULL), "RNL_ERR_NULL"),
+    (dict(Rkv=12), "RNL_ERR_SHAPE"),
+    (dict(Rkv=0), "RNL_ERR_SHAPE"),
+    (dict(R=20), "RNL_ERR_SHAPE"),
+    (dict(gkv=ODD), "RNL_ERR_ALIGN"),
+    (dict(rkv=ctypes.c_void_p(0x10001)), "RNL_ERR_ALIGN"),
+    (dict(ws=NULL), "RNL_ERR_WORKSPACE"),
+    (dict(eps=-1.0), "RNL_ERR_ARG"),
+])
+def test_mla_validation(lib, kw, code):
+    assert mla_call(lib, **kw) == E[code]
+
+
+def test_mla_workspace(lib):
+    # few tokens: no split, bf16 [q_a | kv]; many: fp32 split partials of both
+    assert lib.mla_prolog_bf16_workspace_bytes(4, 7168, 1536, 512, 24576) == 4 * 2048 * 2 + (-(4 * 2048 * 2) % 256)
+    assert lib.mla_prolog_bf16_workspace_bytes(1024, 7168, 1536, 512, 24576) >= 2 * 1024 * 2048 * 4
+
+
 def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, T=4, K=64, R=32,
                N=8, ws=FAKE, wsb=1 << 30):
     return lib.norm_proj_chain(x, Wa, g, eps, Wb, qr, y, rstd, T, K, R, N, ws, wsb, NULL)

@@ -695,3 +695,58 @@ def test_preattn_block_full_size(T):
     y1 = check_preattn_case(case, rows=sample_rows(T, 24))
     y2 = run_preattn(case)[0]
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+
+
+# ---------------------------------------------------------------------------
+# MLA prolog: query chain + KV branch with one stage-1 pass over x (stacked
+# weight).  Stage 1 is an fp32 accumulation rounded to bf16 on both sides, so
+# qr, kv and their rstd are compared with the bf16 / relative bounds of the
+# chain; y is checked from the device's own qr.
+# ---------------------------------------------------------------------------
+def run_mla(case):
+    x, Wa, Wkv, gq, gkv, Wb = (dev(case[k]) for k in ("x", "W_a", "W_kv", "gamma", "gamma_ckv", "W_b"))
+    T, R = x.shape[0], Wa.shape[0]
+    W_akv = torch.cat([Wa, Wkv], dim=0).contiguous()
+    rq = torch.empty(T, dtype=torch.float32, device="cuda")
+    rkv = torch.empty(T, dtype=torch.float32, device="cuda")
+    y, qr, kv = rnl.mla_prolog_bf16(x, W_akv, R, gq, gkv, EPS, Wb, rstd_q_out=rq, rstd_kv_out=rkv)
+    torch.cuda.synchronize()
+    return y.cpu(), qr.cpu(), kv.cpu(), rq.cpu().numpy(), rkv.cpu().numpy()
+
+
+def check_mla_case(case, rows=None):
+    y, qr, kv, rq, rkv = run_mla(case)
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb = bits(case["x"])[rows]
+    gq = None if case["gamma"] is None else bits(case["gamma"])
+    gkv = None if case["gamma_ckv"] is None else bits(case["gamma_ckv"])
+    ref = O.mla_prolog(xb, bits(case["W_a"]), gq, EPS, bits(case["W_b"]), bits(case["W_kv"]), gkv)
+    for got, want, what in ((rq[rows], ref["rstd"], "rstd_q"), (rkv[rows], ref["rstd_kv"], "rstd_kv")):
+        rel = np.abs(got.astype(np.float64) / want - 1)
+        assert rel.max() < 1e-3, f"{case.name}: {what} rel err {rel.max():.3g}"
+    assert_bf16_close(f32(qr)[rows], O.bf16_bits_to_f32(ref["qr"]), case.name + " qr")
+    assert_bf16_close(f32(kv)[rows], O.bf16_bits_to_f32(ref["kv_out"]), case.name + " kv")
+    y_ref = O.project_bf16(O.bf16_bits_to_f32(bits(qr)[rows]), bits(case["W_b"]))
+    assert_bf16_close(f32(y)[rows], y_ref, case.name + " y")
+    return y, kv
+
+
+@pytest.mark.parametrize("T,K,R,Rkv,N,gamma", [
+    (37, 256, 64, 32, 80, True),
+    (64, 4096, 128, 64, 64, True),      # stage 1 split over K
+    (50, 2056, 72, 40, 33, False),      # split with a K tail, ragged R + Rkv
+    (4, 7168, 1536, 512, 520, True),    # few tokens: both stages stream their weights
+    (300, 520, 136, 16, 260, True),
+])
+def test_mla_prolog_small(T, K, R, Rkv, N, gamma):
+    check_mla_case(synthetic.mla_case(T, K, R, Rkv, N, seed=T + Rkv, gamma=gamma))
+
+
+def test_mla_prolog_full_size():
+    """Query chain + KV branch, T=1024, K=7168, R=1536, Rkv=512, N=24576, at full size."""
+    case = synthetic.mla_prolog()
+    y1, kv1 = check_mla_case(case, rows=sample_rows(1024, 12))
+    y2, _, kv2, _, _ = run_mla(case)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and torch.equal(kv1.view(torch.int16),
+                                                                                   kv2.view(torch.int16))
