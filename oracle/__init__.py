@@ -32,4 +32,10 @@ from .rmsnorm_linear import (  # noqa: F401
     head_rms_norm,
     preattn_qkv,
     mla_prolog,
+    e4m3_decode,
+    e4m3_encode,
+    e8m0_decode,
+    mx_quant_rows,
+    mx_scaled_mm,
+    rmsnorm_linear_mxfp8,
 )

@@ -258,6 +258,99 @@ def add_residual(x_bits, r_bits) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# MXFP8 (AT-09 MXFP8 mode): E4M3 elements, one E8M0 scale per 64 elements
+# ----------------------------------------------------------------------------
+MX_BLOCK = 64
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 (FN: no infinities) bytes -> fp32 values.  Sign bit, 4 exponent bits
+    with bias 7, 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9);
+    exponent 15 with mantissa 7 is NaN.  The SK-14 page names the data format of
+    its MXFP8 grouped matmul as E4M3FN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return (sign * mag).astype(F32)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """fp32 -> E4M3 bytes, round to nearest even, saturating to +-448.
+
+    READING: the pages fix the format but not the conversion; the OCP MX rule
+    is taken -- the nearest representable value (ties to the even mantissa),
+    and magnitudes beyond the largest normal 448 are clamped to it.  A zero
+    (of either sign) encodes as +0.
+    """
+    v = np.asarray(v, dtype=F64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                          # a = f * 2^e, f in [0.5, 1)
+    q = np.maximum(e - 1, -6) - 3               # exponent of the spacing at a
+    r = np.rint(a * np.exp2(-q)) * np.exp2(q)   # exact scaling, RNE to the spacing
+    r = np.minimum(r, E4M3_MAX)
+    _, e2 = np.frexp(r)
+    E = e2 - 1
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, E + 7, 0)
+    mant = np.where(normal, r * np.exp2(-E.astype(F64)) * 8 - 8, r * 2.0 ** 9)
+    code = (exp_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(r == 0, 0, code | np.where(v < 0, 0x80, 0))
+    return code.astype(np.uint8)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(code - 127) (fp64; code 255 is NaN)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def mx_quant_rows(n: np.ndarray, block: int = MX_BLOCK):
+    """MX quantisation of fp32 rows n [T, K] (K a multiple of ``block``).
+    Returns (codes [T, K] E4M3 bytes, scales [T, K/block] E8M0 bytes).
+
+    AT-09 page text (AT-10 page section 4): MXFP8 mode multiplies fp8 operands
+    with their scales inside one scaled matmul; the SK-14 page gives the layout
+    (E4M3FN data, E8M0 scale, one scale shared by 64 elements).  READING (how
+    the activations get their scale, not stated): the OCP MX rule -- per block
+    of 64 consecutive k, X = 2^(floor(log2(amax)) - 8) with 8 the largest
+    exponent of E4M3, the exponent clamped to E8M0's [-127, 127]; an all-zero
+    block takes X = 2^-127; each element is e4m3_encode(n / X).
+    """
+    n = np.asarray(n, dtype=F32)
+    T, K = n.shape
+    nb = n.reshape(T, K // block, block).astype(F64)
+    amax = np.max(np.abs(nb), axis=-1)
+    _, e = np.frexp(amax)
+    shared = np.where(amax > 0, e - 1 - 8, -127)
+    shared = np.clip(shared, -127, 127)
+    codes = e4m3_encode(nb * np.exp2(-shared.astype(F64))[..., None]).reshape(T, K)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def mx_scaled_mm(qx, sx, qw, sw, block: int = MX_BLOCK) -> np.ndarray:
+    """scaled_mm(x_fp8, w_fp8, FP32, x_scale, w_scale) with W stored [N, K]:
+    y[t, n] = sum over blocks b of X_x[t, b] X_w[n, b] sum_{k in b} x[t, k] w[n, k].
+
+    The E4M3 products are exact and every scale is a power of two, so the oracle
+    forms the exact sum in fp64 and rounds once to fp32 (AT-10 page section 4:
+    the MXFP8 product accumulates into FP32).
+    """
+    xf = e4m3_decode(qx).astype(F64)
+    wf = e4m3_decode(qw).astype(F64)
+    T, K = xf.shape
+    N = wf.shape[0]
+    xs = e8m0_decode(sx)
+    ws = e8m0_decode(sw)
+    xb = (xf.reshape(T, K // block, block) * xs[..., None]).reshape(T, K)
+    wb = (wf.reshape(N, K // block, block) * ws[..., None]).reshape(N, K)
+    return (xb @ wb.T).astype(F32)
+
+
+# ----------------------------------------------------------------------------
 # Post-projection V stage: per-head RMSNorm and rotary embedding
 # ----------------------------------------------------------------------------
 def rope_rotate_half(n: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
@@ -384,6 +477,18 @@ def norm_proj_chain(x_bits, Wa_bits, gamma_bits, eps, Wb_bits, rstd=None, qa_bit
     qr_bits = f32_to_bf16_bits(n)
     y32 = project_bf16(bf16_bits_to_f32(qr_bits), Wb_bits)
     return {"qa": qa_bits, "qr": qr_bits, "y32": y32, "y_bf16": f32_to_bf16_bits(y32), "rstd": rstd}
+
+
+def rmsnorm_linear_mxfp8(x_bits, gamma_bits, eps, qw, sw, rstd=None):
+    """AT-10 with AT-09's MXFP8 mode: the fp32 normed rows are MX-quantised
+    (64-element blocks) and multiplied by the MXFP8 weight (E4M3 [N, K] with
+    E8M0 scales [N, K/64]) in one scaled product accumulating in fp32.
+    Returns a dict with q (E4M3 bytes), x_scale (E8M0 bytes), y32, y_bf16 (bits),
+    rstd."""
+    n, rstd = rms_norm_rows(x_bits, gamma_bits, eps, rstd)
+    q, xs = mx_quant_rows(n)
+    y32 = mx_scaled_mm(q, xs, qw, sw)
+    return {"q": q, "x_scale": xs, "y32": y32, "y_bf16": f32_to_bf16_bits(y32), "rstd": rstd}
 
 
 def mla_prolog(x_bits, Wa_bits, gq_bits, eps, Wb_bits, Wkv_bits, gkv_bits, rstd=None, rstd_kv=None):

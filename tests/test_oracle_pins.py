@@ -656,3 +656,131 @@ def test_mla_query_outputs_unchanged_by_kv_branch():
     ref = O.norm_proj_chain(x, Wa, gq, 1e-6, Wb)
     for k in ("qa", "qr", "y_bf16", "rstd"):
         assert np.array_equal(out[k], ref[k]), k
+
+
+# ---------------------------------------------------------------------------
+# MXFP8: E4M3 elements, E8M0 scales, 64-element blocks
+# ---------------------------------------------------------------------------
+def test_e4m3_decode_table():
+    """Values fixed by the E4M3 (FN) format: bias 7, 3 mantissa bits, subnormals
+    below 2^-6, largest normal 448, NaN at S.1111.111, no infinities."""
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+             0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+             0xB8: -1.0, 0xFE: -448.0}
+    for code, val in known.items():
+        assert float(O.e4m3_decode(np.uint8(code))) == val, hex(code)
+    assert np.isnan(O.e4m3_decode(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+    v = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = v[~np.isnan(v)]
+    assert len(fin) == 254 and np.max(np.abs(fin)) == 448.0
+
+
+def _e4m3_table():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], dtype=np.uint8)
+    return codes, O.e4m3_decode(codes).astype(np.float64)
+
+
+def test_e4m3_encode_is_nearest_even_and_saturates():
+    """Brute force: the code chosen is the nearest finite E4M3 value; at an exact
+    midpoint the even mantissa wins; beyond 448 the value clamps to 448."""
+    codes, vals = _e4m3_table()
+    rng = np.random.default_rng(60)
+    x = np.concatenate([rng.normal(0, 40, 4000), rng.uniform(-2.0 ** -6, 2.0 ** -6, 500),
+                        [500.0, -1e6, 464.0, 449.0]])
+    # midpoints between neighbouring positive values
+    pos = np.sort(vals[vals > 0])
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([x, mids, -mids]).astype(np.float32)
+    got = O.e4m3_encode(x)
+    gv = O.e4m3_decode(got).astype(np.float64)
+    for xi, g, gc in zip(x.astype(np.float64), gv, got):
+        if abs(xi) >= 448.0:
+            assert g == np.sign(xi) * 448.0
+            continue
+        d = np.abs(vals - xi)
+        best = np.min(d)
+        assert abs(g - xi) == best, (xi, g)
+        ties = codes[d == best]
+        if len(ties) > 1:
+            assert (int(gc) & 1) == 0, (xi, hex(int(gc)))
+
+
+def test_e4m3_encode_round_trips_every_code():
+    codes, vals = _e4m3_table()
+    assert np.array_equal(O.e4m3_encode(vals.astype(np.float32)), codes)
+
+
+def test_mx_scale_rule_and_bounds():
+    """Block amax in [2^k, 2^(k+1)) gives scale 2^(k-8): the scaled block maximum
+    lands in [256, 512) and encodes to 256..448 (clamped above 448); every element
+    is within half a spacing of its scaled value."""
+    rng = np.random.default_rng(61)
+    n = (rng.normal(0, 1, (6, 256)) * np.exp2(rng.integers(-20, 20, (6, 1)))).astype(np.float32)
+    n[2, 64:128] = 0.0
+    q, s = O.mx_quant_rows(n)
+    assert q.shape == (6, 256) and s.shape == (6, 4)
+    nb = n.reshape(6, 4, 64).astype(np.float64)
+    for t in range(6):
+        for b in range(4):
+            blk = nb[t, b]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                assert s[t, b] == 0 and not q[t, 64 * b:64 * b + 64].any()
+                continue
+            k = int(np.floor(np.log2(amax)))
+            assert int(s[t, b]) == k - 8 + 127
+            X = 2.0 ** (k - 8)
+            dec = O.e4m3_decode(q[t, 64 * b:64 * b + 64]).astype(np.float64)
+            assert 256.0 <= np.max(np.abs(dec)) <= 448.0
+            scaled = blk / X
+            spacing = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(scaled), 1e-300))), -6) - 3)
+            err = np.abs(dec - scaled)
+            ok = (err <= spacing / 2) | ((np.abs(scaled) > 448.0) & (np.abs(dec) == 448.0))
+            assert ok.all()
+
+
+def test_mx_scaled_mm_exact_small_case():
+    """Exact rational sum of the scaled E4M3 products, rounded once to fp32."""
+    rng = np.random.default_rng(62)
+    T, N, K = 3, 4, 128
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    qx, qw = rng.choice(finite, (T, K)), rng.choice(finite, (N, K))
+    sx, sw = rng.integers(110, 140, (T, 2)).astype(np.uint8), rng.integers(110, 140, (N, 2)).astype(np.uint8)
+    y = O.mx_scaled_mm(qx, sx, qw, sw)
+    xf, wf = O.e4m3_decode(qx), O.e4m3_decode(qw)
+    for t in range(T):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                b = k // 64
+                acc += (Fraction(float(xf[t, k])) * Fraction(float(wf[n, k]))
+                        * Fraction(2) ** (int(sx[t, b]) - 127) * Fraction(2) ** (int(sw[n, b]) - 127))
+            assert y[t, n] == fraction_to_f32(acc), (t, n)
+
+
+def test_mx_scaled_mm_scale_acts_on_its_64_block():
+    """Raising one weight block's scale by one doubles exactly that block's share."""
+    rng = np.random.default_rng(63)
+    qx = O.e4m3_encode(rng.normal(0, 4, (2, 192)).astype(np.float32))
+    qw = O.e4m3_encode(rng.normal(0, 4, (3, 192)).astype(np.float32))
+    sx = np.full((2, 3), 127, np.uint8)
+    sw = np.full((3, 3), 127, np.uint8)
+    y0 = O.mx_scaled_mm(qx, sx, qw, sw).astype(np.float64)
+    sw2 = sw.copy()
+    sw2[:, 1] += 1
+    y1 = O.mx_scaled_mm(qx, sx, qw, sw2).astype(np.float64)
+    blk = O.e4m3_decode(qx)[:, 64:128].astype(np.float64) @ O.e4m3_decode(qw)[:, 64:128].astype(np.float64).T
+    assert np.allclose(y1 - y0, blk, rtol=1e-6, atol=1e-6 * np.abs(y0).max())
+
+
+def test_rmsnorm_linear_mxfp8_composes():
+    case = synthetic.norm_linear_case(4, 128, 8, seed=64)
+    x, g = bits(case["x"]), bits(case["gamma"])
+    rng = np.random.default_rng(65)
+    qw = O.e4m3_encode(rng.normal(0, 8, (8, 128)).astype(np.float32))
+    sw = np.full((8, 2), 120, np.uint8)
+    out = O.rmsnorm_linear_mxfp8(x, g, 1e-6, qw, sw)
+    n, r = O.rms_norm_rows(x, g, 1e-6)
+    q, s = O.mx_quant_rows(n)
+    assert np.array_equal(out["q"], q) and np.array_equal(out["x_scale"], s) and np.array_equal(out["rstd"], r)
+    assert np.array_equal(out["y32"], O.mx_scaled_mm(q, s, qw, sw))
