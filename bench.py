@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused RMSNorm+Linear TFLOP/s (TOP/s int8) and HBM GB/s, % of roofline"
-PEAK = {"bf16": 2500.0, "int8": 5000.0, "hbm": 8000.0}  # TFLOP/s, TOP/s, GB/s (MI355X dense)
+PEAK = {"bf16": 2500.0, "int8": 5000.0, "fp8": 5000.0, "hbm": 8000.0}  # TFLOP/s, TOP/s, GB/s (MI355X dense)
 CSRC = os.path.join(ROOT, "rmsnorm_linear_projection_amd", "csrc")
 
 WORKLOADS = {
@@ -53,6 +53,8 @@ WORKLOADS = {
                      desc="bf16 RMSNorm + Linear, T=8 K=256 N=128"),
     "int8_w8a8": dict(kind="int8", T=2048, K=4096, N=4096, bound="mfma", dtype="int8",
                       desc="RMSNorm -> per-token int8 quant -> int8 GEMM -> dequant"),
+    "mxfp8_qkv_T4096": dict(kind="mxfp8", T=4096, K=4096, N=6144, bound="mfma", dtype="fp8",
+                            desc="RMSNorm -> MX quant (E4M3, E8M0 per 64) -> MXFP8 scaled GEMM, QKV shape"),
     "mla_q_chain": dict(kind="chain", T=1024, K=7168, R=1536, N=24576, bound="mfma", dtype="bf16",
                         desc="x -> W_a[1536,7168] -> RMSNorm -> W_b[24576,1536]"),
     "mla_prolog": dict(kind="mla", T=1024, K=7168, R=1536, Rkv=512, N=24576, bound="mfma", dtype="bf16",
@@ -64,6 +66,7 @@ DEFAULT = "preattn_qkv_T4096"
 KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.cuh", "gemm_bf16.hip", "gemm_int8.hip", "common.cuh"],
     "small_m": ["small_m.hip", "common.cuh"],
+    "gemm_mx": ["gemm_mx.hip", "common.cuh"],
     "skinny": ["skinny.hip", "common.cuh"],
 }
 
@@ -87,6 +90,8 @@ def bytes_of(w):
         return T * K * 2 * (3 if w.get("add") else 1) + K * 2 + N * K * 2 + T * N * 2
     if w["kind"] == "int8":
         return T * K * 2 + K * 2 + N * K + N * 4 + T * N * 2
+    if w["kind"] == "mxfp8":
+        return T * K * 2 + K * 2 + N * K + N * (K // 64) + T * N * 2
     if w["kind"] == "fp32w":
         return T * K * 2 + N * K * 4 + T * N * 4
     R = w["R"] + w.get("Rkv", 0)  # the KV branch adds its weight rows, gamma and normed outputs
@@ -134,6 +139,7 @@ class Setup:
             "bf16": lambda: synthetic.norm_linear_case(w["T"], w["K"], w["N"], name=name),
             "fp32w": lambda: synthetic.norm_linear_case(w["T"], w["K"], w["N"], gamma=False, w_dtype="fp32", name=name),
             "int8": lambda: synthetic.int8_case(w["T"], w["K"], w["N"], name=name),
+            "mxfp8": lambda: synthetic.mxfp8_qkv(w["T"]),
             "chain": lambda: synthetic.chain_case(w["T"], w["K"], w["R"], w["N"], name=name),
             "preattn": lambda: synthetic.preattn_block(w["T"]),
             "mla": lambda: synthetic.mla_prolog(),
@@ -177,6 +183,15 @@ class Setup:
                 self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
                 self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
                 self.kern_units = ("bf16", flops_of(w))
+        elif kind == "mxfp8":
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(rnl.workspace_bytes("mxfp8", T, K, N), dtype=torch.uint8, device=dev)
+            self.step = lambda i: rnl.rmsnorm_linear_mxfp8(t["x"], t["gamma"], eps, t["Wq"], t["w_scale"], y=y,
+                                                           workspace=ws)
+            xq, xs = rnl.rms_norm_quant_mxfp8(t["x"], t["gamma"], eps)
+            self.kernel, self.kernel_key = "gemm_mx_kernel", "gemm_mx"
+            self.kern = lambda i: rnl.linear_mxfp8(xq, xs, t["Wq"], t["w_scale"], y=y)
+            self.kern_units = ("fp8", flops_of(w))
         elif kind == "preattn":
             Hq, Hkv, D = w["Hq"], w["Hkv"], w["D"]
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
@@ -318,6 +333,8 @@ def cpu_baseline(setup, target_s=8.0):
             O.rmsnorm_linear_bf16(x, g, c.eps, bits(c["W"]))
         elif kind == "fp32w":
             O.rmsnorm_linear_fp32w(x, g, c.eps, c["W"].numpy())
+        elif kind == "mxfp8":
+            O.rmsnorm_linear_mxfp8(x, g, c.eps, c["Wq"].numpy(), c["w_scale"].numpy())
         elif kind == "int8":
             O.rmsnorm_linear_int8(x, g, c.eps, c["Wq"].numpy(), c["w_scale"].numpy())
         elif kind == "mla":
@@ -405,7 +422,7 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
 
 
 COPY_BYTES = 256 << 20  # size of the plain device copy that calibrates FETCH_SIZE / WRITE_SIZE
-KERNEL_MATCH = {"gemm": "gemm_nt_kernel", "small_m": "small_m_kernel", "skinny": "skinny_"}
+KERNEL_MATCH = {"gemm": "gemm_nt_kernel", "small_m": "small_m_kernel", "skinny": "skinny_", "gemm_mx": "gemm_mx_kernel"}
 
 
 def copy_calibration(steps=5):
@@ -447,8 +464,12 @@ def record_counters(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Fold two rocprofv3 --pmc runs of a workload (FETCH_SIZE, then WRITE_SIZE)
     and the same two counters of the calibration copy into profiles/counters.json."""
     w = WORKLOADS[name]
-    key = "skinny" if w["kind"] == "fp32w" else ("small_m" if w["kind"] in ("bf16", "preattn") and w["T"] <= 16
-                                                 else "gemm")
+    if w["kind"] == "fp32w":
+        key = "skinny"
+    elif w["kind"] == "mxfp8":
+        key = "gemm_mx"
+    else:
+        key = "small_m" if w["kind"] in ("bf16", "preattn") and w["T"] <= 16 else "gemm"
     pair = key == "skinny"
     fk, nf = _counter_kib(fetch_csv, KERNEL_MATCH[key], "FETCH_SIZE", pair)
     wk, nw = _counter_kib(write_csv, KERNEL_MATCH[key], "WRITE_SIZE", pair)

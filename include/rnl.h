@@ -171,6 +171,36 @@ RNL_API int add_rmsnorm_linear_int8(const void* x, const void* residual, void* x
 RNL_API size_t add_rmsnorm_linear_int8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype);
 
 /*
+ * rmsnorm_linear_mxfp8 -- fused RMSNorm -> MX quantisation -> MXFP8 scaled GEMM
+ * (AT-10 with AT-09's MXFP8 mode).
+ *
+ * AT-10 page, section 4: in MXFP8 mode the projection is one scaled matmul of
+ * fp8 operands with their scales, accumulating in FP32; the SK-14 page gives
+ * the MXFP8 layout: E4M3FN data, E8M0 scales, one scale per 64 elements.  The
+ * fp32 normed rows (as in rmsnorm_linear_int8) are quantised per block of 64
+ * consecutive k: scale X = 2^e, e = floor(log2(amax)) - 8 clamped to
+ * [-127, 127] (-127 for an all-zero block), element = the E4M3 value nearest
+ * to n / X (ties to even, clamped to +-448, zero as +0).  Then
+ *   y[t, n] = sum over blocks b of X[t, b] * Xw[n, b] * sum_{k in b} q[t, k] * Wq[n, k]
+ * accumulated in fp32, written as bf16 (RNL_BF16) or fp32 (RNL_FP32).
+ *
+ *   x, gamma, eps  as in rmsnorm_linear_bf16.
+ *   Wq        [N, K] E4M3 bytes; w_scale [N, K/64] E8M0 bytes (2^(code - 127)).
+ *   xq_out    [T, K] E4M3 bytes, or NULL; x_scale_out [T, K/64] E8M0, or NULL.
+ *   rstd_out  [T] fp32, or NULL.
+ *   K must be a multiple of 64.  Codes 0x7F / 0xFF (E4M3) and 255 (E8M0) are
+ *   NaN and make the affected outputs NaN.
+ *
+ * Errors: as rmsnorm_linear_bf16 (Wq and w_scale are required).
+ */
+RNL_API int rmsnorm_linear_mxfp8(const void* x, const void* gamma, float eps, const uint8_t* Wq,
+                                 const uint8_t* w_scale, void* y, int out_dtype, uint8_t* xq_out,
+                                 uint8_t* x_scale_out, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+RNL_API size_t rmsnorm_linear_mxfp8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype);
+
+/*
  * norm_proj_chain -- two-stage low-rank projection q_a_proj -> RMSNorm -> q_b_proj.
  *
  * AT-10 page, section 5 (MLAProlog query branch: bf16 product with the
@@ -318,6 +348,22 @@ RNL_API int linear_bf16(const void* a, const void* W, void* y, int out_dtype, in
 RNL_API int linear_int8(const int8_t* xq, const float* x_scale, const int8_t* Wq,
                         const float* w_scale, void* y, int out_dtype, int64_t M, int64_t K,
                         int64_t N, void* stream);
+
+/*
+ * rms_norm_quant_mxfp8 -- AT-03 followed by the MX quantisation of
+ * rmsnorm_linear_mxfp8: xq [T, K] E4M3 and x_scale [T, K/64] E8M0 (required),
+ * rstd_out [T] or NULL.  K must be a multiple of 64.
+ */
+RNL_API int rms_norm_quant_mxfp8(const void* x, const void* gamma, float eps, uint8_t* xq, uint8_t* x_scale,
+                                 float* rstd_out, int64_t T, int64_t K, void* stream);
+
+/*
+ * linear_mxfp8 -- AT-09 Linear Projection, MXFP8 mode: the scaled product of
+ * rmsnorm_linear_mxfp8 on given MX operands, xq [M, K] / x_scale [M, K/64] and
+ * Wq [N, K] / w_scale [N, K/64]; y [M, N] bf16 or fp32.
+ */
+RNL_API int linear_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const uint8_t* Wq, const uint8_t* w_scale,
+                         void* y, int out_dtype, int64_t M, int64_t K, int64_t N, void* stream);
 
 /* Static description of a status code. */
 RNL_API const char* rnl_status_str(int status);

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   (fp32 weights: the normed rows stay fp32, the large-reduction split-K path);
 * :func:`rmsnorm_linear_int8` -- RMSNorm -> per-token int8 quant -> int8 GEMM ->
   dequant;
+* :func:`rmsnorm_linear_mxfp8` -- RMSNorm -> MX quantisation (E4M3, one E8M0 scale
+  per 64 values) -> MXFP8 scaled GEMM;
 * :func:`add_rmsnorm_linear_bf16`, :func:`add_rmsnorm_linear_int8` -- the same
   with the residual add in front (x_add = x + residual, also returned);
 * :func:`preattn_qkv_bf16` -- (residual add ->) RMSNorm -> fused QKV projection ->
@@ -38,6 +40,9 @@ __all__ = [
     "head_rms_norm_bf16",
     "rms_norm_bf16",
     "rms_norm_quant_int8",
+    "rmsnorm_linear_mxfp8",
+    "rms_norm_quant_mxfp8",
+    "linear_mxfp8",
     "linear_bf16",
     "linear_int8",
     "workspace_bytes",
@@ -122,6 +127,14 @@ def load_library() -> ctypes.CDLL:
     lib.mla_prolog_bf16.restype = ctypes.c_int
     lib.mla_prolog_bf16_workspace_bytes.argtypes = [_c_i64] * 5
     lib.mla_prolog_bf16_workspace_bytes.restype = ctypes.c_size_t
+    lib.rmsnorm_linear_mxfp8.argtypes = lib.rmsnorm_linear_int8.argtypes
+    lib.rmsnorm_linear_mxfp8.restype = ctypes.c_int
+    lib.rmsnorm_linear_mxfp8_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.c_int]
+    lib.rmsnorm_linear_mxfp8_workspace_bytes.restype = ctypes.c_size_t
+    lib.rms_norm_quant_mxfp8.argtypes = [_c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p]
+    lib.rms_norm_quant_mxfp8.restype = ctypes.c_int
+    lib.linear_mxfp8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
+    lib.linear_mxfp8.restype = ctypes.c_int
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -181,6 +194,8 @@ def workspace_bytes(kind: str, *shape, w_dtype=torch.bfloat16, out_dtype=torch.b
         return int(lib.add_rmsnorm_linear_bf16_workspace_bytes(*shape, _DTYPE_CODE[w_dtype], _DTYPE_CODE[out_dtype]))
     if kind == "int8":
         return int(lib.rmsnorm_linear_int8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
+    if kind == "mxfp8":
+        return int(lib.rmsnorm_linear_mxfp8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
     if kind == "add_int8":
         return int(lib.add_rmsnorm_linear_int8_workspace_bytes(*shape, _DTYPE_CODE[out_dtype]))
     if kind == "chain":
@@ -342,6 +357,84 @@ def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None,
                                  _ptr(rstd_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
     _check(rc)
     return y, qr_out
+
+
+def rmsnorm_linear_mxfp8(x, gamma, eps, Wq, w_scale, out_dtype=torch.bfloat16, xq_out=None, x_scale_out=None,
+                         rstd_out=None, y=None, workspace=None):
+    """AT-10 with AT-09's MXFP8 mode: RMSNorm -> MX quantisation of the normed rows
+    (E4M3 codes, one E8M0 scale per 64 values) -> scaled product with Wq [N, K]
+    (uint8 E4M3) and w_scale [N, K/64] (uint8 E8M0), fp32 accumulation."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(Wq, "Wq", torch.uint8, 2)
+    _dev_tensor(w_scale, "w_scale", torch.uint8, 2)
+    _dev_tensor(xq_out, "xq_out", torch.uint8)
+    _dev_tensor(x_scale_out, "x_scale_out", torch.uint8)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    N = Wq.shape[0]
+    _shape(Wq.shape[1] == K, "Wq must be [N, K]")
+    _shape(K % 64 == 0 and tuple(w_scale.shape) == (N, K // 64), "w_scale must be [N, K/64]")
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(xq_out is None or xq_out.numel() == T * K, "xq_out must be [T, K]")
+    _shape(x_scale_out is None or x_scale_out.numel() == T * (K // 64), "x_scale_out must be [T, K/64]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    ocode = _DTYPE_CODE[out_dtype]
+    if y is None:
+        y = torch.empty((T, N), dtype=out_dtype, device=x.device)
+    _dev_tensor(y, "y", out_dtype)
+    _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
+    with torch.cuda.device(x.device):
+        need = int(lib.rmsnorm_linear_mxfp8_workspace_bytes(T, K, N, ocode))
+        if xq_out is not None and x_scale_out is not None:
+            need = 0
+        ws, ws_bytes = _workspace(need, x.device, workspace)
+        rc = lib.rmsnorm_linear_mxfp8(_ptr(x), _ptr(gamma), float(eps), _ptr(Wq), _ptr(w_scale), _ptr(y), ocode,
+                                      _ptr(xq_out), _ptr(x_scale_out), _ptr(rstd_out), T, K, N, _ptr(ws), ws_bytes,
+                                      _stream(x.device))
+    _check(rc)
+    return y
+
+
+def rms_norm_quant_mxfp8(x, gamma, eps, xq=None, x_scale=None, rstd_out=None):
+    """RMSNorm + MX quantisation: returns (xq [T, K] E4M3 bytes, x_scale [T, K/64] E8M0 bytes)."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    _shape(K % 64 == 0, "K must be a multiple of 64")
+    xq = torch.empty((T, K), dtype=torch.uint8, device=x.device) if xq is None else xq
+    x_scale = torch.empty((T, K // 64), dtype=torch.uint8, device=x.device) if x_scale is None else x_scale
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(x_scale, "x_scale", torch.uint8)
+    _shape(xq.numel() == T * K and x_scale.numel() == T * (K // 64), "xq / x_scale sizes")
+    with torch.cuda.device(x.device):
+        rc = lib.rms_norm_quant_mxfp8(_ptr(x), _ptr(gamma), float(eps), _ptr(xq), _ptr(x_scale), _ptr(rstd_out), T,
+                                      K, _stream(x.device))
+    _check(rc)
+    return xq, x_scale
+
+
+def linear_mxfp8(xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, y=None):
+    """AT-09 MXFP8 mode on given MX operands: y [M, N] bf16 or fp32."""
+    lib = load_library()
+    for t, n in ((xq, "xq"), (x_scale, "x_scale"), (Wq, "Wq"), (w_scale, "w_scale")):
+        _dev_tensor(t, n, torch.uint8, 2)
+    M, K = xq.shape
+    N = Wq.shape[0]
+    _shape(Wq.shape[1] == K and K % 64 == 0, "Wq must be [N, K], K a multiple of 64")
+    _shape(tuple(x_scale.shape) == (M, K // 64) and tuple(w_scale.shape) == (N, K // 64), "scales must be [*, K/64]")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _dev_tensor(y, "y", out_dtype)
+    _shape(tuple(y.shape) == (M, N), "y must be [M, N]")
+    with torch.cuda.device(xq.device):
+        rc = lib.linear_mxfp8(_ptr(xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), _ptr(y), _DTYPE_CODE[out_dtype], M, K,
+                              N, _stream(xq.device))
+    _check(rc)
+    return y
 
 
 def mla_prolog_bf16(x, W_akv, R, gamma_cq, gamma_ckv, eps, W_b, qr_out=None, kv_out=None, y=None, rstd_q_out=None,

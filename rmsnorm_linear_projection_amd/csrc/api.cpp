@@ -352,6 +352,46 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
                     "chain stage-2 projection launch");
 }
 
+size_t rmsnorm_linear_mxfp8_workspace_bytes(int64_t T, int64_t K, int64_t N, int out_dtype) {
+  (void)N;
+  (void)out_dtype;
+  if (T <= 0 || K <= 0) return 0;
+  return align256((size_t)T * (size_t)K) + align256((size_t)T * (size_t)(K / 64));
+}
+
+int rmsnorm_linear_mxfp8(const void* x, const void* gamma, float eps, const uint8_t* Wq, const uint8_t* w_scale,
+                         void* y, int out_dtype, uint8_t* xq_out, uint8_t* x_scale_out, float* rstd_out, int64_t T,
+                         int64_t K, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || Wq == nullptr || w_scale == nullptr || y == nullptr)
+    return fail(RNL_ERR_NULL, "x, Wq, w_scale and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK));
+  if (K % 64 != 0) return fail(RNL_ERR_SHAPE, "MXFP8 needs K %% 64 == 0 (K=%lld)", (long long)K);
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(Wq, 16, "Wq");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(xq_out, 16, "xq_out");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(workspace, 256, "workspace");
+  const size_t q_bytes = xq_out ? 0 : align256((size_t)T * (size_t)K);
+  const size_t s_bytes = x_scale_out ? 0 : align256((size_t)T * (size_t)(K / 64));
+  const size_t need = q_bytes + s_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(RNL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* q = xq_out ? xq_out : static_cast<uint8_t*>(workspace);
+  uint8_t* xs = x_scale_out ? x_scale_out : static_cast<uint8_t*>(workspace) + q_bytes;
+  const hipError_t e = rnl::launch_norm_rows_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma),
+                                                eps, T, K, q, xs, rstd_out, s);
+  if (e != hipSuccess) return hip_status(e, "norm+MX quant launch");
+  return hip_status(rnl::launch_gemm_mx(q, xs, Wq, w_scale, y, out_dtype == RNL_FP32 ? rnl::OUT_F32 : rnl::OUT_BF16,
+                                        T, N, K, s),
+                    "MXFP8 GEMM launch");
+}
+
 size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N) {
   (void)N;
   if (T <= 0 || R <= 0 || Rkv <= 0 || K <= 0) return 0;
@@ -525,6 +565,36 @@ int linear_bf16(const void* a, const void* W, void* y, int out_dtype, int64_t M,
                                  out_dtype == RNL_BF16 ? rnl::OUT_BF16 : rnl::OUT_F32, M, N, K,
                                  static_cast<hipStream_t>(stream)),
                     "bf16 projection launch");
+}
+
+int rms_norm_quant_mxfp8(const void* x, const void* gamma, float eps, uint8_t* xq, uint8_t* x_scale,
+                         float* rstd_out, int64_t T, int64_t K, void* stream) {
+  if (x == nullptr || xq == nullptr || x_scale == nullptr) return fail(RNL_ERR_NULL, "x, xq and x_scale are required");
+  RNL_TRY(check_dims(T, K, 1, kMaxK));
+  if (K % 64 != 0) return fail(RNL_ERR_SHAPE, "MXFP8 needs K %% 64 == 0 (K=%lld)", (long long)K);
+  RNL_TRY(check_eps(eps));
+  RNL_ALIGN(x, 16, "x");
+  RNL_ALIGN(gamma, 16, "gamma");
+  RNL_ALIGN(xq, 16, "xq");
+  RNL_ALIGN(rstd_out, 4, "rstd_out");
+  return hip_status(rnl::launch_norm_rows_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma), eps,
+                                             T, K, xq, x_scale, rstd_out, static_cast<hipStream_t>(stream)),
+                    "norm+MX quant launch");
+}
+
+int linear_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const uint8_t* Wq, const uint8_t* w_scale, void* y,
+                 int out_dtype, int64_t M, int64_t K, int64_t N, void* stream) {
+  if (xq == nullptr || x_scale == nullptr || Wq == nullptr || w_scale == nullptr || y == nullptr)
+    return fail(RNL_ERR_NULL, "xq, x_scale, Wq, w_scale and y are required");
+  RNL_TRY(check_dims(M, K, N, kMaxK));
+  if (K % 64 != 0) return fail(RNL_ERR_SHAPE, "MXFP8 needs K %% 64 == 0 (K=%lld)", (long long)K);
+  if (out_dtype != RNL_BF16 && out_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "out_dtype must be RNL_BF16 or RNL_FP32");
+  RNL_ALIGN(xq, 16, "xq");
+  RNL_ALIGN(Wq, 16, "Wq");
+  RNL_ALIGN(y, 16, "y");
+  return hip_status(rnl::launch_gemm_mx(xq, x_scale, Wq, w_scale, y, out_dtype == RNL_FP32 ? rnl::OUT_F32 : rnl::OUT_BF16,
+                                        M, N, K, static_cast<hipStream_t>(stream)),
+                    "MXFP8 GEMM launch");
 }
 
 int linear_int8(const int8_t* xq, const float* x_scale, const int8_t* Wq, const float* w_scale, void* y,

@@ -1,0 +1,275 @@
+// MXFP8 GEMM for the projection step (gfx950): C[M,N] = A[M,K] . B[N,K]^T with
+// E4M3 operands and one E8M0 scale per 64 consecutive k of every row of A (the
+// MX-quantised normed activations, scales As[M, K/64]) and of B (the weight,
+// scales Bs[N, K/64]) -- AT-09's MXFP8 mode, the scaled product of the AT-10
+// page section 4, accumulated in fp32.
+//
+// One k-step is 128 bytes (= 128 k) of every tile row and one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per 16 x 16 output block.  The instruction
+// takes from lane l (row l & 15, group g = l >> 4) the 16-byte chunks g and
+// 4 + g of its row's k-step (k = 16g..16g+15 and 64+16g..64+16g+15), and the
+// scale of the 32-wide k block g of its row; a 64-block of the pages is two
+// such blocks, so lane group g passes the scale of 64-block 2 kt + g / 2.  The
+// scale registers are byte loads from global memory, issued one k-step ahead.
+//
+// Staging follows the bf16 / int8 GEMM: global -> LDS by direct-to-LDS DMA,
+// 128-byte rows with 16-byte chunk c of row r at slot c ^ (r & 7), a 2 x 2 grid
+// of wavefronts, XCD-aware tile order.  With two LDS stages every wait on the
+// DMA is a wait for all loads (vmcnt 0), which also covers the scale loads.
+// Per k-step, phase A issues the MFMAs of the first half of the activation
+// fragments while the second half is read; after the barrier, phase B issues
+// the rest while the next k-step's first half and weight fragments are read
+// (weight fragments are double-buffered) and the free stage is refilled.
+#include "common.cuh"
+#include "launch.h"
+
+namespace rnl {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt unchanged (gfx9 encoding)
+#define RNL_MX_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ uint32_t buf_load_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+template <int BM, int BN, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ As,
+                    const uint8_t* __restrict__ Bs, void* __restrict__ C, int M, int N, int K, int tiles_m,
+                    int tiles_n) {
+  constexpr int NST = 2;
+  constexpr int GROUP_M = 4;
+  constexpr int ROWB = 128;
+  constexpr int A_CH = BM * 8 / 256;  // DMA instructions per wave and stage for A
+  constexpr int B_CH = BN * 8 / 256;
+  constexpr int LPS = A_CH + B_CH;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NMI = WM / 16, NNI = WN / 16;
+  constexpr int HM = NMI / 2;  // activation fragments per phase
+  constexpr int STAGE = (BM + BN) * ROWB;
+  static_assert(BM % 64 == 0 && BN % 32 == 0, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // workgroup -> tile: contiguous range per XCD, grouped along M inside it
+  const int bid = blockIdx.x, nwg = gridDim.x;
+  const int tile = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int per_group = GROUP_M * tiles_n;
+  const int group = tile / per_group;
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = tile - group * per_group;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t kbytes = (uint32_t)K;
+  const int nk = (K + ROWB - 1) / ROWB;
+  const int kb64 = K >> 6;  // scale bytes per row
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * kbytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * kbytes);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As + (size_t)m0 * kb64, (uint32_t)(rows_a * kb64));
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(Bs + (size_t)n0 * kb64, (uint32_t)(rows_b * kb64));
+
+  // DMA: one instruction fills 8 consecutive tile rows (1 KiB); lane -> row lane/8, slot lane%8
+  const int drow = lane >> 3, dslot = lane & 7;
+  const int dchunk = dslot ^ drow;
+  const uint32_t d_goff = (uint32_t)drow * kbytes + (uint32_t)dchunk * 16u;
+  auto dload_one = [&](int kt, int buf, int g) {
+    const uint32_t kb = (uint32_t)kt * ROWB;
+    const bool live = kt < nk && kb + (uint32_t)dchunk * 16u < kbytes;
+    char* s = smem + buf * STAGE;
+    if (g < A_CH) {
+      const int j = wave * A_CH + g;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(s + j * 1024), 16,
+          live ? d_goff + (uint32_t)j * 8u * kbytes + kb : kOOB, 0, 0, 0);
+    } else {
+      const int j = wave * B_CH + (g - A_CH);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(s + BM * ROWB + j * 1024), 16,
+          live ? d_goff + (uint32_t)j * 8u * kbytes + kb : kOOB, 0, 0, 0);
+    }
+  };
+
+  // fragment reads: operand row = lane & 15, chunks (lane >> 4) and 4 + (lane >> 4)
+  const int frow = lane & 15, fg = lane >> 4;
+  const uint32_t foff0 = (uint32_t)frow * ROWB + (uint32_t)((fg ^ (frow & 7)) * 16);
+  const uint32_t foff1 = (uint32_t)frow * ROWB + (uint32_t)(((4 + fg) ^ (frow & 7)) * 16);
+  auto lds16 = [&](int buf, int row0, uint32_t fo) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(smem + buf * STAGE + row0 * ROWB + fo);
+  };
+  struct Frag {
+    u32x4 lo, hi;
+  };
+  Frag a[NMI];
+  struct WFrag {
+    Frag f[NNI];
+  };
+  WFrag b0, b1;
+  struct Scales {
+    uint32_t w[NNI], x[NMI];
+  };
+  Scales s0, s1;
+
+  auto read_a = [&](int buf, int i) {
+    const int r0 = wm * WM + i * 16;
+    a[i].lo = lds16(buf, r0, foff0);
+    a[i].hi = lds16(buf, r0, foff1);
+  };
+  auto read_b = [&](WFrag& bf, int buf, int j) {
+    const int r0 = BM + wn * WN + j * 16;
+    bf.f[j].lo = lds16(buf, r0, foff0);
+    bf.f[j].hi = lds16(buf, r0, foff1);
+  };
+  // scale bytes of k-step kt for this lane's rows (64-block 2 kt + g / 2; past K: 1.0)
+  auto load_scales = [&](Scales& sc, int kt) {
+    const int blk = 2 * kt + (fg >> 1);
+    const bool in_k = blk < kb64;
+#pragma unroll
+    for (int j = 0; j < NNI; ++j) {
+      const uint32_t o = (uint32_t)((wn * WN + j * 16 + frow) * kb64 + blk);
+      sc.w[j] = in_k ? buf_load_u8(rsb, o) : 127u;
+    }
+#pragma unroll
+    for (int i = 0; i < NMI; ++i) {
+      const uint32_t o = (uint32_t)((wm * WM + i * 16 + frow) * kb64 + blk);
+      sc.x[i] = in_k ? buf_load_u8(rsa, o) : 127u;
+    }
+  };
+
+  f32x4 acc[NMI][NNI];
+#pragma unroll
+  for (int i = 0; i < NMI; ++i)
+#pragma unroll
+    for (int j = 0; j < NNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const WFrag& bf, const Scales& sc, int i, int j) {
+    const i32x8 wv = __builtin_bit_cast(i32x8, __builtin_shufflevector(bf.f[j].lo, bf.f[j].hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    const i32x8 xv = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[i].lo, a[i].hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv, acc[i][j], 0, 0, 0, (int)sc.w[j], 0,
+                                                                 (int)sc.x[i]);
+  };
+
+  // one k-step: bc / sc hold its weight fragments and scales, bn / sn receive the next k-step's
+  auto kstep = [&](WFrag& bc, WFrag& bn, Scales& sc, Scales& sn, int kt) {
+    const int slot = kt & 1, nslot = slot ^ 1;
+    // phase A: MFMAs of activation fragments [0, HM); read [HM, NMI) of this k-step
+    load_scales(sn, kt + 1);
+#pragma unroll
+    for (int i = 0; i < HM; ++i) {
+      read_a(slot, HM + i);
+#pragma unroll
+      for (int j = 0; j < NNI; ++j) mma(bc, sc, i, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // k-step kt + 1 has landed and every wave has finished reading stage `slot`
+    RNL_MX_WAIT_VM_LGKM0(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // phase B: refill `slot` with k-step kt + 2; MFMAs of [HM, NMI); read the next k-step's
+    // first half and weight fragments from stage nslot
+#pragma unroll
+    for (int g = 0; g < LPS; ++g) dload_one(kt + 2, slot, g);
+#pragma unroll
+    for (int i = 0; i < HM; ++i) {
+      read_a(nslot, i);
+      if (i < NNI) read_b(bn, nslot, i);
+#pragma unroll
+      for (int j = 0; j < NNI; ++j) mma(bc, sc, HM + i, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = HM; j < NNI; ++j) read_b(bn, nslot, j);
+  };
+
+  // prologue: both stages, the scales of k-step 0, the first half and weights of k-step 0
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int g = 0; g < LPS; ++g) dload_one(st, st, g);
+  load_scales(s0, 0);
+  RNL_MX_WAIT_VM_LGKM0(0);
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < HM; ++i) read_a(0, i);
+#pragma unroll
+  for (int j = 0; j < NNI; ++j) read_b(b0, 0, j);
+
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(b0, b1, s0, s1, kt);
+    kstep(b1, b0, s1, s0, kt + 1);
+  }
+  if (kt < nk) kstep(b0, b1, s0, s1, kt);
+  RNL_MX_WAIT_VM_LGKM0(0);
+
+  // epilogue: lane holds C[m][n .. n+3]
+  const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < NMI; ++i) {
+    const int m = m0 + wm * WM + i * 16 + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NNI; ++j) {
+      const int n = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
+      if (n >= N) continue;
+      const size_t off = (size_t)m * (size_t)N + (size_t)n;
+      const bool full = vec_ok && (n + 3 < N);
+      const f32x4 v = acc[i][j];
+      if constexpr (OUT_BF16) {
+        uint16_t* c = static_cast<uint16_t*>(C) + off;
+        if (full) {
+          *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        } else {
+          for (int r = 0; r < 4 && n + r < N; ++r) c[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xFFFFu);
+        }
+      } else {
+        float* c = static_cast<float*>(C) + off;
+        if (full) {
+          *reinterpret_cast<f32x4*>(c) = v;
+        } else {
+          for (int r = 0; r < 4 && n + r < N; ++r) c[r] = v[r];
+        }
+      }
+    }
+  }
+}
+
+#undef RNL_MX_WAIT_VM_LGKM0
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <int BM, int BN>
+hipError_t launch_mx_tile(const uint8_t* A, const uint8_t* B, const uint8_t* As, const uint8_t* Bs, void* C,
+                          bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const int tiles_m = (int)cdiv64(M, BM), tiles_n = (int)cdiv64(N, BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
+  if (out_bf16)
+    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, true>), grid, block, 0, s, A, B, As, Bs, C, (int)M, (int)N, (int)K,
+                       tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false>), grid, block, 0, s, A, B, As, Bs, C, (int)M, (int)N,
+                       (int)K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
+                          int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const bool ob = out_kind == OUT_BF16;
+  // largest tile that still gives every CU a workgroup
+  if (cdiv64(M, 256) * cdiv64(N, 192) >= 256) return launch_mx_tile<256, 192>(A, B, As, Bs, C, ob, M, N, K, s);
+  if (cdiv64(M, 256) * cdiv64(N, 128) >= 256) return launch_mx_tile<256, 128>(A, B, As, Bs, C, ob, M, N, K, s);
+  if (cdiv64(M, 128) * cdiv64(N, 256) >= 256) return launch_mx_tile<128, 256>(A, B, As, Bs, C, ob, M, N, K, s);
+  return launch_mx_tile<128, 128>(A, B, As, Bs, C, ob, M, N, K, s);
+}
+
+}  // namespace rnl

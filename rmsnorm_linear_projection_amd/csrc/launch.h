@@ -68,6 +68,16 @@ hipError_t launch_gemm_int8(const int8_t* A, const int8_t* B, void* C, int out_k
                             const float* xs, const float* ws, int64_t M, int64_t N, int64_t K,
                             hipStream_t s);
 
+// RMSNorm, then MX quantisation of the fp32 normed rows: q_out [T, K] E4M3 codes,
+// s_out [T, K/64] E8M0 scales (one per 64 consecutive values).  K % 64 == 0.
+hipError_t launch_norm_rows_mx(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T, int64_t K,
+                               uint8_t* q_out, uint8_t* s_out, float* rstd_out, hipStream_t s);
+
+// MXFP8 GEMM: C[M,N] = sum over 64-blocks of As * Bs * (A . B^T) with E4M3
+// A[M,K], B[N,K] and E8M0 scales As[M,K/64], Bs[N,K/64]; C bf16 or fp32.
+hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs, void* C,
+                          int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 // C[M,N] = A[M,K] . W[N,K]^T for M <= 16 (weight streaming), bf16 or fp32 out.
 // R = weight rows per workgroup (a multiple of 4, at most 32), or 0 to let
 // small_m_rows(N) spread the rows evenly over the compute units.

@@ -28,7 +28,7 @@ EPS = 1e-6
 
 # stream ids: one per tensor role, so that adding a tensor never shifts another
 _S_X, _S_GAMMA, _S_W, _S_WSCALE, _S_WA, _S_WB, _S_RES = 1, 2, 3, 4, 5, 6, 7
-_S_GQ, _S_GK, _S_ANGLE, _S_WKV, _S_GKV = 8, 9, 10, 11, 12
+_S_GQ, _S_GK, _S_ANGLE, _S_WKV, _S_GKV, _S_WSC = 8, 9, 10, 11, 12, 13
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -127,6 +127,30 @@ def preattn_case(T: int, K: int, Hq: int, Hkv: int, D: int, seed: int = 0, resid
     return case
 
 
+def e4m3_codes(shape, std: float, seed: int, stream: int) -> torch.Tensor:
+    """E4M3 bytes of N(0, std^2) draws (torch's float8_e4m3fn conversion), as uint8."""
+    t = torch.randn(tuple(shape), generator=_gen(seed, stream), dtype=torch.float32)
+    return (t * std).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
+def e8m0_codes(shape, lo: int, hi: int, seed: int, stream: int) -> torch.Tensor:
+    """E8M0 scale bytes uniform in [lo, hi] (scale 2^(code - 127)), as uint8."""
+    return torch.randint(lo, hi + 1, tuple(shape), generator=_gen(seed, stream), dtype=torch.int32).to(torch.uint8)
+
+
+def mxfp8_case(T: int, K: int, N: int, seed: int = 0, gamma: bool = True, name: str | None = None) -> Case:
+    """x[T,K] bf16, optional gamma[K], MXFP8 weight Wq[N,K] (E4M3 of N(0, 8^2)) with
+    E8M0 scales w_scale[N, K/64] in 2^-10 .. 2^-8, so that a weight value has a
+    standard deviation near 1/sqrt(4096)."""
+    t = {
+        "x": normal((T, K), 1.0, seed, _S_X),
+        "gamma": uniform((K,), 0.5, 1.5, seed, _S_GAMMA) if gamma else None,
+        "Wq": e4m3_codes((N, K), 8.0, seed, _S_W),
+        "w_scale": e8m0_codes((N, K // 64), 117, 119, seed, _S_WSC),
+    }
+    return Case(name or f"mxfp8_T{T}_K{K}_N{N}", t, EPS, {"T": T, "K": K, "N": N})
+
+
 def chain_case(T: int, K: int, R: int, N: int, seed: int = 0, gamma: bool = True,
                name: str | None = None) -> Case:
     """x[T,K] -> W_a[R,K] -> RMSNorm(R, gamma) -> W_b[N,R]; all bf16."""
@@ -179,6 +203,11 @@ def int8_w8a8(seed: int = 0) -> Case:
 def mla_q_chain(seed: int = 0) -> Case:
     """Low-rank query chain x[1024,7168] -> W_a[1536,7168] -> norm -> W_b[24576,1536]."""
     return chain_case(1024, 7168, 1536, 24576, seed, name="mla_q_chain_T1024_K7168_R1536_N24576")
+
+
+def mxfp8_qkv(T: int = 4096, seed: int = 0) -> Case:
+    """Pre-attention norm + fused QKV projection in MXFP8, K=4096, N=6144."""
+    return mxfp8_case(T, 4096, 6144, seed, name=f"mxfp8_qkv_T{T}_K4096_N6144")
 
 
 def mla_prolog(seed: int = 0) -> Case:

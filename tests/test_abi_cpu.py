@@ -265,6 +265,37 @@ def test_mla_workspace(lib):
     assert lib.mla_prolog_bf16_workspace_bytes(1024, 7168, 1536, 512, 24576) >= 2 * 1024 * 2048 * 4
 
 
+def mx_call(lib, x=FAKE, g=NULL, eps=1e-6, Wq=FAKE, ws=FAKE, y=FAKE, od=1, xq=NULL, xs=NULL, rstd=NULL, T=4, K=128,
+            N=8, wsp=FAKE, wsb=1 << 30):
+    return lib.rmsnorm_linear_mxfp8(x, g, eps, Wq, ws, y, od, xq, xs, rstd, T, K, N, wsp, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=NULL), "RNL_ERR_NULL"),
+    (dict(Wq=NULL), "RNL_ERR_NULL"),
+    (dict(K=96), "RNL_ERR_SHAPE"),         # not a multiple of 64
+    (dict(K=(1 << 20) + 64), "RNL_ERR_SHAPE"),
+    (dict(od=4), "RNL_ERR_DTYPE"),         # no raw accumulator output
+    (dict(od=3), "RNL_ERR_DTYPE"),
+    (dict(xq=ODD), "RNL_ERR_ALIGN"),
+    (dict(Wq=ODD), "RNL_ERR_ALIGN"),
+    (dict(wsp=NULL), "RNL_ERR_WORKSPACE"),
+    (dict(wsb=64), "RNL_ERR_WORKSPACE"),
+    (dict(eps=float("inf")), "RNL_ERR_ARG"),
+])
+def test_mxfp8_validation(lib, kw, code):
+    assert mx_call(lib, **kw) == E[code]
+
+
+def test_mxfp8_workspace_and_atoms(lib):
+    assert lib.rmsnorm_linear_mxfp8_workspace_bytes(4096, 4096, 6144, 1) >= 4096 * 4096 + 4096 * 64
+    assert lib.rms_norm_quant_mxfp8(FAKE, NULL, 1e-6, FAKE, NULL, NULL, 4, 128, NULL) == E["RNL_ERR_NULL"]
+    assert lib.rms_norm_quant_mxfp8(FAKE, NULL, 1e-6, FAKE, FAKE, NULL, 4, 100, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.linear_mxfp8(FAKE, FAKE, FAKE, NULL, FAKE, 1, 4, 128, 8, NULL) == E["RNL_ERR_NULL"]
+    assert lib.linear_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 160, 8, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.linear_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 128, 8, NULL) == E["RNL_ERR_DTYPE"]
+
+
 def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, T=4, K=64, R=32,
                N=8, ws=FAKE, wsb=1 << 30):
     return lib.norm_proj_chain(x, Wa, g, eps, Wb, qr, y, rstd, T, K, R, N, ws, wsb, NULL)

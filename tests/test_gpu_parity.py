@@ -750,3 +750,110 @@ def test_mla_prolog_full_size():
     y2, _, kv2, _, _ = run_mla(case)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and torch.equal(kv1.view(torch.int16),
                                                                                    kv2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8: E4M3 codes and E8M0 scales of the normed rows bit-exact against the
+# oracle (given the device's rstd); the scaled product against the oracle's
+# exact sum on the device's own codes.  The scaled MFMA sums its 128 exact
+# products per instruction in a wide fixed-point adder rather than as a
+# correctly rounded fp32 sum, so the fp32 output is held to a bound relative to
+# the sum of the magnitudes of the scaled products.
+# ---------------------------------------------------------------------------
+def mx_abs_sum(xq, xs, wq, ws):
+    xa = np.abs(O.e4m3_decode(xq).astype(np.float64)) * np.repeat(O.e8m0_decode(xs), 64, axis=1)
+    wa = np.abs(O.e4m3_decode(wq).astype(np.float64)) * np.repeat(O.e8m0_decode(ws), 64, axis=1)
+    return xa @ wa.T
+
+
+MX_REL = 2.0 ** -12  # of the sum of |scaled products|
+
+
+def assert_mx_close(y, y_ref, s_abs, what, bf16=False):
+    """|y - y_ref| <= 2^-12 sum|terms| + (one bf16 rounding, or 1e-6) |y_ref|."""
+    err = np.abs(np.asarray(y, np.float64) - y_ref)
+    bound = MX_REL * s_abs + (2.0 ** -8 if bf16 else 1e-6) * np.abs(y_ref)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} outside; worst err/sum|terms| {np.max(err / np.maximum(s_abs, 1e-300)):.3g}"
+
+
+@pytest.mark.parametrize("T,K", [(5, 64), (9, 4160), (33, 8192), (3, 20480), (130, 256)])
+@pytest.mark.parametrize("gamma", [True, False])
+def test_mx_quant_atom(T, K, gamma):
+    case = synthetic.mxfp8_case(T, K, 8, seed=T + K, gamma=gamma)
+    x = case.tensors["x"].clone()
+    x[T // 2] = 0                                              # all-zero row: scale 2^-127, codes 0
+    x[0, :64] = (x[0, :64].float() * 2.0 ** -100).to(torch.bfloat16)  # a tiny block
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    xq, xs = rnl.rms_norm_quant_mxfp8(x.cuda(), dev(case["gamma"]), EPS, rstd_out=rstd)
+    torch.cuda.synchronize()
+    r = rstd.cpu().numpy()
+    xb = bits(x)
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    assert_rstd(r, O.rms_norm_rows(xb, gb, EPS)[1], f"mx T{T} K{K}")
+    n, _ = O.rms_norm_rows(xb, gb, EPS, rstd=r)
+    q_ref, s_ref = O.mx_quant_rows(n)
+    assert np.array_equal(xs.cpu().numpy(), s_ref), f"scales differ at {np.argwhere(xs.cpu().numpy() != s_ref)[:4]}"
+    bad = xq.cpu().numpy() != q_ref
+    assert not bad.any(), f"{int(bad.sum())} codes differ, first at {np.argwhere(bad)[:4]}"
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 128, 16), (37, 4160, 100), (300, 1024, 520), (1000, 512, 3000)])
+def test_linear_mxfp8_atom(M, K, N):
+    """The scaled GEMM on random MX operands (full E4M3 range in the activations)."""
+    xq = synthetic.e4m3_codes((M, K), 40.0, M + K, 20)
+    xs = synthetic.e8m0_codes((M, K // 64), 120, 134, M + K, 21)
+    wq = synthetic.e4m3_codes((N, K), 8.0, M + K, 22)
+    ws = synthetic.e8m0_codes((N, K // 64), 117, 119, M + K, 23)
+    y = rnl.linear_mxfp8(xq.cuda(), xs.cuda(), wq.cuda(), ws.cuda(), out_dtype=torch.float32)
+    yb = rnl.linear_mxfp8(xq.cuda(), xs.cuda(), wq.cuda(), ws.cuda())
+    torch.cuda.synchronize()
+    q, s, w, t = xq.numpy(), xs.numpy(), wq.numpy(), ws.numpy()
+    y_ref = O.mx_scaled_mm(q, s, w, t).astype(np.float64)
+    s_abs = mx_abs_sum(q, s, w, t)
+    assert_mx_close(y.cpu().numpy(), y_ref, s_abs, f"mx gemm {M}x{K}x{N}")
+    assert_mx_close(f32(yb), y_ref, s_abs, f"mx gemm bf16 {M}x{K}x{N}", bf16=True)
+
+
+def run_mx(case, out_dtype):
+    x, g, Wq, ws = dev(case["x"]), dev(case["gamma"]), dev(case["Wq"]), dev(case["w_scale"])
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, K // 64), dtype=torch.uint8, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    y = rnl.rmsnorm_linear_mxfp8(x, g, EPS, Wq, ws, out_dtype=out_dtype, xq_out=xq, x_scale_out=xs, rstd_out=rstd)
+    torch.cuda.synchronize()
+    return y.cpu(), xq.cpu().numpy(), xs.cpu().numpy(), rstd.cpu().numpy()
+
+
+def check_mx_case(case, rows=None):
+    T = case["x"].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    xb = bits(case["x"])[rows]
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    wq, ws = case["Wq"].numpy(), case["w_scale"].numpy()
+    y, xq, xs, rstd = run_mx(case, torch.float32)
+    assert_rstd(rstd[rows], O.rms_norm_rows(xb, gb, EPS)[1], case.name)
+    ref = O.rmsnorm_linear_mxfp8(xb, gb, EPS, wq, ws, rstd=rstd[rows])
+    assert np.array_equal(xq[rows], ref["q"]), f"{case.name}: codes differ"
+    assert np.array_equal(xs[rows], ref["x_scale"]), f"{case.name}: scales differ"
+    s_abs = mx_abs_sum(ref["q"], ref["x_scale"], wq, ws)
+    assert_mx_close(y.numpy()[rows], ref["y32"].astype(np.float64), s_abs, case.name)
+    yb, xq2, xs2, _ = run_mx(case, torch.bfloat16)
+    assert np.array_equal(xq2, xq) and np.array_equal(xs2, xs)
+    assert_mx_close(f32(yb)[rows], ref["y32"].astype(np.float64), s_abs, case.name + " bf16", bf16=True)
+    return yb
+
+
+@pytest.mark.parametrize("T,K,N,gamma", [(8, 256, 128, True), (37, 4160, 100, False), (300, 1024, 520, True),
+                                         (1, 64, 24, True)])
+def test_rmsnorm_linear_mxfp8_small(T, K, N, gamma):
+    check_mx_case(synthetic.mxfp8_case(T, K, N, seed=T + N, gamma=gamma))
+
+
+def test_mxfp8_qkv_full_size():
+    """Pre-attention norm + fused QKV in MXFP8, T=4096, K=4096, N=6144, at full size."""
+    case = synthetic.mxfp8_qkv()
+    y1 = check_mx_case(case, rows=sample_rows(4096, 24))
+    y2, _, _, _ = run_mx(case, torch.bfloat16)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
