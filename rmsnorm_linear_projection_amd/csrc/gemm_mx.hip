@@ -9,17 +9,24 @@
 // takes from lane l (row l & 15, group g = l >> 4) the 16-byte chunks g and
 // 4 + g of its row's k-step (k = 16g..16g+15 and 64+16g..64+16g+15), and the
 // scale of the 32-wide k block g of its row; a 64-block of the pages is two
-// such blocks, so lane group g passes the scale of 64-block 2 kt + g / 2.  The
-// scale registers are byte loads from global memory, issued one k-step ahead.
+// such blocks, so lane group g passes the scale of 64-block 2 kt + g / 2.
+//
+// Scales: every 32 k-steps (4096 k) the tile's scale bytes for those k-steps
+// (64 per row) are staged in LDS with 16-byte loads, rows padded to 80 bytes so
+// that the 16 rows one instruction reads fall in distinct banks; every second
+// k-step each lane reads one dword per operand row (the scales of both k-steps)
+// and picks its byte by shifting.
 //
 // Staging follows the bf16 / int8 GEMM: global -> LDS by direct-to-LDS DMA,
 // 128-byte rows with 16-byte chunk c of row r at slot c ^ (r & 7), a 2 x 2 grid
 // of wavefronts, XCD-aware tile order.  With two LDS stages every wait on the
-// DMA is a wait for all loads (vmcnt 0), which also covers the scale loads.
+// DMA is a wait for all loads (vmcnt 0).
 // Per k-step, phase A issues the MFMAs of the first half of the activation
 // fragments while the second half is read; after the barrier, phase B issues
 // the rest while the next k-step's first half and weight fragments are read
 // (weight fragments are double-buffered) and the free stage is refilled.
+#include <type_traits>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -50,8 +57,11 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
   constexpr int NMI = WM / 16, NNI = WN / 16;
   constexpr int HM = NMI / 2;  // activation fragments per phase
   constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int SC_CHUNK = 32;  // k-steps per scale chunk
+  constexpr int SC_ROW = 80;    // LDS bytes per scale row (64 used)
   static_assert(BM % 64 == 0 && BN % 32 == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + (BM + BN) * SC_ROW];
+  char* const sscale = smem + NST * STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -114,10 +124,8 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
     Frag f[NNI];
   };
   WFrag b0, b1;
-  struct Scales {
-    uint32_t w[NNI], x[NMI];
-  };
-  Scales s0, s1;
+  // scale dwords of the current pair of k-steps (bytes: blocks 2kt .. 2kt+3 of the row)
+  uint32_t sw[NNI], sx[NMI];
 
   auto read_a = [&](int buf, int i) {
     const int r0 = wm * WM + i * 16;
@@ -129,20 +137,38 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
     bf.f[j].lo = lds16(buf, r0, foff0);
     bf.f[j].hi = lds16(buf, r0, foff1);
   };
-  // scale bytes of k-step kt for this lane's rows (64-block 2 kt + g / 2; past K: 1.0)
-  auto load_scales = [&](Scales& sc, int kt) {
-    const int blk = 2 * kt + (fg >> 1);
-    const bool in_k = blk < kb64;
-#pragma unroll
-    for (int j = 0; j < NNI; ++j) {
-      const uint32_t o = (uint32_t)((wn * WN + j * 16 + frow) * kb64 + blk);
-      sc.w[j] = in_k ? buf_load_u8(rsb, o) : 127u;
+  // stage the scale bytes of k-steps [32 c, 32 c + 32) for all tile rows; bytes past
+  // K read as 127 (scale 1: their data are zero), rows past M / N as 0
+  auto stage_scales = [&](int c) {
+    const int b0 = c * 2 * SC_CHUNK;
+    for (int p = tid; p < (BM + BN) * 4; p += 256) {
+      const int row = p >> 2, q = p & 3;
+      const int byte0 = b0 + 16 * q;
+      const bool is_a = row < BM;
+      const __amdgpu_buffer_rsrc_t rs = is_a ? rsa : rsb;
+      const uint32_t roff = (uint32_t)((is_a ? row : row - BM) * kb64);
+      u32x4 v;
+      if ((kb64 & 15) == 0) {
+        v = byte0 < kb64 ? buf_load16(rs, roff + (uint32_t)byte0)
+                         : u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      } else {
+        v = u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t bv = byte0 + e < kb64 ? buf_load_u8(rs, roff + (uint32_t)(byte0 + e)) : 127u;
+          v[e >> 2] |= bv << (8 * (e & 3));
+        }
+      }
+      *reinterpret_cast<u32x4*>(sscale + row * SC_ROW + 16 * q) = v;
     }
+  };
+  auto read_scales = [&](int kt) {  // kt even: the dword holds the blocks of kt and kt + 1
+    const int o = 2 * (kt % SC_CHUNK);
 #pragma unroll
-    for (int i = 0; i < NMI; ++i) {
-      const uint32_t o = (uint32_t)((wm * WM + i * 16 + frow) * kb64 + blk);
-      sc.x[i] = in_k ? buf_load_u8(rsa, o) : 127u;
-    }
+    for (int j = 0; j < NNI; ++j)
+      sw[j] = *reinterpret_cast<const uint32_t*>(sscale + (BM + wn * WN + j * 16 + frow) * SC_ROW + o);
+#pragma unroll
+    for (int i = 0; i < NMI; ++i)
+      sx[i] = *reinterpret_cast<const uint32_t*>(sscale + (wm * WM + i * 16 + frow) * SC_ROW + o);
   };
 
   f32x4 acc[NMI][NNI];
@@ -150,23 +176,34 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
   for (int i = 0; i < NMI; ++i)
 #pragma unroll
     for (int j = 0; j < NNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const WFrag& bf, const Scales& sc, int i, int j) {
+  auto mma = [&](const WFrag& bf, int shift, int i, int j) {
     const i32x8 wv = __builtin_bit_cast(i32x8, __builtin_shufflevector(bf.f[j].lo, bf.f[j].hi, 0, 1, 2, 3, 4, 5, 6, 7));
     const i32x8 xv = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[i].lo, a[i].hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv, acc[i][j], 0, 0, 0, (int)sc.w[j], 0,
-                                                                 (int)sc.x[i]);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv, acc[i][j], 0, 0, 0, (int)(sw[j] >> shift), 0,
+                                                                 (int)(sx[i] >> shift));
   };
 
-  // one k-step: bc / sc hold its weight fragments and scales, bn / sn receive the next k-step's
-  auto kstep = [&](WFrag& bc, WFrag& bn, Scales& sc, Scales& sn, int kt) {
-    const int slot = kt & 1, nslot = slot ^ 1;
+  // one k-step: bc holds its weight fragments, bn receives the next k-step's; PAR = kt & 1
+  auto kstep = [&](WFrag& bc, WFrag& bn, int kt, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const int slot = PAR, nslot = PAR ^ 1;
+    if constexpr (PAR == 0) {
+      if (kt > 0 && kt % SC_CHUNK == 0) {
+        // every wave read the previous chunk two k-steps ago, before the barrier of
+        // the previous k-step; the new chunk is visible after this barrier
+        stage_scales(kt / SC_CHUNK);
+        __syncthreads();
+      }
+      read_scales(kt);
+    }
+    // this lane's scale byte sits at bit 8 * (2 PAR + g / 2) of the row's dword
+    const int shift = 8 * (2 * PAR + (fg >> 1));
     // phase A: MFMAs of activation fragments [0, HM); read [HM, NMI) of this k-step
-    load_scales(sn, kt + 1);
 #pragma unroll
     for (int i = 0; i < HM; ++i) {
       read_a(slot, HM + i);
 #pragma unroll
-      for (int j = 0; j < NNI; ++j) mma(bc, sc, i, j);
+      for (int j = 0; j < NNI; ++j) mma(bc, shift, i, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     // k-step kt + 1 has landed and every wave has finished reading stage `slot`
@@ -182,7 +219,7 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
       read_a(nslot, i);
       if (i < NNI) read_b(bn, nslot, i);
 #pragma unroll
-      for (int j = 0; j < NNI; ++j) mma(bc, sc, HM + i, j);
+      for (int j = 0; j < NNI; ++j) mma(bc, shift, HM + i, j);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -194,7 +231,7 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
   for (int st = 0; st < NST; ++st)
 #pragma unroll
     for (int g = 0; g < LPS; ++g) dload_one(st, st, g);
-  load_scales(s0, 0);
+  stage_scales(0);
   RNL_MX_WAIT_VM_LGKM0(0);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -204,10 +241,10 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
 
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    kstep(b0, b1, s0, s1, kt);
-    kstep(b1, b0, s1, s0, kt + 1);
+    kstep(b0, b1, kt, std::integral_constant<int, 0>{});
+    kstep(b1, b0, kt + 1, std::integral_constant<int, 1>{});
   }
-  if (kt < nk) kstep(b0, b1, s0, s1, kt);
+  if (kt < nk) kstep(b0, b1, kt, std::integral_constant<int, 0>{});
   RNL_MX_WAIT_VM_LGKM0(0);
 
   // epilogue: lane holds C[m][n .. n+3]

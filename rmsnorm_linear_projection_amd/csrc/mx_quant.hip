@@ -7,10 +7,12 @@
 // E4M3 code nearest to n / X (ties to the even mantissa, magnitudes beyond 448
 // clamped to 448, a zero result encoded as +0).
 //
-// One wavefront per row.  Pass 1 streams the row for the fp32 sum of squares;
-// pass 2 streams it again (from cache), norms each 8-value chunk, and the 8
-// lanes that hold one 64-block exchange their maxima with xor shuffles.  Every
-// lane runs the same number of iterations, so the shuffles never run in
+// One wavefront per row.  Rows of up to 64 * 8 * CPL values are loaded once
+// into registers (all CPL 16-byte loads of a lane in flight together); longer
+// rows (CPL = 0) are streamed twice, the second time from cache.  The fp32 sum
+// of squares is a wavefront reduction; each 8-value chunk is then normed, and
+// the 8 lanes that hold one 64-block exchange their maxima with xor shuffles.
+// Every lane runs the same number of iterations, so the shuffles never run in
 // divergent code.
 #include "launch.h"
 #include "rows.cuh"
@@ -20,28 +22,53 @@ namespace {
 
 constexpr int kMxThreads = 256;
 
-// E4M3 code of v: nearest even, saturating at 448, +0 for a zero result.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t ab = b & 0x7FFFFFFFu;
-  const float a = __uint_as_float(ab);
-  uint32_t mag;
-  if (!(a < 448.0f)) {
-    mag = 0x7Eu;
-  } else if (a < 0.015625f) {
-    // below 2^-6 the spacing is 2^-9: the code is the rounded multiple itself
-    // (a rounded value of 8 is 2^-6, whose code is 0x08)
-    mag = (uint32_t)rintf(a * 512.0f);
-  } else {
-    // keep 3 mantissa bits, round to nearest even at bit 20, rebias 127 -> 7
-    const uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20;
-    mag = r - ((127u - 7u) << 3);
-    if (mag > 0x7Eu) mag = 0x7Eu;
-  }
-  return mag == 0u ? 0u : (mag | ((b >> 24) & 0x80u));
+// Four E4M3 codes (nearest even) of v[0..3], packed low byte first.  The values
+// are first clamped to +-448 (the largest E4M3 value, so the conversion never
+// overflows); v_cvt_pk_fp8_f32 then rounds to nearest even, subnormals included.
+// A negative value that rounds to zero comes out as 0x80 (-0); it is turned
+// into +0, the code the reading of the pages takes for any zero.
+__device__ __forceinline__ uint32_t e4m3x4(const float* v) {
+  float c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(v[j], -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  const uint32_t u = (uint32_t)w;
+  // bytes equal to 0x80: t has a zero byte there
+  const uint32_t t = u ^ 0x80808080u;
+  const uint32_t zero = ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;
+  return u & ~zero;
 }
 
-template <bool GAMMA>
+// max over the 8 lanes 8q .. 8q+7 (DPP: swap neighbours, swap pairs, mirror the half-row)
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+  return v;
+}
+
+// MX-quantise the 8 normed values of chunk idx (8 lanes hold one 64-block)
+__device__ __forceinline__ void mx_emit(const float n[8], bool live, int idx, int lane, u32x2* qrow, uint8_t* srow) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(n[j]));
+  amax = max8(amax);
+  // floor(log2(amax)) is the exponent field of amax (a subnormal or zero amax
+  // gives a field of 0, which the clamp turns into -127)
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  const int e = max(ebits - 127 - 8, -127);
+  const float inv_x = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = n[j] * inv_x;
+  if (live) {
+    qrow[idx] = u32x2{e4m3x4(v), e4m3x4(v + 4)};
+    if ((lane & 7) == 0) srow[idx >> 3] = (uint8_t)(e + 127);
+  }
+}
+
+template <int CPL, bool GAMMA>
 __global__ __launch_bounds__(kMxThreads) void norm_rows_mx_kernel(const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ gamma, float eps,
                                                                   float inv_k, int64_t T, int64_t K,
@@ -54,40 +81,44 @@ __global__ __launch_bounds__(kMxThreads) void norm_rows_mx_kernel(const uint16_t
   const int nch = (int)(K >> 3);  // a multiple of 8: a 64-block is 8 whole chunks
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * K);
   const u32x4* gr = GAMMA ? reinterpret_cast<const u32x4*>(gamma) : nullptr;
-
-  float ss = 0.f;
-  for (int base = 0; base < nch; base += kWave) {
-    const int idx = base + lane;
-    if (idx < nch) ss += sumsq8(xr[idx]);
-  }
-  const float rstd = rstd_from_sumsq(wave_sum(ss), inv_k, eps);
-  if (lane == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
-
   u32x2* qrow = reinterpret_cast<u32x2*>(q_out + t * K);
   uint8_t* srow = s_out + t * (K >> 6);
-  for (int base = 0; base < nch; base += kWave) {
-    const int idx = base + lane;
-    const bool live = idx < nch;  // the same for all 8 lanes of a 64-block
-    const u32x4 w = live ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
-    float n[8];
-    normed8(w, gr, live ? idx : 0, rstd, n);
-    float amax = 0.f;
+
+  if constexpr (CPL > 0) {
+    u32x4 v[CPL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(n[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-    // floor(log2(amax)) is the exponent field of amax (a subnormal or zero amax
-    // gives a field of 0, which the clamp turns into -127)
-    const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
-    const int e = max(ebits - 127 - 8, -127);
-    const float inv_x = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
-    uint32_t c[2] = {0u, 0u};
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + kWave * c;
+      v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+    float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) c[j >> 2] |= e4m3_rne(n[j] * inv_x) << (8 * (j & 3));
-    if (live) {
-      qrow[idx] = u32x2{c[0], c[1]};
-      if ((lane & 7) == 0) srow[idx >> 3] = (uint8_t)(e + 127);
+    for (int c = 0; c < CPL; ++c) ss += sumsq8(v[c]);
+    const float rstd = rstd_from_sumsq(wave_sum(ss), inv_k, eps);
+    if (lane == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + kWave * c;
+      const bool live = idx < nch;
+      float n[8];
+      normed8(v[c], gr, live ? idx : 0, rstd, n);
+      mx_emit(n, live, idx, lane, qrow, srow);
+    }
+  } else {
+    float ss = 0.f;
+    for (int base = 0; base < nch; base += kWave) {
+      const int idx = base + lane;
+      if (idx < nch) ss += sumsq8(xr[idx]);
+    }
+    const float rstd = rstd_from_sumsq(wave_sum(ss), inv_k, eps);
+    if (lane == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
+    for (int base = 0; base < nch; base += kWave) {
+      const int idx = base + lane;
+      const bool live = idx < nch;
+      const u32x4 w = live ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+      float n[8];
+      normed8(w, gr, live ? idx : 0, rstd, n);
+      mx_emit(n, live, idx, lane, qrow, srow);
     }
   }
 }
@@ -98,12 +129,20 @@ hipError_t launch_norm_rows_mx(const uint16_t* x, const uint16_t* gamma, float e
                                uint8_t* q_out, uint8_t* s_out, float* rstd_out, hipStream_t s) {
   const float inv_k = 1.0f / (float)K;
   const dim3 grid((unsigned)((T + 3) / 4)), block(kMxThreads);
-  if (gamma != nullptr)
-    hipLaunchKernelGGL(norm_rows_mx_kernel<true>, grid, block, 0, s, x, gamma, eps, inv_k, T, K, q_out, s_out,
-                       rstd_out);
-  else
-    hipLaunchKernelGGL(norm_rows_mx_kernel<false>, grid, block, 0, s, x, gamma, eps, inv_k, T, K, q_out, s_out,
-                       rstd_out);
+  const int64_t per = (K / 8 + kWave - 1) / kWave;  // chunks per lane
+#define RNL_MX(C, G)                                                                                          \
+  hipLaunchKernelGGL((norm_rows_mx_kernel<C, G>), grid, block, 0, s, x, gamma, eps, inv_k, T, K, q_out, s_out, \
+                     rstd_out)
+#define RNL_MX_G(C) \
+  if (gamma != nullptr) RNL_MX(C, true); else RNL_MX(C, false)
+  if (per <= 1) RNL_MX_G(1);
+  else if (per <= 2) RNL_MX_G(2);
+  else if (per <= 4) RNL_MX_G(4);
+  else if (per <= 8) RNL_MX_G(8);
+  else if (per <= 16) RNL_MX_G(16);
+  else RNL_MX_G(0);
+#undef RNL_MX_G
+#undef RNL_MX
   return hipGetLastError();
 }
 

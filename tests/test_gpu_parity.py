@@ -798,7 +798,9 @@ def test_mx_quant_atom(T, K, gamma):
     assert not bad.any(), f"{int(bad.sum())} codes differ, first at {np.argwhere(bad)[:4]}"
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 128, 16), (37, 4160, 100), (300, 1024, 520), (1000, 512, 3000)])
+@pytest.mark.parametrize("M,K,N", [(16, 128, 16), (37, 4160, 100), (300, 1024, 520), (1000, 512, 3000),
+                                   (40, 8256, 72),     # scales staged in three chunks, K not a multiple of 1024
+                                   (260, 12288, 200)])  # three full chunks
 def test_linear_mxfp8_atom(M, K, N):
     """The scaled GEMM on random MX operands (full E4M3 range in the activations)."""
     xq = synthetic.e4m3_codes((M, K), 40.0, M + K, 20)
