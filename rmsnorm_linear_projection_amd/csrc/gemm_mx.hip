@@ -23,10 +23,10 @@
 // DMA is a wait for all loads (vmcnt 0).
 // Per k-step, phase A issues the MFMAs of the first half of the activation
 // fragments while the second half is read; after the barrier, phase B issues
-// the rest while the next k-step's first half and weight fragments are read
-// (weight fragments are double-buffered) and the free stage is refilled.
-#include <type_traits>
-
+// the rest while the free stage is refilled and the next k-step's first half
+// is read.  Both phases run weight fragment by weight fragment, and phase B
+// reloads weight fragment j for the next k-step right after its last MFMA, so
+// the weight fragments need no second register set.
 #include "common.cuh"
 #include "launch.h"
 
@@ -120,10 +120,7 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
     u32x4 lo, hi;
   };
   Frag a[NMI];
-  struct WFrag {
-    Frag f[NNI];
-  };
-  WFrag b0, b1;
+  Frag b[NNI];
   // scale dwords of the current pair of k-steps (bytes: blocks 2kt .. 2kt+3 of the row)
   uint32_t sw[NNI], sx[NMI];
 
@@ -132,10 +129,10 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
     a[i].lo = lds16(buf, r0, foff0);
     a[i].hi = lds16(buf, r0, foff1);
   };
-  auto read_b = [&](WFrag& bf, int buf, int j) {
+  auto read_b = [&](int buf, int j) {
     const int r0 = BM + wn * WN + j * 16;
-    bf.f[j].lo = lds16(buf, r0, foff0);
-    bf.f[j].hi = lds16(buf, r0, foff1);
+    b[j].lo = lds16(buf, r0, foff0);
+    b[j].hi = lds16(buf, r0, foff1);
   };
   // stage the scale bytes of k-steps [32 c, 32 c + 32) for all tile rows; bytes past
   // K read as 127 (scale 1: their data are zero), rows past M / N as 0
@@ -176,18 +173,19 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
   for (int i = 0; i < NMI; ++i)
 #pragma unroll
     for (int j = 0; j < NNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const WFrag& bf, int shift, int i, int j) {
-    const i32x8 wv = __builtin_bit_cast(i32x8, __builtin_shufflevector(bf.f[j].lo, bf.f[j].hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  auto mma = [&](int shift, int i, int j) {
+    const i32x8 wv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b[j].lo, b[j].hi, 0, 1, 2, 3, 4, 5, 6, 7));
     const i32x8 xv = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[i].lo, a[i].hi, 0, 1, 2, 3, 4, 5, 6, 7));
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv, acc[i][j], 0, 0, 0, (int)(sw[j] >> shift), 0,
                                                                  (int)(sx[i] >> shift));
   };
 
-  // one k-step: bc holds its weight fragments, bn receives the next k-step's; PAR = kt & 1
-  auto kstep = [&](WFrag& bc, WFrag& bn, int kt, auto par) {
-    constexpr int PAR = decltype(par)::value;
+  // one k-step; PAR = kt & 1.  (The loop runs one k-step per iteration: with two
+  // k-steps per iteration and a compile-time parity the register allocator moves
+  // accumulators between AGPRs and VGPRs around the MFMAs.)
+  auto kstep = [&](int kt, int PAR) {
     const int slot = PAR, nslot = PAR ^ 1;
-    if constexpr (PAR == 0) {
+    if (PAR == 0) {
       if (kt > 0 && kt % SC_CHUNK == 0) {
         // every wave read the previous chunk two k-steps ago, before the barrier of
         // the previous k-step; the new chunk is visible after this barrier
@@ -200,30 +198,32 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
     const int shift = 8 * (2 * PAR + (fg >> 1));
     // phase A: MFMAs of activation fragments [0, HM); read [HM, NMI) of this k-step
 #pragma unroll
-    for (int i = 0; i < HM; ++i) {
-      read_a(slot, HM + i);
+    for (int j = 0; j < NNI; ++j) {
+      if (j < HM) read_a(slot, HM + j);
 #pragma unroll
-      for (int j = 0; j < NNI; ++j) mma(bc, shift, i, j);
+      for (int i = 0; i < HM; ++i) mma(shift, i, j);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int i = NNI; i < HM; ++i) read_a(slot, HM + i);
     // k-step kt + 1 has landed and every wave has finished reading stage `slot`
     RNL_MX_WAIT_VM_LGKM0(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // phase B: refill `slot` with k-step kt + 2; MFMAs of [HM, NMI); read the next k-step's
-    // first half and weight fragments from stage nslot
+    // phase B: refill `slot` with k-step kt + 2; MFMAs of [HM, NMI); read the next
+    // k-step's first half and, after its last use, each weight fragment
 #pragma unroll
     for (int g = 0; g < LPS; ++g) dload_one(kt + 2, slot, g);
 #pragma unroll
-    for (int i = 0; i < HM; ++i) {
-      read_a(nslot, i);
-      if (i < NNI) read_b(bn, nslot, i);
+    for (int j = 0; j < NNI; ++j) {
+      if (j < HM) read_a(nslot, j);
 #pragma unroll
-      for (int j = 0; j < NNI; ++j) mma(bc, shift, HM + i, j);
+      for (int i = HM; i < NMI; ++i) mma(shift, i, j);
+      read_b(nslot, j);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int j = HM; j < NNI; ++j) read_b(bn, nslot, j);
+    for (int i = NNI; i < HM; ++i) read_a(nslot, i);
   };
 
   // prologue: both stages, the scales of k-step 0, the first half and weights of k-step 0
@@ -237,14 +237,10 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
 #pragma unroll
   for (int i = 0; i < HM; ++i) read_a(0, i);
 #pragma unroll
-  for (int j = 0; j < NNI; ++j) read_b(b0, 0, j);
+  for (int j = 0; j < NNI; ++j) read_b(0, j);
 
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    kstep(b0, b1, kt, std::integral_constant<int, 0>{});
-    kstep(b1, b0, kt + 1, std::integral_constant<int, 1>{});
-  }
-  if (kt < nk) kstep(b0, b1, kt, std::integral_constant<int, 0>{});
+  for (; kt < nk; ++kt) kstep(kt, kt & 1);
   RNL_MX_WAIT_VM_LGKM0(0);
 
   // epilogue: lane holds C[m][n .. n+3]
