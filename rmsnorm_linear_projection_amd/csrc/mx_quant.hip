@@ -11,9 +11,9 @@
 // into registers (all CPL 16-byte loads of a lane in flight together); longer
 // rows (CPL = 0) are streamed twice, the second time from cache.  The fp32 sum
 // of squares is a wavefront reduction; each 8-value chunk is then normed, and
-// the 8 lanes that hold one 64-block exchange their maxima with xor shuffles.
-// Every lane runs the same number of iterations, so the shuffles never run in
-// divergent code.
+// the 8 lanes that hold one 64-block exchange their maxima with DPP moves.
+// Every lane runs the same number of iterations, so the cross-lane moves never
+// run in divergent code.
 #include "launch.h"
 #include "rows.cuh"
 
