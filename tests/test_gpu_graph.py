@@ -1,0 +1,128 @@
+"""Graph replay: every entry point captured in a HIP graph (as the benchmark
+times it) gives, on each of several replays, the same bits as the eager call.
+Between replays the outputs are overwritten by eager work and the device is
+synchronised, so a replay that skipped or reordered work would show."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import rmsnorm_linear_projection_amd as rnl
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    rnl.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(case):
+    return {k: (v.cuda() if v is not None else None) for k, v in case.tensors.items()}
+
+
+def check_replays(fn, outs, replays=3):
+    """fn() writes into the preallocated tensors ``outs``."""
+    fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm the side stream once before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    for r in range(replays):
+        for o in outs:
+            o.view(torch.uint8).fill_(0xA5)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, ref):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), f"replay {r} differs"
+
+
+def ws_for(kind, *shape, **kw):
+    n = rnl.workspace_bytes(kind, *shape, **kw)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 1032, 200), (16, 4096, 512), (1, 256, 64)])
+def test_graph_bf16(T, K, N):
+    t = dev(synthetic.norm_linear_case(T, K, N, seed=1))
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    ws = ws_for("bf16", T, K, N)
+    check_replays(lambda: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], EPS, t["W"], y=y, rstd_out=rstd, workspace=ws),
+                  [y, rstd])
+
+
+def test_graph_fp32_weights():
+    T, K, N = 64, 8192, 24
+    t = dev(synthetic.norm_linear_case(T, K, N, seed=2, gamma=False, w_dtype="fp32"))
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    ws = ws_for("bf16", T, K, N, w_dtype=torch.float32, out_dtype=torch.float32)
+    check_replays(lambda: rnl.rmsnorm_linear_bf16(t["x"], None, EPS, t["W"], out_dtype=torch.float32, y=y,
+                                                  workspace=ws), [y])
+
+
+def test_graph_int8_and_add():
+    T, K, N = 130, 4112, 100
+    t = dev(synthetic.with_residual(synthetic.int8_case(T, K, N, seed=3)))
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    xa = torch.empty_like(t["x"])
+    xq = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(T, dtype=torch.float32, device="cuda")
+    check_replays(lambda: rnl.add_rmsnorm_linear_int8(t["x"], t["residual"], t["gamma"], EPS, t["Wq"], t["w_scale"],
+                                                      y=y, x_add_out=xa, xq_out=xq, x_scale_out=xs),
+                  [y, xa, xq, xs])
+
+
+def test_graph_chain_and_mla():
+    T, K, R, Rkv, N = 64, 4096, 128, 64, 64  # stage 1 split over K
+    t = dev(synthetic.mla_case(T, K, R, Rkv, N, seed=4))
+    W_akv = torch.cat([t["W_a"], t["W_kv"]], 0).contiguous()
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((T, Rkv), dtype=torch.bfloat16, device="cuda")
+    ws = ws_for("mla", T, K, R, Rkv, N)
+    check_replays(lambda: rnl.mla_prolog_bf16(t["x"], W_akv, R, t["gamma"], t["gamma_ckv"], EPS, t["W_b"], qr_out=qr,
+                                              kv_out=kv, y=y, workspace=ws), [y, qr, kv])
+    y2 = torch.empty_like(y)
+    qr2 = torch.empty_like(qr)
+    ws2 = ws_for("chain", T, K, R, N)
+    check_replays(lambda: rnl.norm_proj_chain(t["x"], t["W_a"], t["gamma"], EPS, t["W_b"], qr_out=qr2, y=y2,
+                                              workspace=ws2), [y2, qr2])
+
+
+def test_graph_preattn_block():
+    T = 40
+    t = dev(synthetic.preattn_case(T, 1032, 6, 1, 128, seed=5, residual=True))
+    N = 8 * 128
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    xa = torch.empty_like(t["x"])
+    hr = torch.empty((T, 7), dtype=torch.float32, device="cuda")
+    ws = ws_for("preattn", T, 1032, 6, 1, 128)
+    check_replays(lambda: rnl.preattn_qkv_bf16(t["x"], t["gamma"], EPS, t["W"], 6, 1, 128, t["gamma_q"], t["gamma_k"],
+                                               EPS, t["cos"], t["sin"], residual=t["residual"], x_add_out=xa, y=y,
+                                               head_rstd_out=hr, workspace=ws), [y, xa, hr])
+
+
+def test_graph_mxfp8():
+    T, K, N = 300, 4160, 520  # K not a multiple of 1024: byte-wise scale staging
+    t = dev(synthetic.mxfp8_case(T, K, N, seed=6))
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    xq = torch.empty((T, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, K // 64), dtype=torch.uint8, device="cuda")
+    check_replays(lambda: rnl.rmsnorm_linear_mxfp8(t["x"], t["gamma"], EPS, t["Wq"], t["w_scale"],
+                                                   out_dtype=torch.float32, y=y, xq_out=xq, x_scale_out=xs),
+                  [y, xq, xs])
