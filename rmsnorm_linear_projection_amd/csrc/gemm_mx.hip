@@ -12,8 +12,9 @@
 // such blocks, so lane group g passes the scale of 64-block 2 kt + g / 2.
 //
 // Scales: every 32 k-steps (4096 k) the tile's scale bytes for those k-steps
-// (64 per row) are staged in LDS with 16-byte loads, rows padded to 80 bytes so
-// that the 16 rows one instruction reads fall in distinct banks; every second
+// (64 per row) are staged in LDS with 16-byte loads, rows padded to 68 bytes (an
+// odd number of dwords) so that the 16 rows one instruction reads fall in
+// distinct banks; every second
 // k-step each lane reads one dword per operand row (the scales of both k-steps)
 // and picks its byte by shifting.
 //
@@ -58,7 +59,7 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
   constexpr int HM = NMI / 2;  // activation fragments per phase
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int SC_CHUNK = 32;  // k-steps per scale chunk
-  constexpr int SC_ROW = 80;    // LDS bytes per scale row (64 used)
+  constexpr int SC_ROW = 68;    // LDS bytes per scale row (64 used; 17 dwords)
   static_assert(BM % 64 == 0 && BN % 32 == 0, "tile shape");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + (BM + BN) * SC_ROW];
   char* const sscale = smem + NST * STAGE;
@@ -155,7 +156,9 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
           v[e >> 2] |= bv << (8 * (e & 3));
         }
       }
-      *reinterpret_cast<u32x4*>(sscale + row * SC_ROW + 16 * q) = v;
+      uint32_t* d = reinterpret_cast<uint32_t*>(sscale + row * SC_ROW + 16 * q);  // 4-byte aligned only
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = v[e];
     }
   };
   auto read_scales = [&](int kt) {  // kt even: the dword holds the blocks of kt and kt + 1
