@@ -283,9 +283,10 @@ struct Plan {
 };
 
 // About one workgroup per CU: the K range is split into S pieces of spw k-steps,
-// spw a power of two (>= 8) so that each piece of a token row starts and ends on
-// a 2^n-byte boundary (unaligned pieces stream measurably slower from HBM), the
-// smallest such that tg * nc * S does not exceed 256.
+// spw the smallest multiple of 4 (>= 8) such that tg * nc * S does not exceed
+// 256.  A piece of a token row is then a multiple of 256 bytes long and starts
+// on a 256-byte boundary of the row (T = 512, K = 28672: spw = 28, 8 x 32 = 256
+// workgroups).
 Plan plan_of(int64_t T, int64_t K, int64_t N, int tg_rows = kTG) {
   Plan p;
   p.tg = (int)((T + tg_rows - 1) / tg_rows);
@@ -293,8 +294,9 @@ Plan plan_of(int64_t T, int64_t K, int64_t N, int tg_rows = kTG) {
   p.Npad = p.nc * kNC;
   p.nsteps = (int)((K + 31) / 32);
   const int64_t tiles = (int64_t)p.tg * p.nc;
-  int64_t spw = 8;
-  while (spw < 4096 && tiles * ((p.nsteps + spw - 1) / spw) > 256) spw *= 2;
+  const int64_t per_tile = std::max<int64_t>(1, 256 / tiles);  // pieces per token tile
+  int64_t spw = std::max<int64_t>(8, ((p.nsteps + per_tile - 1) / per_tile + 3) / 4 * 4);
+  while (spw < 4096 && tiles * ((p.nsteps + spw - 1) / spw) > 256) spw += 4;
   p.spw = (int)spw;
   p.S = (int)((p.nsteps + spw - 1) / spw);
   return p;
