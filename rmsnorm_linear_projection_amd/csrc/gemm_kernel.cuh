@@ -78,8 +78,10 @@ enum Epi : int {
 // s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt unchanged (gfx9 encoding)
 #define RNL_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
 
-template <typename TIn, int BM, int BN, int NST, int GROUP_M, int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// WPE: workgroups per CU the kernel is built for (1, or 2 for tiles that fit twice
+// in LDS and in half the register file).
+template <typename TIn, int BM, int BN, int NST, int GROUP_M, int EPI, int WPE = 1>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* __restrict__ C,
                     const float* __restrict__ xs, const float* __restrict__ ws, int M, int N, int K,
                     int tiles_m, int tiles_n, int ksplit, int steps_per_split) {
@@ -276,21 +278,23 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename TIn, int BM, int BN, int NST, int EPI>
+template <typename TIn, int BM, int BN, int NST, int EPI, int WPE = 1>
 hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws, int64_t M,
                        int64_t N, int64_t K, int ksplit, hipStream_t s) {
   const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   const int nk = (int)cdiv(K * (int64_t)sizeof(TIn), 128);
   const int sps = (int)cdiv(nk, ksplit);
   const int nwg = tiles_m * tiles_n * ksplit;
-  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI>), dim3(nwg), dim3(256), 0, s, A, B, C,
+  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI, WPE>), dim3(nwg), dim3(256), 0, s, A, B, C,
                      xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n, ksplit, sps);
   return hipGetLastError();
 }
 
 // Tile shapes, largest first: 256x192 (2 LDS stages, 112 KiB), 256x128 and 128x256
-// (3 stages, 144 KiB), 128x128 (4 stages, 128 KiB).
-enum Shape { S256x192, S256x128, S128x256, S128x128 };
+// (3 stages, 144 KiB), 128x128 (4 stages, 128 KiB); and 128x128 with 2 stages
+// (64 KiB), two workgroups per CU, so that one tile's prologue, barriers and
+// output writes overlap the other's k-loop (used by the int8 GEMM).
+enum Shape { S256x192, S256x128, S128x256, S128x128, S128x128_2PerCU };
 
 inline Shape pick_shape(int64_t M, int64_t N) {
   // Largest tile that still gives every CU at least one workgroup.
@@ -307,6 +311,7 @@ hipError_t launch_shape(Shape sh, const TIn* A, const TIn* B, void* C, const flo
     case S256x192: return launch_tile<TIn, 256, 192, 2, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S256x128: return launch_tile<TIn, 256, 128, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x256: return launch_tile<TIn, 128, 256, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    case S128x128_2PerCU: return launch_tile<TIn, 128, 128, 2, EPI, 2>(A, B, C, xs, ws, M, N, K, ksplit, s);
     default: return launch_tile<TIn, 128, 128, 4, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
   }
 }
