@@ -65,7 +65,8 @@ WORKLOADS = {
 DEFAULT = "preattn_qkv_T4096"
 KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.cuh", "gemm_bf16.hip", "gemm_int8.hip", "common.cuh"],
-    "small_m": ["small_m.hip", "common.cuh"],
+    "small_m": ["small_m.hip", "common.cuh", "rows.cuh"],
+    "small_m_norm": ["small_m.hip", "common.cuh", "rows.cuh"],
     "gemm_mx": ["gemm_mx.hip", "common.cuh"],
     "skinny": ["skinny.hip", "common.cuh"],
 }
@@ -104,6 +105,24 @@ def src_sha(names):
         with open(os.path.join(CSRC, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def fused_small_norm(w):
+    """True when the library norms the rows inside the weight-streaming kernel:
+    at most 4 rows, no residual, normed rows within 64 KiB."""
+    T, K = w["T"], w["K"]
+    return w["kind"] == "bf16" and not w.get("add") and T <= 4 and T * ((K + 31) // 32) * 64 <= 64 * 1024
+
+
+def kernel_key_of(w):
+    """Key of the dominant kernel of a workload (KERNEL_MATCH, KERNEL_SOURCES)."""
+    if w["kind"] == "fp32w":
+        return "skinny"
+    if w["kind"] == "mxfp8":
+        return "gemm_mx"
+    if fused_small_norm(w):
+        return "small_m_norm"
+    return "small_m" if w["kind"] in ("bf16", "preattn") and w["T"] <= 16 else "gemm"
 
 
 def load_traffic(name, kernel_key, launches_per_step=1):
@@ -173,7 +192,12 @@ class Setup:
                 self.step = lambda i: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], y=y,
                                                               workspace=ws)
             a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
-            if T <= 16:
+            if fused_small_norm(w):
+                # the norm runs inside the weight-streaming kernel: the step is that one launch
+                self.kernel, self.kernel_key = "small_m_norm_kernel", "small_m_norm"
+                self.kern = self.step
+                self.kern_units = ("hbm", bytes_of(w))
+            elif T <= 16:
                 # weight streaming: the normed activations are re-read from L2,
                 # the weight (rotated) from HBM
                 self.kernel, self.kernel_key = "small_m_kernel", "small_m"
@@ -422,7 +446,8 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
 
 
 COPY_BYTES = 256 << 20  # size of the plain device copy that calibrates FETCH_SIZE / WRITE_SIZE
-KERNEL_MATCH = {"gemm": "gemm_nt_kernel", "small_m": "small_m_kernel", "skinny": "skinny_", "gemm_mx": "gemm_mx_kernel"}
+KERNEL_MATCH = {"gemm": "gemm_nt_kernel", "small_m": "small_m_kernel", "small_m_norm": "small_m_norm_kernel",
+                "skinny": "skinny_", "gemm_mx": "gemm_mx_kernel"}
 
 
 def copy_calibration(steps=5):
@@ -463,13 +488,7 @@ def _counter_kib(csv_path, name_part, counter, all_names=False):
 def record_counters(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Fold two rocprofv3 --pmc runs of a workload (FETCH_SIZE, then WRITE_SIZE)
     and the same two counters of the calibration copy into profiles/counters.json."""
-    w = WORKLOADS[name]
-    if w["kind"] == "fp32w":
-        key = "skinny"
-    elif w["kind"] == "mxfp8":
-        key = "gemm_mx"
-    else:
-        key = "small_m" if w["kind"] in ("bf16", "preattn") and w["T"] <= 16 else "gemm"
+    key = kernel_key_of(WORKLOADS[name])
     pair = key == "skinny"
     fk, nf = _counter_kib(fetch_csv, KERNEL_MATCH[key], "FETCH_SIZE", pair)
     wk, nw = _counter_kib(write_csv, KERNEL_MATCH[key], "WRITE_SIZE", pair)

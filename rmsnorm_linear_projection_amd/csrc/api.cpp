@@ -40,6 +40,7 @@ constexpr int64_t kMaxK_int8 = 133144;  // K * 127 * 127 <= 2^31 - 1
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 32-bit tile offsets in range
 constexpr int64_t kMaxN_fp32w = int64_t(1) << 20;  // fp32 weights: column blocks of 32 fit one grid axis
 constexpr int64_t kSmallM = 16;  // at most this many activation rows: weight-streaming kernel
+constexpr int64_t kFusedNormM = 4;  // at most this many (and no residual): the norm runs inside it
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -154,6 +155,10 @@ int bf16_path(const void* x, const void* residual, void* x_add, const void* gamm
                       "skinny split-K launch");
   }
   const uint16_t* wb = static_cast<const uint16_t*>(W);
+  // a few tokens whose normed rows fit LDS: the norm runs inside the weight-streaming kernel
+  if (rb == nullptr && T <= kFusedNormM && use_small_m(T) && rnl::small_m_norm_lds(T, K) <= rnl::kSmallNormLds)
+    return hip_status(rnl::launch_small_m_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
+                      "fused norm + projection launch");
   uint16_t* a = static_cast<uint16_t*>(workspace);
   const hipError_t e = rb != nullptr ? rnl::launch_add_norm_rows_bf16(xb, rb, xab, gb, eps, T, K, a, rstd_out, s)
                                      : rnl::launch_norm_rows_bf16(xb, gb, eps, T, K, a, rstd_out, s);

@@ -82,6 +82,14 @@ hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B,
 // R = weight rows per workgroup (a multiple of 4, at most 32), or 0 to let
 // small_m_rows(N) spread the rows evenly over the compute units.
 int small_m_rows(int64_t N);
+// The same with the RMSNorm of the raw rows X[M,K] fused in (M <= 16): y = bf16(
+// RMSNorm(X) * gamma) . W^T; rstd_out [M] may be null.  The normed rows live in
+// LDS: small_m_norm_lds(M, K) bytes, which must not exceed kSmallNormLds.
+constexpr size_t kSmallNormLds = 64 * 1024;
+size_t small_m_norm_lds(int64_t M, int64_t K);
+hipError_t launch_small_m_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
+                                    void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
+                                    hipStream_t s);
 hipError_t launch_small_m_bf16(const uint16_t* A, const uint16_t* W, void* C, int out_kind, int64_t M,
                                int64_t N, int64_t K, int R, hipStream_t s);
 

@@ -119,6 +119,11 @@ BF16_SMALL = [
     (9, 20480, 24),
     (16, 4096, 24576),  # 32 weight rows per workgroup, three workgroups per CU
     (2, 2048, 200),
+    (1, 8200, 40),  # norm fused into the weight streaming: a row longer than one load batch
+    (2, 12296, 100),  # the same with two rows and a K tail
+    (4, 8192, 200),  # four normed rows filling the 64 KiB LDS budget exactly
+    (4, 64, 9),  # two k-steps: two of the four wavefronts have no part of K
+    (8, 4096, 200),  # more rows than the fused norm takes: pre-pass
 ]
 
 
