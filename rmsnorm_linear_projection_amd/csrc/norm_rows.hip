@@ -46,15 +46,22 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
+// Four int8 codes q = clamp(rint(fl(n * s)), -127, 127), packed little-endian.
+// With s = fl(127/amax) and |n| <= amax, |fl(n * s)| <= 127 + 2^-17, so the
+// clamp never binds and rint is all that is left: adding 1.5 * 2^23 rounds the
+// product to the nearest integer, ties to even (floats in [2^23, 2^24) are
+// spaced 1 apart), and the low byte of the sum's bit pattern is that integer's
+// two's-complement byte.  v_perm gathers the four bytes.  (s = +inf, for amax
+// below 127 / FLT_MAX, would give 0 instead of +-127; rows with such an amax
+// need denormal inputs.)
 __device__ __forceinline__ uint32_t q4(const float n[8], int base, float s) {
-  uint32_t r = 0;
+#pragma clang fp contract(off)
+  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+  uint32_t b[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float q = rintf(__fmul_rn(n[base + j], s));
-    q = fminf(fmaxf(q, -127.f), 127.f);
-    r |= ((uint32_t)(int)q & 0xFFu) << (8 * j);
-  }
-  return r;
+  for (int j = 0; j < 4; ++j) b[j] = __float_as_uint(n[base + j] * s + kRound);
+  // perm selector bytes 0-3 pick bytes of the second operand, 4-7 of the first, 0x0c gives 0
+  return __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
 }
 
 // x + residual for 8 packed bf16 pairs: each sum in fp32 (one rounding), then
@@ -199,40 +206,40 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 // lane loads its CPL chunks of x and of gamma in one round trip, the sum of
 // squares and amax are reduced with wavefront shuffles (no barriers), and the
 // normed values stay in registers between the amax and the quantisation.
-template <int CPL, bool INT8, bool ADD>
+template <int CPL, bool INT8, bool ADD, bool G>
 __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual, uint16_t* __restrict__ x_add,
     const uint16_t* __restrict__ gamma, float eps, float inv_k, int64_t T, int64_t K,
     void* __restrict__ out, float* __restrict__ x_scale_out, float* __restrict__ rstd_out) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the row index is wavefront-uniform: readfirstlane lets the buffer resources live in scalar registers
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront: no barrier follows
-  const int nch = (int)(K >> 3);
-  const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * K);
-  const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
+  // Chunk c of this lane is the 16 bytes at (lane + 64 c) * 16 of the row.  All
+  // row accesses go through buffer resources sized to the row, so chunks past K
+  // read as zero and their stores are dropped: no per-chunk branches.
+  const uint32_t kb = (uint32_t)K * 2u;  // K <= 8192
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + t * K, kb);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, G ? kb : 0u);
+  auto off = [&](int c) -> uint32_t { return (uint32_t)(lane + 64 * c) * 16u; };
   u32x4 v[CPL], gv[CPL];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int idx = lane + 64 * c;
-    v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
-    gv[c] = (gr != nullptr && idx < nch) ? gr[idx] : u32x4{0u, 0u, 0u, 0u};
+    v[c] = buf_load16(rx, off(c));
+    if constexpr (G) gv[c] = buf_load16(rg, off(c));
   }
   if constexpr (ADD) {
     // x + residual: the sum is what the norm reads, and is written back
-    const u32x4* rr = reinterpret_cast<const u32x4*>(residual + t * K);
-    u32x4* xa = reinterpret_cast<u32x4*>(x_add + t * K);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(residual + t * K, kb);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(x_add + t * K, kb);
     u32x4 rv[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int idx = lane + 64 * c;
-      rv[c] = idx < nch ? rr[idx] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < CPL; ++c) rv[c] = buf_load16(rr, off(c));
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int idx = lane + 64 * c;
       v[c] = add_bf16x8(v[c], rv[c]);
-      if (idx < nch) xa[idx] = v[c];
+      __builtin_amdgcn_raw_buffer_store_b128(v[c], ra, off(c), 0, 0);
     }
   }
 #pragma unroll
@@ -247,21 +254,20 @@ __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
     for (int j = 0; j < 4; ++j) {
       n[c][2 * j] = __fmul_rn(bf16lo(v[c][j]), rstd);
       n[c][2 * j + 1] = __fmul_rn(bf16hi(v[c][j]), rstd);
-      if (gr != nullptr) {
+      if constexpr (G) {
         n[c][2 * j] = __fmul_rn(n[c][2 * j], bf16lo(gv[c][j]));
         n[c][2 * j + 1] = __fmul_rn(n[c][2 * j + 1], bf16hi(gv[c][j]));
       }
     }
   }
   if constexpr (!INT8) {
-    u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + t * K);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(out) + t * K, kb);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int idx = lane + 64 * c;
-      if (idx < nch)
-        orow[idx] = u32x4{pack_bf16x2(n[c][0], n[c][1]), pack_bf16x2(n[c][2], n[c][3]),
-                          pack_bf16x2(n[c][4], n[c][5]), pack_bf16x2(n[c][6], n[c][7])};
-    }
+    for (int c = 0; c < CPL; ++c)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{pack_bf16x2(n[c][0], n[c][1]), pack_bf16x2(n[c][2], n[c][3]), pack_bf16x2(n[c][4], n[c][5]),
+                pack_bf16x2(n[c][6], n[c][7])},
+          ro, off(c), 0, 0);
   } else {
     float amax = 0.f;
 #pragma unroll
@@ -271,12 +277,10 @@ __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
     amax = wave_max(amax);
     const float s = amax > 0.f ? __fdiv_rn(127.0f, amax) : 0.f;
     if (lane == 0 && x_scale_out != nullptr) x_scale_out[t] = __fdiv_rn(amax, 127.0f);
-    u32x2* orow = reinterpret_cast<u32x2*>(static_cast<int8_t*>(out) + t * K);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<int8_t*>(out) + t * K, (uint32_t)K);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int idx = lane + 64 * c;
-      if (idx < nch) orow[idx] = u32x2{q4(n[c], 0, s), q4(n[c], 4, s)};
-    }
+    for (int c = 0; c < CPL; ++c)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{q4(n[c], 0, s), q4(n[c], 4, s)}, ro, off(c) / 2u, 0, 0);
   }
 }
 
@@ -287,9 +291,15 @@ hipError_t launch_norm_wave(const uint16_t* x, const uint16_t* residual, uint16_
   const float inv_k = 1.0f / (float)K;
   const int64_t per = (K / 8 + 63) / 64;
   dim3 grid((unsigned)((T + 3) / 4)), block(kThreads);
-#define RNL_NORM_WAVE(C)                                                                                     \
-  hipLaunchKernelGGL((norm_rows_wave_kernel<C, INT8, ADD>), grid, block, 0, s, x, residual, x_add, gamma, eps, \
-                     inv_k, T, K, out, x_scale_out, rstd_out)
+#define RNL_NORM_WAVE(C)                                                                                      \
+  do {                                                                                                          \
+    if (gamma != nullptr)                                                                                       \
+      hipLaunchKernelGGL((norm_rows_wave_kernel<C, INT8, ADD, true>), grid, block, 0, s, x, residual, x_add,    \
+                         gamma, eps, inv_k, T, K, out, x_scale_out, rstd_out);                                  \
+    else                                                                                                        \
+      hipLaunchKernelGGL((norm_rows_wave_kernel<C, INT8, ADD, false>), grid, block, 0, s, x, residual, x_add,   \
+                         gamma, eps, inv_k, T, K, out, x_scale_out, rstd_out);                                  \
+  } while (0)
   if (per <= 1) RNL_NORM_WAVE(1);
   else if (per <= 2) RNL_NORM_WAVE(2);
   else if (per <= 4) RNL_NORM_WAVE(4);
