@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kMxThreads) void norm_rows_mx_kernel(const uint16_t
                                                                   uint8_t* __restrict__ s_out,
                                                                   float* __restrict__ rstd_out) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * (kMxThreads / kWave) + (threadIdx.x >> 6);
+  // the row index is wavefront-uniform: readfirstlane keeps the row's buffer resource in scalar registers
+  const int64_t t = (int64_t)blockIdx.x * (kMxThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;  // whole wavefront; no barrier follows
   const int nch = (int)(K >> 3);  // a multiple of 8: a 64-block is 8 whole chunks
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + t * K);
@@ -85,12 +86,19 @@ __global__ __launch_bounds__(kMxThreads) void norm_rows_mx_kernel(const uint16_t
   uint8_t* srow = s_out + t * (K >> 6);
 
   if constexpr (CPL > 0) {
-    u32x4 v[CPL];
+    // x and gamma chunks all requested up front (buffer loads: chunks past K read as
+    // zero); the stores of the normed codes then never wait on a gamma load
+    const uint32_t kb = (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + t * K, kb);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gamma, GAMMA ? kb : 0u);
+    u32x4 v[CPL], gv[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int idx = lane + kWave * c;
-      v[c] = idx < nch ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t o = (uint32_t)(lane + kWave * c) * 16u;
+      v[c] = buf_load16(rx, o);
+      if constexpr (GAMMA) gv[c] = buf_load16(rg, o);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the gamma loads stay in flight with the row's
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) ss += sumsq8(v[c]);
@@ -99,10 +107,17 @@ __global__ __launch_bounds__(kMxThreads) void norm_rows_mx_kernel(const uint16_t
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int idx = lane + kWave * c;
-      const bool live = idx < nch;
       float n[8];
-      normed8(v[c], gr, live ? idx : 0, rstd, n);
-      mx_emit(n, live, idx, lane, qrow, srow);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        n[2 * j] = __fmul_rn(bf16lo(v[c][j]), rstd);
+        n[2 * j + 1] = __fmul_rn(bf16hi(v[c][j]), rstd);
+        if constexpr (GAMMA) {
+          n[2 * j] = __fmul_rn(n[2 * j], bf16lo(gv[c][j]));
+          n[2 * j + 1] = __fmul_rn(n[2 * j + 1], bf16hi(gv[c][j]));
+        }
+      }
+      mx_emit(n, idx < nch, idx, lane, qrow, srow);
     }
   } else {
     float ss = 0.f;

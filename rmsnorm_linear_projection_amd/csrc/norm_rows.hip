@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
     v[c] = buf_load16(rx, off(c));
     if constexpr (G) gv[c] = buf_load16(rg, off(c));
   }
+  // keep the gamma loads here, in flight with the row's (the scheduler would
+  // otherwise sink them past the reduction, adding a round trip)
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (ADD) {
     // x + residual: the sum is what the norm reads, and is written back
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(residual + t * K, kb);
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows_wave_kernel(
     u32x4 rv[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) rv[c] = buf_load16(rr, off(c));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       v[c] = add_bf16x8(v[c], rv[c]);
