@@ -280,10 +280,11 @@ RNL_API size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, 
  *   gamma_q, gamma_k  [D] bf16 head-norm scales, or NULL; head_eps.
  *   cos, sin  [T, D/2] fp32 rotation tables, both or neither (no RoPE).
  *   head_rstd_out [T, Hq + Hkv] fp32 rstd of every normed head, or NULL.
- *   D must be a multiple of 16 and at most 512.
+ *   D must be a multiple of 16 and at most 512; T (Hq + Hkv) < 2^31.
  *
  * Errors: as rmsnorm_linear_bf16; RNL_ERR_NULL also when only one of
- * residual / x_add_out or of cos / sin is given; RNL_ERR_SHAPE for D.
+ * residual / x_add_out or of cos / sin is given; RNL_ERR_SHAPE for D and for
+ * T (Hq + Hkv).
  */
 RNL_API int preattn_qkv_bf16(const void* x, const void* residual, void* x_add_out, const void* gamma, float eps,
                              const void* W, void* y, float* rstd_out, const void* gamma_q, const void* gamma_k,
@@ -325,7 +326,7 @@ RNL_API int rms_norm_quant_int8(const void* x, const void* gamma, float eps, int
  * places of y_out, the other columns of y_out are not written.  y_out may be
  * y_in (in place) but may not overlap it otherwise (RNL_ERR_ARG).
  * rstd_out [T, H] or NULL.  ld and col0 multiples of 8; D a multiple of 16,
- * at most 512; col0 + H D <= ld.
+ * at most 512; col0 + H D <= ld; T H < 2^31 (RNL_ERR_SHAPE otherwise).
  */
 RNL_API int head_rms_norm_bf16(const void* y_in, void* y_out, const void* gamma, float eps, const float* cos,
                                const float* sin, float* rstd_out, int64_t T, int64_t ld, int64_t col0, int64_t H,

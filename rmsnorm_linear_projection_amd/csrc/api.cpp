@@ -38,6 +38,7 @@ int hip_status(hipError_t e, const char* what) {
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxK_int8 = 133144;  // K * 127 * 127 <= 2^31 - 1
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 32-bit tile offsets in range
+constexpr int64_t kMaxHeads = (int64_t(1) << 31) - 1;  // T * heads: the per-head kernel divides in 32 bits
 constexpr int64_t kMaxN_fp32w = int64_t(1) << 20;  // fp32 weights: column blocks of 32 fit one grid axis
 constexpr int64_t kSmallM = 16;  // at most this many activation rows: weight-streaming kernel
 constexpr int64_t kFusedNormM = 4;  // at most this many (and no residual): the norm runs inside it
@@ -483,6 +484,7 @@ int preattn_qkv_bf16(const void* x, const void* residual, void* x_add_out, const
                 (long long)K, (long long)Hq, (long long)Hkv);
   RNL_TRY(check_head_dim(D));
   if (Hq + 2 * Hkv > kMaxDim / D) return fail(RNL_ERR_SHAPE, "(Hq + 2 Hkv) * D must be <= 2^24");
+  if (T > kMaxHeads / (Hq + Hkv)) return fail(RNL_ERR_SHAPE, "T * (Hq + Hkv) must be < 2^31");
   RNL_TRY(check_eps(head_eps));
   RNL_ALIGN(gamma_q, 16, "gamma_q");
   RNL_ALIGN(gamma_k, 16, "gamma_k");
@@ -511,6 +513,7 @@ int head_rms_norm_bf16(const void* y_in, void* y_out, const void* gamma, float e
   if (T > kMaxDim || ld > kMaxDim) return fail(RNL_ERR_SHAPE, "T and ld must be <= 2^24");
   if (ld % 8 != 0 || col0 % 8 != 0) return fail(RNL_ERR_SHAPE, "ld and col0 must be multiples of 8");
   if (H > (ld - col0) / D) return fail(RNL_ERR_SHAPE, "col0 + H * D exceeds the row length ld");
+  if (T > kMaxHeads / H) return fail(RNL_ERR_SHAPE, "T * H must be < 2^31");
   RNL_TRY(check_eps(eps));
   RNL_ALIGN(y_in, 16, "y_in");
   RNL_ALIGN(y_out, 16, "y_out");

@@ -13,13 +13,13 @@
 // operators under contract(off), so no FMA is formed), and the result is a
 // fixed function of the fp32 rstd.
 //
-// Layout of the work: a head of D bf16 values is D/8 16-byte chunks, one per
-// lane; a group of GP lanes (D/8 rounded up to a power of two) takes one head,
-// so a wavefront takes 64/GP heads at once.  The sum of squares is reduced
-// with xor shuffles inside the group; the RoPE partner chunk (i + D/2 for the
-// first half, i - D/2 for the second) comes from the partner lane by a
-// shuffle, so every chunk is read from memory once, by the lane that writes
-// it back -- y_out may therefore be y_in.
+// Layout of the work: a head of D bf16 values is D/8 16-byte chunks, and lane
+// i of the head's group of GP lanes (D/16 rounded up to a power of two) holds
+// chunk i and chunk i + D/16, i.e. both members of every rotate-half pair it
+// owns, so the rotation needs no data from other lanes and reads each angle
+// once.  All loads (the two chunks, their gammas, the angles) are issued
+// together.  The sum of squares is reduced inside the group with DPP moves;
+// each chunk is written back by the lane that read it, so y_out may be y_in.
 #include "launch.h"
 #include "rows.cuh"
 
@@ -27,6 +27,23 @@ namespace rnl {
 namespace {
 
 constexpr int kHeadThreads = 256;
+
+// sum over the GP lanes of a group (GP a power of two <= 32, groups aligned to
+// GP lanes); every lane of the group ends with the same value
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+template <int GP>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (GP >= 2) v += dpp_f<0xB1>(v);   // quad_perm 1,0,3,2: lane ^ 1
+  if constexpr (GP >= 4) v += dpp_f<0x4E>(v);   // quad_perm 2,3,0,1: lane ^ 2
+  if constexpr (GP >= 8) v += dpp_f<0x141>(v);  // row_half_mirror: the two quads of 8 lanes
+  if constexpr (GP >= 16) v += dpp_f<0x140>(v); // row_mirror: the two halves of 16 lanes
+  if constexpr (GP >= 32) v += __shfl_xor(v, 16, kWave);
+  return v;
+}
 
 template <int GP, bool ROPE>
 __global__ __launch_bounds__(kHeadThreads) void head_norm_kernel(
@@ -38,53 +55,72 @@ __global__ __launch_bounds__(kHeadThreads) void head_norm_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gl = lane & (GP - 1);
   const int64_t head = ((int64_t)blockIdx.x * (kHeadThreads / kWave) + wave) * HPW + lane / GP;
-  const int G = D >> 3;  // chunks per head
+  const int P = D >> 4;  // chunk pairs per head
   const bool live = head < nheads_total;
-  const bool act = live && gl < G;
-  const int64_t t = live ? head / H : 0;
-  const int h = live ? (int)(head - t * H) : 0;
-  const uint16_t* row_in = y_in + t * ld + col0 + (int64_t)h * D;
+  const bool act = live && gl < P;
+  // nheads_total = T * H < 2^31 (checked on the host): 32-bit division
+  const uint32_t hu = live ? (uint32_t)head : 0u;
+  const uint32_t tu = hu / (uint32_t)H;
+  const int64_t t = (int64_t)tu;
+  const int h = (int)(hu - tu * (uint32_t)H);
+  const int64_t row = t * ld + col0 + (int64_t)h * D;
+  const int c0 = gl * 8, c1 = (gl + P) * 8;  // first elements of the lane's two chunks
+  const uint16_t* gamma = h < H1 ? gamma1 : gamma2;
 
-  u32x4 v = act ? *reinterpret_cast<const u32x4*>(row_in + gl * 8) : u32x4{0u, 0u, 0u, 0u};
-  float ss = sumsq8(v);
-#pragma unroll
-  for (int off = GP / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-  const float rstd = rstd_from_sumsq(ss, inv_d, eps);
-  const u32x4* gr = reinterpret_cast<const u32x4*>(h < H1 ? gamma1 : gamma2);
-
-  float n[8];
-  normed8(v, gr, act ? gl : 0, rstd, n);
+  // Every lane loads unconditionally (inactive lanes from the first chunk of y,
+  // always in bounds, and never store), so that all the loads are issued back
+  // to back without branches between them.
+  const int64_t e0 = act ? row + c0 : 0, e1 = act ? row + c1 : 0;
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(y_in + e0);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(y_in + e1);
+  const bool g_on = act && gamma != nullptr;
+  const uint16_t* gsrc = g_on ? gamma : y_in;
+  const u32x4 g0 = *reinterpret_cast<const u32x4*>(gsrc + (g_on ? c0 : 0));
+  const u32x4 g1 = *reinterpret_cast<const u32x4*>(gsrc + (g_on ? c1 : 0));
+  f32x4 cs[2], sn[2];
   if constexpr (ROPE) {
-    // partner chunk of the rotate-half pairing, fetched from its lane
-    const int half = G >> 1;
-    const int partner = gl < half ? gl + half : gl - half;
-    const int src = (lane & ~(GP - 1)) + (gl < G ? partner : gl);
-    u32x4 pv;
+    const int64_t ab = act ? t * (int64_t)(D >> 1) + c0 : 0;  // angles of pair elements c0 .. c0 + 7
+    cs[0] = *reinterpret_cast<const f32x4*>(cos_t + ab);
+    cs[1] = *reinterpret_cast<const f32x4*>(cos_t + ab + 4);
+    sn[0] = *reinterpret_cast<const f32x4*>(sin_t + ab);
+    sn[1] = *reinterpret_cast<const f32x4*>(sin_t + ab + 4);
+  }
+  // lanes that own no chunk (past D/16, or past the last head) add nothing to their group's sum
+  const float ss = act ? sumsq8(v0) + sumsq8(v1) : 0.f;
+  const float rstd = rstd_from_sumsq(group_sum<GP>(ss), inv_d, eps);
+
+  float n0[8], n1[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pv[j] = (uint32_t)__shfl((int)v[j], src, kWave);
-    float pn[8];
-    normed8(pv, gr, act ? partner : 0, rstd, pn);
-    if (act) {
-      const int64_t ab = t * (int64_t)(D >> 1) + (int64_t)(gl < half ? gl : gl - half) * 8;
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cos_t + ab);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(cos_t + ab + 4);
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sin_t + ab);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(sin_t + ab + 4);
-      const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-      const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      const bool first = gl < half;
+  for (int j = 0; j < 4; ++j) {
+    n0[2 * j] = bf16lo(v0[j]) * rstd;
+    n0[2 * j + 1] = bf16hi(v0[j]) * rstd;
+    n1[2 * j] = bf16lo(v1[j]) * rstd;
+    n1[2 * j + 1] = bf16hi(v1[j]) * rstd;
+  }
+  if (g_on) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = n[e] * c[e];
-        const float b = pn[e] * s[e];
-        n[e] = first ? a - b : a + b;
-      }
+    for (int j = 0; j < 4; ++j) {
+      n0[2 * j] = n0[2 * j] * bf16lo(g0[j]);
+      n0[2 * j + 1] = n0[2 * j + 1] * bf16hi(g0[j]);
+      n1[2 * j] = n1[2 * j] * bf16lo(g1[j]);
+      n1[2 * j + 1] = n1[2 * j + 1] * bf16hi(g1[j]);
+    }
+  }
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = cs[e >> 2][e & 3], s = sn[e >> 2][e & 3];
+      const float lo = n0[e] * c - n1[e] * s;  // element i
+      const float hi = n1[e] * c + n0[e] * s;  // element i + D/2
+      n0[e] = lo;
+      n1[e] = hi;
     }
   }
   if (act) {
-    uint16_t* row_out = y_out + t * ld + col0 + (int64_t)h * D;
-    *reinterpret_cast<u32x4*>(row_out + gl * 8) =
-        u32x4{pack_bf16x2(n[0], n[1]), pack_bf16x2(n[2], n[3]), pack_bf16x2(n[4], n[5]), pack_bf16x2(n[6], n[7])};
+    *reinterpret_cast<u32x4*>(y_out + row + c0) =
+        u32x4{pack_bf16x2(n0[0], n0[1]), pack_bf16x2(n0[2], n0[3]), pack_bf16x2(n0[4], n0[5]), pack_bf16x2(n0[6], n0[7])};
+    *reinterpret_cast<u32x4*>(y_out + row + c1) =
+        u32x4{pack_bf16x2(n1[0], n1[1]), pack_bf16x2(n1[2], n1[3]), pack_bf16x2(n1[4], n1[5]), pack_bf16x2(n1[6], n1[7])};
     if (gl == 0 && rstd_out != nullptr) rstd_out[head] = rstd;
   }
 }
@@ -95,10 +131,11 @@ hipError_t launch_head_norm_bf16(const uint16_t* y_in, uint16_t* y_out, int64_t 
                                  int64_t H, int64_t D, int64_t H1, const uint16_t* gamma1, const uint16_t* gamma2,
                                  float eps, const float* cos_t, const float* sin_t, float* rstd_out,
                                  hipStream_t s) {
-  const int G = (int)(D / 8);
-  int gp = 8;
-  while (gp < G) gp *= 2;
+  const int P = (int)(D / 16);  // lanes per head
+  int gp = 1;
+  while (gp < P) gp *= 2;
   const int64_t total = T * H;
+  if (total > 0x7fffffff) return hipErrorInvalidValue;  // the kernel divides head indices in 32 bits
   const int64_t heads_per_block = (kHeadThreads / kWave) * (kWave / gp);
   const dim3 grid((unsigned)((total + heads_per_block - 1) / heads_per_block)), block(kHeadThreads);
   const float inv_d = 1.0f / (float)D;
@@ -109,10 +146,12 @@ hipError_t launch_head_norm_bf16(const uint16_t* y_in, uint16_t* y_out, int64_t 
 #define RNL_HEAD_GP(GP) \
   if (rope) RNL_HEAD(GP, true); else RNL_HEAD(GP, false)
   switch (gp) {
+    case 1: RNL_HEAD_GP(1); break;
+    case 2: RNL_HEAD_GP(2); break;
+    case 4: RNL_HEAD_GP(4); break;
     case 8: RNL_HEAD_GP(8); break;
     case 16: RNL_HEAD_GP(16); break;
-    case 32: RNL_HEAD_GP(32); break;
-    default: RNL_HEAD_GP(64); break;
+    default: RNL_HEAD_GP(32); break;
   }
 #undef RNL_HEAD_GP
 #undef RNL_HEAD
