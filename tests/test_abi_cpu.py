@@ -200,6 +200,7 @@ def preattn_call(lib, x=FAKE, r=NULL, xa=NULL, g=NULL, eps=1e-6, W=FAKE, y=FAKE,
     (dict(Hq=0), "RNL_ERR_SHAPE"),
     (dict(Hkv=-1), "RNL_ERR_SHAPE"),
     (dict(Hq=1 << 20), "RNL_ERR_SHAPE"),
+    (dict(T=1 << 24, Hq=128, Hkv=0, D=16), "RNL_ERR_SHAPE"),  # T * (Hq + Hkv) = 2^31 heads
     (dict(heps=-1.0), "RNL_ERR_ARG"),
     (dict(gq=ODD), "RNL_ERR_ALIGN"),
     (dict(cos=ctypes.c_void_p(0x40004), sin=ctypes.c_void_p(0x50000)), "RNL_ERR_ALIGN"),
@@ -230,6 +231,7 @@ def head_call(lib, yi=FAKE, yo=FAKE, g=NULL, eps=1e-6, cos=NULL, sin=NULL, rstd=
     (dict(ld=516, H=1), "RNL_ERR_SHAPE"),    # ld not a multiple of 8
     (dict(D=40, H=1), "RNL_ERR_SHAPE"),      # D not a multiple of 16
     (dict(T=0), "RNL_ERR_SHAPE"),
+    (dict(T=1 << 24, ld=4096, H=256, D=16), "RNL_ERR_SHAPE"),  # T * H = 2^32 heads
     (dict(eps=float("nan")), "RNL_ERR_ARG"),
     (dict(yo=ctypes.c_void_p(0x10000 + 1024)), "RNL_ERR_ARG"),  # overlaps y_in without being it
     (dict(g=ODD), "RNL_ERR_ALIGN"),
