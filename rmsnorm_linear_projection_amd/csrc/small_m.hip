@@ -346,6 +346,27 @@ int small_m_rows(int64_t N) {
   return best;
 }
 
+namespace {
+// Weight rows per workgroup of the fused-norm kernel: one 16-row MFMA block
+// (R <= 16), the fewest rows on the busiest CU, then the largest R.  Measured
+// against small_m_rows' choice (which allows two blocks): N = 6144, K = 4096:
+// R = 12 12.7 us against R = 24 13.3; N = 24576, K = 1536: R = 16 16.9 us
+// against R = 32 20.1.
+int small_m_norm_rows(int64_t N) {
+  int best = 16;
+  int64_t best_load = INT64_MAX;
+  for (int R = 16; R >= 4; R -= 4) {
+    const int64_t wgs = (N + R - 1) / R;
+    const int64_t load = ((wgs + kCUs - 1) / kCUs) * R;
+    if (load < best_load) {
+      best_load = load;
+      best = R;
+    }
+  }
+  return best;
+}
+}  // namespace
+
 size_t small_m_norm_lds(int64_t M, int64_t K) {
   const size_t rows = (size_t)M * (size_t)((K + 31) / 32) * 64u;
   const size_t red = 3u * 2u * 64u * sizeof(f32x4);  // (NW - 1) x NB x 64 accumulators, at most
@@ -355,7 +376,7 @@ size_t small_m_norm_lds(int64_t M, int64_t K) {
 hipError_t launch_small_m_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
                                     void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
                                     hipStream_t s) {
-  const int R = small_m_rows(N);
+  const int R = small_m_norm_rows(N);
   dim3 grid((unsigned)((N + R - 1) / R)), block(256);
   const bool ob = out_kind == OUT_BF16;
   const float inv_k = 1.0f / (float)K;
@@ -366,11 +387,8 @@ hipError_t launch_small_m_norm_bf16(const uint16_t* X, const uint16_t* gamma, fl
                      rstd_out, (int)M, (int)K, (int)N, R)
 #define RNL_SMALL_MN_G(NB, O) \
   if (gamma != nullptr) RNL_SMALL_MN(NB, O, true); else RNL_SMALL_MN(NB, O, false)
-  if (R <= 16) {
-    if (ob) RNL_SMALL_MN_G(1, true); else RNL_SMALL_MN_G(1, false);
-  } else {
-    if (ob) RNL_SMALL_MN_G(2, true); else RNL_SMALL_MN_G(2, false);
-  }
+  // R <= 16: one MFMA block of weight rows
+  if (ob) RNL_SMALL_MN_G(1, true); else RNL_SMALL_MN_G(1, false);
 #undef RNL_SMALL_MN_G
 #undef RNL_SMALL_MN
   return hipGetLastError();
