@@ -179,6 +179,7 @@ class Setup:
         self.t = t
         self.kernel = None
         self.kernel_key = None
+        self.vendor = None  # (description, fn(i)): the vendor library on the dominant kernel's operands
         if kind == "bf16":
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(max(1, rnl.workspace_bytes("add_bf16" if w.get("add") else "bf16", T, K, N)),
@@ -207,6 +208,8 @@ class Setup:
                 self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
                 self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
                 self.kern_units = ("bf16", flops_of(w))
+            Wv = Wc if T <= 16 else [t["W"]]
+            self.vendor = ("torch.matmul(a, W.t()), bf16", lambda i: torch.matmul(a, Wv[i % len(Wv)].t(), out=y))
         elif kind == "mxfp8":
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(rnl.workspace_bytes("mxfp8", T, K, N), dtype=torch.uint8, device=dev)
@@ -234,6 +237,8 @@ class Setup:
                 self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
                 self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
                 self.kern_units = ("bf16", flops_of(w))
+            Wv = Wc if T <= 16 else [t["W"]]
+            self.vendor = ("torch.matmul(a, W.t()), bf16", lambda i: torch.matmul(a, Wv[i % len(Wv)].t(), out=y))
         elif kind == "fp32w":
             y = torch.empty((T, N), dtype=torch.float32, device=dev)
             ws = torch.empty(max(1, rnl.workspace_bytes("bf16", T, K, N, w_dtype=torch.float32,
@@ -244,6 +249,9 @@ class Setup:
             self.kernel, self.kernel_key = "skinny_partial_kernel+skinny_finalize_kernel", "skinny"
             self.kern = self.step
             self.kern_units = ("hbm", bytes_of(w))
+            xf = [v.float() for v in xc]  # the vendor contraction takes fp32 rows
+            self.vendor = ("torch.matmul(x.float(), W.t()), fp32 (the contraction only: no norm)",
+                           lambda i: torch.matmul(xf[i % len(xf)], t["W"].t(), out=y))
         elif kind == "int8":
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(rnl.workspace_bytes("int8", T, K, N), dtype=torch.uint8, device=dev)
@@ -253,6 +261,10 @@ class Setup:
             self.kernel, self.kernel_key = "gemm_nt_kernel<int8>", "gemm"
             self.kern = lambda i: rnl.linear_int8(xq, xs, t["Wq"], t["w_scale"], y=y)
             self.kern_units = ("int8", flops_of(w))
+            acc = torch.empty((T, N), dtype=torch.int32, device=dev)
+            Wqt = t["Wq"].t()
+            self.vendor = ("torch._int_mm(xq, Wq.t()), int32 accumulators (no dequant)",
+                           lambda i: torch._int_mm(xq, Wqt, out=acc))
         elif kind == "mla":
             R, Rkv = w["R"], w["Rkv"]
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
@@ -266,6 +278,7 @@ class Setup:
             self.kernel, self.kernel_key = "gemm_nt_kernel<bf16> (stage 2, qr . W_b^T)", "gemm"
             self.kern = lambda i: rnl.linear_bf16(qr, t["W_b"], y=y)
             self.kern_units = ("bf16", 2.0 * T * R * N)
+            self.vendor = ("torch.matmul(qr, W_b.t()), bf16 (stage 2)", lambda i: torch.matmul(qr, t["W_b"].t(), out=y))
         else:
             R = w["R"]
             y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
@@ -277,6 +290,7 @@ class Setup:
             self.kernel, self.kernel_key = "gemm_nt_kernel<bf16> (stage 2, qr . W_b^T)", "gemm"
             self.kern = lambda i: rnl.linear_bf16(qr, t["W_b"], y=y)
             self.kern_units = ("bf16", 2.0 * T * R * N)
+            self.vendor = ("torch.matmul(qr, W_b.t()), bf16 (stage 2)", lambda i: torch.matmul(qr, t["W_b"].t(), out=y))
         torch.cuda.synchronize()
 
 
@@ -398,7 +412,7 @@ def cpu_baseline(setup, target_s=8.0):
             "sample": f"first {rows} of {T} token rows, {calls} call(s), {per_call:.3f} s per call"}
 
 
-def bench_one(name, steps, warmup, with_cpu=True, graph=True):
+def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False):
     import torch
 
     w = WORKLOADS[name]
@@ -438,6 +452,15 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True):
                      "kernel_ms": round(kms, 6),
                      "traffic": None if traffic is None else int(traffic)},
     }
+    if vendor and s.vendor is not None:
+        # context, not a target: the vendor library (hipBLASLt / rocBLAS through torch) timed the same
+        # way on the same operands as the dominant kernel, in the same process
+        desc, fn = s.vendor
+        try:
+            line["vendor"] = {"op": desc, "ms": round(time_loop(fn, steps, warmup, graph)[0], 6),
+                              "kernel_ms": round(kms, 6)}
+        except RuntimeError as e:  # an op the installed torch cannot run or capture
+            line["vendor"] = {"op": desc, "error": str(e).splitlines()[0][:200]}
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(s)
     del s
@@ -518,6 +541,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured graph")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the vendor library (torch.matmul / torch._int_mm) on the dominant kernel's operands")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the plain copy that calibrates the HBM byte counters")
     ap.add_argument("--record-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -546,7 +571,8 @@ def main():
         __graft_entry__.build()
     names = sorted(WORKLOADS, key=lambda n: n != DEFAULT) if args.all else [args.workload]
     for n in names:
-        print(json.dumps(bench_one(n, args.steps, args.warmup, with_cpu=not args.no_cpu, graph=not args.eager)),
+        print(json.dumps(bench_one(n, args.steps, args.warmup, with_cpu=not args.no_cpu, graph=not args.eager,
+                                   vendor=args.vendor)),
               flush=True)
 
 
