@@ -595,6 +595,9 @@ def _np(t):
     (3, 24576, 0, 128, 192),   # 24 lanes per head, padded to 32
     (2, 1536, 512, 2, 512),    # one head per wavefront
     (1, 136, 8, 1, 128),
+    (4, 512, 16, 5, 48),       # 3 chunk pairs per head: groups of 4 lanes, one idle
+    (3, 400, 0, 5, 80),        # 5 chunk pairs per head: groups of 8 lanes, three idle
+    (6, 96, 32, 2, 32),        # 2 chunk pairs per head
 ])
 @pytest.mark.parametrize("gamma,rope,inplace", [(True, True, True), (False, True, False), (True, False, False),
                                                 (False, False, True)])
