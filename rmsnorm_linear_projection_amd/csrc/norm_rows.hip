@@ -1,9 +1,10 @@
 // Row-wise RMSNorm pre-pass for the large-T GEMM paths (gfx950).
 //
-// Rows of up to 8192 values: one wavefront per row (shuffle reductions only).
-// Longer rows: one 256-thread workgroup per row, the row read once with 16-byte
-// coalesced loads (kept in registers when K <= 16384) and the fp32 sum of
-// squares reduced across the wavefronts.  The normed row is written either as
+// Rows of up to 8192 values, at least 256 of them or shorter than 2048: one
+// wavefront per row (shuffle reductions only).  Longer rows, or fewer rows than
+// CUs: one 256-thread workgroup per row, the row read once with 16-byte coalesced loads
+// (kept in registers when K <= 16384) and the fp32 sum of squares reduced
+// across the wavefronts.  The normed row is written either as
 // bf16 (the A operand of the bf16 GEMM) or as per-token symmetric int8 plus
 // its dequant scale (the A operand of the int8 GEMM).
 //
@@ -75,6 +76,22 @@ __device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
   return r;
 }
 
+// normed8 with the gamma chunk already loaded (g is ignored when has_g is false)
+__device__ __forceinline__ void normed8g(u32x4 w, u32x4 g, bool has_g, float rstd, float n[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    n[2 * j] = __fmul_rn(bf16lo(w[j]), rstd);
+    n[2 * j + 1] = __fmul_rn(bf16hi(w[j]), rstd);
+  }
+  if (has_g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      n[2 * j] = __fmul_rn(n[2 * j], bf16lo(g[j]));
+      n[2 * j + 1] = __fmul_rn(n[2 * j + 1], bf16hi(g[j]));
+    }
+  }
+}
+
 // Row sources: chunk idx (8 consecutive elements, packed bf16) of row t.
 // keep(t, idx, v) is called once per chunk in the first pass over the row.
 struct RowBf16 {
@@ -126,13 +143,20 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
   const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
 
   constexpr int NV = CPT > 0 ? CPT : 1;
-  u32x4 v[NV];
+  u32x4 v[NV], gv[NV];
+  const bool has_g = gamma != nullptr;
   float ss = 0.f;
   if constexpr (CPT > 0) {
+    // the gamma chunks are requested with the row's, not after the reduction
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * kThreads;
       v[c] = idx < nch ? row(t, idx) : u32x4{0u, 0u, 0u, 0u};
+      gv[c] = (has_g && idx < nch) ? gr[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kThreads;
       if (idx < nch) row.keep(t, idx, v[c]);
       ss += sumsq8(v[c]);
     }
@@ -149,9 +173,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 
   if constexpr (!INT8) {
     u32x4* orow = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + t * K);
-    auto emit = [&](u32x4 w, int idx) {
-      float n[8];
-      normed8(w, gr, idx, rstd, n);
+    auto store = [&](const float n[8], int idx) {
       orow[idx] = u32x4{pack_bf16x2(n[0], n[1]), pack_bf16x2(n[2], n[3]), pack_bf16x2(n[4], n[5]),
                         pack_bf16x2(n[6], n[7])};
     };
@@ -159,10 +181,16 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + c * kThreads;
-        if (idx < nch) emit(v[c], idx);
+        float n[8];
+        normed8g(v[c], gv[c], has_g, rstd, n);
+        if (idx < nch) store(n, idx);
       }
     } else {
-      for (int idx = tid; idx < nch; idx += kThreads) emit(row(t, idx), idx);
+      for (int idx = tid; idx < nch; idx += kThreads) {
+        float n[8];
+        normed8(row(t, idx), gr, idx, rstd, n);
+        store(n, idx);
+      }
     }
   } else {
     float amax = 0.f;
@@ -175,8 +203,10 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
     if constexpr (CPT > 0) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int idx = tid + c * kThreads;
-        if (idx < nch) amax_of(v[c], idx);
+        float n[8];
+        normed8g(v[c], gv[c], has_g, rstd, n);  // chunks past K are zero
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(n[j]));
       }
     } else {
       for (int idx = tid; idx < nch; idx += kThreads) amax_of(row(t, idx), idx);
@@ -194,7 +224,9 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + c * kThreads;
-        if (idx < nch) emit(v[c], idx);
+        float n[8];
+        normed8g(v[c], gv[c], has_g, rstd, n);
+        if (idx < nch) orow[idx] = u32x2{q4(n, 0, s), q4(n, 4, s)};
       }
     } else {
       for (int idx = tid; idx < nch; idx += kThreads) emit(row(t, idx), idx);
@@ -314,6 +346,13 @@ hipError_t launch_norm_wave(const uint16_t* x, const uint16_t* residual, uint16_
 }
 
 constexpr int64_t kWaveRowMaxK = 8192;
+// Fewer rows than CUs, each with a chunk for every thread of a workgroup: a
+// workgroup per row (four wavefronts share the row, so each runs a quarter of the
+// arithmetic) finishes sooner than a wavefront per row.
+constexpr int64_t kWaveRowMinT = 256;
+inline bool wave_rows(int64_t T, int64_t K) {
+  return K <= kWaveRowMaxK && (T >= kWaveRowMinT || K < 8 * kThreads);
+}
 
 template <bool INT8, class Row>
 hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int64_t K, void* out,
@@ -338,7 +377,7 @@ hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int
 
 hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
-  if (K <= kWaveRowMaxK)
+  if (wave_rows(T, K))
     return launch_norm_wave<false, false>(x, nullptr, nullptr, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
   return launch_norm<false>(RowBf16{x, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
@@ -351,7 +390,7 @@ hipError_t launch_norm_rows_bf16_strided(const uint16_t* x, int64_t ld, const ui
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                                  int64_t K, int8_t* q_out, float* x_scale_out, float* rstd_out,
                                  hipStream_t s) {
-  if (K <= kWaveRowMaxK)
+  if (wave_rows(T, K))
     return launch_norm_wave<true, false>(x, nullptr, nullptr, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
   return launch_norm<true>(RowBf16{x, K}, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
 }
@@ -359,7 +398,7 @@ hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float
 hipError_t launch_add_norm_rows_bf16(const uint16_t* x, const uint16_t* residual, uint16_t* x_add,
                                      const uint16_t* gamma, float eps, int64_t T, int64_t K, uint16_t* a_out,
                                      float* rstd_out, hipStream_t s) {
-  if (K <= kWaveRowMaxK)
+  if (wave_rows(T, K))
     return launch_norm_wave<false, true>(x, residual, x_add, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
   return launch_norm<false>(RowAddBf16{x, residual, x_add, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
@@ -367,7 +406,7 @@ hipError_t launch_add_norm_rows_bf16(const uint16_t* x, const uint16_t* residual
 hipError_t launch_add_norm_rows_int8(const uint16_t* x, const uint16_t* residual, uint16_t* x_add,
                                      const uint16_t* gamma, float eps, int64_t T, int64_t K, int8_t* q_out,
                                      float* x_scale_out, float* rstd_out, hipStream_t s) {
-  if (K <= kWaveRowMaxK)
+  if (wave_rows(T, K))
     return launch_norm_wave<true, true>(x, residual, x_add, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
   return launch_norm<true>(RowAddBf16{x, residual, x_add, K}, gamma, eps, T, K, q_out, x_scale_out, rstd_out, s);
 }
