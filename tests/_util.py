@@ -52,3 +52,36 @@ def fraction_to_f32(fr: Fraction) -> np.float32:
     if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
         fl += 1
     return np.float32(sign * float(fl * scale))
+
+
+def parse_fraction(tok: str) -> float:
+    """A fixture value written as an exact decimal or as p/q."""
+    if "/" in tok:
+        a, b = tok.split("/")
+        return float(Fraction(a) / Fraction(b))
+    return float(tok)
+
+
+def golden_cases(path: str) -> list[dict]:
+    """Cases of a tests/golden fixture: "case <name>" opens a case; "K", "eps",
+    "gamma" and per-row "x", "q", "x_scale" lines follow."""
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {"name": vals[0], "x": [], "q": [], "x_scale": []}
+            cases.append(cur)
+        elif key == "K":
+            cur[key] = int(vals[0])
+        elif key == "eps":
+            cur[key] = float(vals[0])
+        elif key == "gamma":
+            cur[key] = [parse_fraction(v) for v in vals]
+        elif key in ("x", "q"):
+            cur[key].append([parse_fraction(v) for v in vals])
+        elif key == "x_scale":
+            cur[key].append(parse_fraction(vals[0]))
+    return cases

@@ -26,7 +26,7 @@ import torch
 import oracle as O
 import rmsnorm_linear_projection_amd as rnl
 import synthetic
-from tests._util import bits, f32, ulp_diff
+from tests._util import bits, f32, golden_cases, ulp_diff
 
 pytestmark = pytest.mark.gpu
 
@@ -383,6 +383,31 @@ def test_atom_rms_norm_quant_int8(T, K):
     n, _ = O.rms_norm_rows(bits(case["x"]), bits(case["gamma"]), EPS, rstd=rstd.cpu().numpy())
     q, s, _ = O.quant_rows(n)
     assert np.array_equal(xq.cpu().numpy(), q) and np.array_equal(xs.cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("reps,T", [
+    (2, 4),      # K = 16: a wavefront per row
+    (512, 4),    # K = 4096, few rows: a workgroup per row
+    (512, 300),  # K = 4096, 300 rows: a wavefront per row
+])
+def test_atom_quant_int8_golden_ties(reps, T):
+    """The hand-derived rows of tests/golden/int8_quant_ties.txt (eps = 0, rstd = 1, s = 64 exactly, so n * s
+    lands on exact .5 ties), each row repeated `reps` times along K and the rows cycled to T: the device's codes
+    and x_scale must be the fixture's, whatever the kernel."""
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "int8_quant_ties.txt")
+    for c in golden_cases(golden):
+        x = np.tile(np.array(c["x"], dtype=np.float32), (1, reps))
+        q = np.tile(np.array(c["q"], dtype=np.int8), (1, reps))
+        xs = np.array(c["x_scale"], dtype=np.float32)
+        pick = np.arange(T) % x.shape[0]
+        g = np.tile(np.array(c["gamma"], dtype=np.float32), reps)
+        xd = torch.from_numpy(x[pick]).to(torch.bfloat16).cuda()
+        gd = torch.from_numpy(g).to(torch.bfloat16).cuda()
+        assert np.array_equal(f32(xd.cpu()), x[pick]) and np.array_equal(f32(gd.cpu()), g), "fixture not bf16-exact"
+        xq, x_scale = rnl.rms_norm_quant_int8(xd, gd, c["eps"])
+        torch.cuda.synchronize()
+        assert np.array_equal(xq.cpu().numpy(), q[pick]), f"{c['name']}: codes differ"
+        assert np.array_equal(x_scale.cpu().numpy(), xs[pick]), f"{c['name']}: x_scale differs"
 
 
 @pytest.mark.parametrize("M,K,N", [(33, 72, 17), (300, 1032, 200), (4000, 264, 6100)])

@@ -18,7 +18,7 @@ import torch
 
 import oracle as O
 import synthetic
-from tests._util import bits, fraction_to_f32, ulp_diff
+from tests._util import bits, fraction_to_f32, golden_cases, ulp_diff
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(12345)
@@ -264,38 +264,8 @@ def test_fp32_projection_exact_and_keeps_fp32():
 # ---------------------------------------------------------------------------
 # int8 W8A8
 # ---------------------------------------------------------------------------
-def _parse_fraction(tok):
-    if "/" in tok:
-        a, b = tok.split("/")
-        return float(Fraction(a) / Fraction(b))
-    return float(tok)
-
-
-def _golden_cases(path):
-    cases, cur = [], None
-    for line in open(path):
-        line = line.strip()
-        if not line or line.startswith("#"):
-            continue
-        key, *vals = line.split()
-        if key == "case":
-            cur = {"name": vals[0], "x": [], "q": [], "x_scale": []}
-            cases.append(cur)
-        elif key in ("K",):
-            cur[key] = int(vals[0])
-        elif key == "eps":
-            cur[key] = float(vals[0])
-        elif key == "gamma":
-            cur[key] = [_parse_fraction(v) for v in vals]
-        elif key in ("x", "q"):
-            cur[key].append([_parse_fraction(v) for v in vals])
-        elif key == "x_scale":
-            cur[key].append(_parse_fraction(vals[0]))
-    return cases
-
-
 def test_int8_quant_golden_ties():
-    for c in _golden_cases(os.path.join(GOLDEN, "int8_quant_ties.txt")):
+    for c in golden_cases(os.path.join(GOLDEN, "int8_quant_ties.txt")):
         x = O.f32_to_bf16_bits(np.array(c["x"], dtype=np.float32))
         g = O.f32_to_bf16_bits(np.array(c["gamma"], dtype=np.float32))
         # the fixture's values must be bf16-exact
