@@ -457,6 +457,23 @@ def test_atom_linear_int8(M, K, N):
     assert np.array_equal(y.cpu().numpy(), y_ref)
 
 
+def test_atom_linear_int8_large_tiles():
+    """Enough 256 x 192 tiles for one per CU (eight-wavefront workgroups), ragged in M and N: sampled rows of
+    the int32 accumulators and of the dequantised output, bit for bit."""
+    M, K, N = 4100, 144, 3080
+    q = synthetic.int8_uniform((M, K), 6, 1)
+    W = synthetic.int8_uniform((N, K), 6, 2)
+    xs = synthetic.uniform((M,), 1e-3, 1e-2, 6, 3, dtype=torch.float32)
+    ws = synthetic.uniform((N,), 1e-3, 1e-2, 6, 4, dtype=torch.float32)
+    acc = rnl.linear_int8(dev(q), dev(xs), dev(W), dev(ws), out_dtype=torch.int32)
+    y = rnl.linear_int8(dev(q), dev(xs), dev(W), dev(ws), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    acc_ref = O.int8_gemm(q.numpy()[rows], W.numpy())
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), acc_ref)
+    assert np.array_equal(y.cpu().numpy()[rows], O.dequant(acc_ref, xs.numpy()[rows], ws.numpy()))
+
+
 # ---------------------------------------------------------------------------
 # residual add before the norm: x_add bit-exact against the oracle's add, then
 # the same checks as the paths without the add, on x_add; and the call must
