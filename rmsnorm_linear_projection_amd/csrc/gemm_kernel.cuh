@@ -9,13 +9,12 @@
 //   int8: v_mfma_i32_16x16x64_i8    (16 int8 per lane, int32 accumulation)
 // A k-step therefore holds two MFMA k-chunks ("halves").
 //
-// Workgroup: 2 x WNW wavefronts over a BM x BN tile: 4 (one per SIMD, 2 x 2),
-// or 8 for the 256 x 192 tile (two per SIMD, 2 x 4, each 128 x 48), whose two
-// wavefronts per SIMD hide each other's LDS reads (the chain's second stage
-// 70.6 -> 69.4 us, the QKV GEMM 161.1 -> 160.6 us on one box).  The weight
-// fragment is the MFMA "A" source and the activation fragment the "B" source,
-// so each lane ends up with 4 consecutive output columns of one token row and
-// stores them as one vector.
+// Workgroup: WMW x WNW wavefronts over a BM x BN tile: 4 (one per SIMD, 2 x 2),
+// or 8 for the 256 x 192 tile (two per SIMD, 4 x 2, each 64 x 96), whose two
+// wavefronts per SIMD hide each other's LDS reads.  The weight fragment is the
+// MFMA "A" source and the activation fragment the "B" source, so each lane ends
+// up with 4 consecutive output columns of one token row and stores them as one
+// vector.
 //
 // Pipeline (one barrier per k-step):
 //   * global -> LDS with buffer_load ... lds (direct-to-LDS DMA, no VGPR
@@ -82,20 +81,20 @@ enum Epi : int {
 #define RNL_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
 
 // WPE: workgroups per CU the kernel is built for (1, or 2 for tiles that fit twice
-// in LDS and in half the register file); WNW: wavefronts along N (2 or 4).
-template <typename TIn, int BM, int BN, int NST, int GROUP_M, int EPI, int WPE = 1, int WNW = 2>
-__global__ __attribute__((amdgpu_flat_work_group_size(128 * WNW, 128 * WNW), amdgpu_waves_per_eu(WPE * WNW / 2, WPE * WNW / 2)))
+// in LDS and in half the register file); WMW x WNW: the wavefront grid (M x N).
+template <typename TIn, int BM, int BN, int NST, int GROUP_M, int EPI, int WPE = 1, int WNW = 2, int WMW = 2>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WMW * WNW, 64 * WMW * WNW), amdgpu_waves_per_eu(WPE * WMW * WNW / 4, WPE * WMW * WNW / 4)))
 void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* __restrict__ C,
                     const float* __restrict__ xs, const float* __restrict__ ws, int M, int N, int K,
                     int tiles_m, int tiles_n, int ksplit, int steps_per_split) {
   using Acc = typename Mfma<TIn>::Acc;
   constexpr int ROWB = 128;
-  constexpr int NWV = 2 * WNW;       // wavefronts: 2 along M x WNW along N
+  constexpr int NWV = WMW * WNW;       // wavefronts: WMW along M x WNW along N
   constexpr int A_CH = BM / (8 * NWV);  // DMA instructions per wave and stage for A
   constexpr int B_CH = BN / (8 * NWV);
   static_assert(A_CH * 8 * NWV == BM && B_CH * 8 * NWV == BN, "DMA rows must split evenly over the waves");
   constexpr int LPS = A_CH + B_CH;    // DMA instructions per wave and stage
-  constexpr int WM = BM / 2, WN = BN / WNW;
+  constexpr int WM = BM / WMW, WN = BN / WNW;
   constexpr int NMI = WM / 16, NNI = WN / 16;
   constexpr int NF = NMI + NNI;       // fragment reads per half
   constexpr int NMM = NMI * NNI;      // MFMAs per half
@@ -283,14 +282,14 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename TIn, int BM, int BN, int NST, int EPI, int WPE = 1, int WNW = 2>
+template <typename TIn, int BM, int BN, int NST, int EPI, int WPE = 1, int WNW = 2, int WMW = 2>
 hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws, int64_t M,
                        int64_t N, int64_t K, int ksplit, hipStream_t s) {
   const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   const int nk = (int)cdiv(K * (int64_t)sizeof(TIn), 128);
   const int sps = (int)cdiv(nk, ksplit);
   const int nwg = tiles_m * tiles_n * ksplit;
-  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI, WPE, WNW>), dim3(nwg), dim3(128 * WNW), 0, s, A, B, C,
+  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI, WPE, WNW, WMW>), dim3(nwg), dim3(64 * WMW * WNW), 0, s, A, B, C,
                      xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n, ksplit, sps);
   return hipGetLastError();
 }
@@ -313,7 +312,7 @@ template <typename TIn, int EPI>
 hipError_t launch_shape(Shape sh, const TIn* A, const TIn* B, void* C, const float* xs, const float* ws,
                         int64_t M, int64_t N, int64_t K, int ksplit, hipStream_t s) {
   switch (sh) {
-    case S256x192: return launch_tile<TIn, 256, 192, 2, EPI, 1, 4>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    case S256x192: return launch_tile<TIn, 256, 192, 2, EPI, 1, 2, 4>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S256x128: return launch_tile<TIn, 256, 128, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x256: return launch_tile<TIn, 128, 256, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x128_2PerCU: return launch_tile<TIn, 128, 128, 2, EPI, 2>(A, B, C, xs, ws, M, N, K, ksplit, s);
