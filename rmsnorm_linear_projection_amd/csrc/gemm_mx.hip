@@ -19,9 +19,10 @@
 // and picks its byte by shifting.
 //
 // Staging follows the bf16 / int8 GEMM: global -> LDS by direct-to-LDS DMA,
-// 128-byte rows with 16-byte chunk c of row r at slot c ^ (r & 7), a 2 x 2 grid
-// of wavefronts, XCD-aware tile order.  With two LDS stages every wait on the
-// DMA is a wait for all loads (vmcnt 0).
+// 128-byte rows with 16-byte chunk c of row r at slot c ^ (r & 7), XCD-aware
+// tile order, and a WMW x WNW grid of wavefronts: 4 x 2 (two per SIMD, each
+// 64 x 96) for the 256 x 192 tile, 2 x 2 for the others.  With two LDS stages
+// every wait on the DMA is a wait for all loads (vmcnt 0).
 // Per k-step, phase A issues the MFMAs of the first half of the activation
 // fragments while the second half is read; after the barrier, phase B issues
 // the rest while the free stage is refilled and the next k-step's first half
@@ -43,18 +44,21 @@ __device__ __forceinline__ uint32_t buf_load_u8(__amdgpu_buffer_rsrc_t r, uint32
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
-template <int BM, int BN, bool OUT_BF16>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, bool OUT_BF16, int WMW = 2, int WNW = 2>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WMW * WNW, 64 * WMW * WNW),
+                          amdgpu_waves_per_eu(WMW * WNW / 4, WMW * WNW / 4)))
 void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ As,
                     const uint8_t* __restrict__ Bs, void* __restrict__ C, int M, int N, int K, int tiles_m,
                     int tiles_n) {
   constexpr int NST = 2;
   constexpr int GROUP_M = 4;
   constexpr int ROWB = 128;
-  constexpr int A_CH = BM * 8 / 256;  // DMA instructions per wave and stage for A
-  constexpr int B_CH = BN * 8 / 256;
+  constexpr int NT = 64 * WMW * WNW;  // threads
+  constexpr int A_CH = BM / (8 * WMW * WNW);  // DMA instructions per wave and stage for A
+  constexpr int B_CH = BN / (8 * WMW * WNW);
+  static_assert(A_CH * 8 * WMW * WNW == BM && B_CH * 8 * WMW * WNW == BN, "DMA rows must split evenly");
   constexpr int LPS = A_CH + B_CH;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WMW, WN = BN / WNW;
   constexpr int NMI = WM / 16, NNI = WN / 16;
   constexpr int HM = NMI / 2;  // activation fragments per phase
   constexpr int STAGE = (BM + BN) * ROWB;
@@ -66,7 +70,7 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
 
   // workgroup -> tile: contiguous range per XCD, grouped along M inside it
   const int bid = blockIdx.x, nwg = gridDim.x;
@@ -139,7 +143,7 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
   // K read as 127 (scale 1: their data are zero), rows past M / N as 0
   auto stage_scales = [&](int c) {
     const int b0 = c * 2 * SC_CHUNK;
-    for (int p = tid; p < (BM + BN) * 4; p += 256) {
+    for (int p = tid; p < (BM + BN) * 4; p += NT) {
       const int row = p >> 2, q = p & 3;
       const int byte0 = b0 + 16 * q;
       const bool is_a = row < BM;
@@ -282,16 +286,16 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <int BM, int BN>
+template <int BM, int BN, int WMW = 2, int WNW = 2>
 hipError_t launch_mx_tile(const uint8_t* A, const uint8_t* B, const uint8_t* As, const uint8_t* Bs, void* C,
                           bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   const int tiles_m = (int)cdiv64(M, BM), tiles_n = (int)cdiv64(N, BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WMW * WNW);
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, true>), grid, block, 0, s, A, B, As, Bs, C, (int)M, (int)N, (int)K,
-                       tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, true, WMW, WNW>), grid, block, 0, s, A, B, As, Bs, C, (int)M, (int)N,
+                       (int)K, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false>), grid, block, 0, s, A, B, As, Bs, C, (int)M, (int)N,
+    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false, WMW, WNW>), grid, block, 0, s, A, B, As, Bs, C, (int)M, (int)N,
                        (int)K, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -302,7 +306,7 @@ hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* As, const uint8_t* B,
                           int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   const bool ob = out_kind == OUT_BF16;
   // largest tile that still gives every CU a workgroup
-  if (cdiv64(M, 256) * cdiv64(N, 192) >= 256) return launch_mx_tile<256, 192>(A, B, As, Bs, C, ob, M, N, K, s);
+  if (cdiv64(M, 256) * cdiv64(N, 192) >= 256) return launch_mx_tile<256, 192, 4, 2>(A, B, As, Bs, C, ob, M, N, K, s);
   if (cdiv64(M, 256) * cdiv64(N, 128) >= 256) return launch_mx_tile<256, 128>(A, B, As, Bs, C, ob, M, N, K, s);
   if (cdiv64(M, 128) * cdiv64(N, 256) >= 256) return launch_mx_tile<128, 256>(A, B, As, Bs, C, ob, M, N, K, s);
   return launch_mx_tile<128, 128>(A, B, As, Bs, C, ob, M, N, K, s);
