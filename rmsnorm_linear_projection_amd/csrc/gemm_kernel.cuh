@@ -9,9 +9,10 @@
 //   int8: v_mfma_i32_16x16x64_i8    (16 int8 per lane, int32 accumulation)
 // A k-step therefore holds two MFMA k-chunks ("halves").
 //
-// Workgroup: WMW x WNW wavefronts over a BM x BN tile: 4 (one per SIMD, 2 x 2),
-// or 8 for the 256 x 192 tile (two per SIMD, 4 x 2, each 64 x 96), whose two
-// wavefronts per SIMD hide each other's LDS reads.  The weight fragment is the
+// Workgroup: WMW x WNW wavefronts over a BM x BN tile: 8 (two per SIMD, 4 x 2)
+// for the 256 x 192 tile (64 x 96 each) and the 128 x 128 one (32 x 64 each),
+// whose two wavefronts per SIMD hide each other's LDS reads; 4 (one per SIMD,
+// 2 x 2) for the others.  The weight fragment is the
 // MFMA "A" source and the activation fragment the "B" source, so each lane ends
 // up with 4 consecutive output columns of one token row and stores them as one
 // vector.
@@ -316,7 +317,7 @@ hipError_t launch_shape(Shape sh, const TIn* A, const TIn* B, void* C, const flo
     case S256x128: return launch_tile<TIn, 256, 128, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x256: return launch_tile<TIn, 128, 256, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x128_2PerCU: return launch_tile<TIn, 128, 128, 2, EPI, 2>(A, B, C, xs, ws, M, N, K, ksplit, s);
-    default: return launch_tile<TIn, 128, 128, 4, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    default: return launch_tile<TIn, 128, 128, 4, EPI, 1, 2, 4>(A, B, C, xs, ws, M, N, K, ksplit, s);
   }
 }
 
