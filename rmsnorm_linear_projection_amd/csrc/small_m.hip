@@ -17,7 +17,9 @@
 // source (lane l: weight row l & 15, 16 bytes at k-chunk l >> 4) and the
 // activations as the B source (lane l: token l & 15, same k-chunk).  Weight
 // rows >= R, tokens >= M and the K tail read as zero through the buffer
-// bounds.  Loads run KU k-steps ahead in two alternating register batches.
+// bounds.  Loads run KU k-steps ahead in two alternating register batches
+// (KU = 2: at N = 6144, K = 4096, T = 16 the kernel takes 13.0 us against 13.7
+// with KU = 4, 14.5 with 3 and 15.4 with 1).
 // The four wavefront accumulators are added through LDS in a fixed order.
 #include "launch.h"
 #include "rows.cuh"
@@ -400,7 +402,7 @@ hipError_t launch_small_m_bf16(const uint16_t* A, const uint16_t* W, void* C, in
   dim3 grid((unsigned)((N + R - 1) / R)), block(256);
   const bool ob = out_kind == OUT_BF16;
 #define RNL_SMALL_M(NB, O) \
-  hipLaunchKernelGGL((small_m_kernel<NB, 4, 4, O>), grid, block, 0, s, A, W, C, (int)M, (int)K, (int)N, R)
+  hipLaunchKernelGGL((small_m_kernel<NB, 4, 2, O>), grid, block, 0, s, A, W, C, (int)M, (int)K, (int)N, R)
   if (R <= 16) {
     if (ob) RNL_SMALL_M(1, true); else RNL_SMALL_M(1, false);
   } else {
