@@ -2,9 +2,9 @@
 //
 // Rows of up to 8192 values, at least 256 of them or shorter than 2048: one
 // wavefront per row (shuffle reductions only).  Longer rows, or fewer rows than
-// CUs: one 256-thread workgroup per row, the row read once with 16-byte coalesced loads
-// (kept in registers when K <= 16384) and the fp32 sum of squares reduced
-// across the wavefronts.  The normed row is written either as
+// CUs: one 256-thread workgroup per row, the row read once with 16-byte
+// coalesced loads (kept in registers when K <= 16384) and the fp32 sum of
+// squares reduced across the wavefronts.  The normed row is written either as
 // bf16 (the A operand of the bf16 GEMM) or as per-token symmetric int8 plus
 // its dequant scale (the A operand of the int8 GEMM).
 //
