@@ -67,6 +67,7 @@ KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.cuh", "gemm_bf16.hip", "gemm_int8.hip", "common.cuh"],
     "small_m": ["small_m.hip", "common.cuh", "rows.cuh"],
     "small_m_norm": ["small_m.hip", "common.cuh", "rows.cuh"],
+    "row_gemv": ["row_gemv.hip", "common.cuh"],
     "gemm_mx": ["gemm_mx.hip", "common.cuh"],
     "skinny": ["skinny.hip", "common.cuh"],
 }
@@ -114,12 +115,20 @@ def fused_small_norm(w):
     return w["kind"] == "bf16" and not w.get("add") and T <= 4 and T * ((K + 31) // 32) * 64 <= 64 * 1024
 
 
+def row_gemv(w):
+    """True when one token goes to the whole-row VALU kernel: T = 1, no
+    residual, K at most 8192."""
+    return w["kind"] == "bf16" and not w.get("add") and w["T"] == 1 and w["K"] <= 8192
+
+
 def kernel_key_of(w):
     """Key of the dominant kernel of a workload (KERNEL_MATCH, KERNEL_SOURCES)."""
     if w["kind"] == "fp32w":
         return "skinny"
     if w["kind"] == "mxfp8":
         return "gemm_mx"
+    if row_gemv(w):
+        return "row_gemv"
     if fused_small_norm(w):
         return "small_m_norm"
     return "small_m" if w["kind"] in ("bf16", "preattn") and w["T"] <= 16 else "gemm"
@@ -193,9 +202,10 @@ class Setup:
                 self.step = lambda i: rnl.rmsnorm_linear_bf16(t["x"], t["gamma"], eps, Wc[i % len(Wc)], y=y,
                                                               workspace=ws)
             a = rnl.rms_norm_bf16(t["x"], t["gamma"], eps)
-            if fused_small_norm(w):
+            if row_gemv(w) or fused_small_norm(w):
                 # the norm runs inside the weight-streaming kernel: the step is that one launch
-                self.kernel, self.kernel_key = "small_m_norm_kernel", "small_m_norm"
+                self.kernel_key = kernel_key_of(w)
+                self.kernel = KERNEL_MATCH[self.kernel_key]
                 self.kern = self.step
                 self.kern_units = ("hbm", bytes_of(w))
             elif T <= 16:
@@ -470,6 +480,7 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False):
 
 COPY_BYTES = 256 << 20  # size of the plain device copy that calibrates FETCH_SIZE / WRITE_SIZE
 KERNEL_MATCH = {"gemm": "gemm_nt_kernel", "small_m": "small_m_kernel", "small_m_norm": "small_m_norm_kernel",
+                "row_gemv": "row_gemv_norm_kernel",
                 "skinny": "skinny_", "gemm_mx": "gemm_mx_kernel"}
 
 

@@ -156,6 +156,10 @@ int bf16_path(const void* x, const void* residual, void* x_add, const void* gamm
                       "skinny split-K launch");
   }
   const uint16_t* wb = static_cast<const uint16_t*>(W);
+  // one token: each wavefront norms the row and streams whole weight rows
+  if (rb == nullptr && T == 1 && use_small_m(T) && rnl::row_gemv_fits(K))
+    return hip_status(rnl::launch_row_gemv_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, N, K, s),
+                      "single-token norm + projection launch");
   // a few tokens whose normed rows fit LDS: the norm runs inside the weight-streaming kernel
   if (rb == nullptr && T <= kFusedNormM && use_small_m(T) && rnl::small_m_norm_lds(T, K) <= rnl::kSmallNormLds)
     return hip_status(rnl::launch_small_m_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),

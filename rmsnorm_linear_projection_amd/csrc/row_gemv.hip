@@ -1,0 +1,198 @@
+// Single-token RMSNorm -> projection (decode at T = 1) for gfx950.
+//
+// What it computes is the fused RMSNorm -> Linear of the AT-10 page (compute
+// flow, section 2; the AT-03 norm of section 3; bf16 operands with the weight
+// stored [N, K], section 4) for one activation row:
+//   rstd = 1 / sqrt(fl(fl(S / K) + eps)),  S = fp32 sum of x[k]^2,
+//   a[k] = bf16(fl(fl(x[k] * rstd) * gamma[k])),
+//   y[n] = sum_k a[k] * W[n, k]  (fp32 accumulation, then bf16 or fp32).
+//
+// One output row is a dot product of K bf16 pairs, so the weight read is the
+// whole cost (HBM-bound).  Layout of the work:
+//   * wavefront v (four to a workgroup, which share nothing) owns RW
+//     consecutive weight rows (RW is a template argument: rows past N are
+//     skipped by the buffer resource, but rows the wavefront never uses would
+//     still cost load slots and registers);
+//   * lane l owns the 16-byte chunks c * 64 + l (c < KC) of every row, so each
+//     load instruction reads 1 KiB of one row, contiguous; all RW x KC weight
+//     chunks are requested at once, after the token row and gamma, which come
+//     from L2 once the first wavefront has brought them in;
+//   * every wavefront norms the token row itself (a wavefront sum of squares,
+//     no LDS, no barrier), keeping its own chunks of a in registers;
+//   * the products run on the VALU (v_dot2c_f32_bf16: two bf16 products added
+//     to an fp32 accumulator per instruction); one token needs no matrix core;
+//   * each row's 64 lane partials are summed across the wavefront and lane r
+//     stores row r.
+// Rows past N and chunks past K read as zero through the buffer resource.
+#include "common.cuh"
+#include "launch.h"
+
+namespace rnl {
+namespace {
+
+// fp32 dot product of 8 bf16 pairs, added to acc (element copies go through a
+// scalar before the bit cast: a cast of a vector element reference reads
+// element 0)
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 a, float acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t wj = w[j], aj = a[j];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wj), __builtin_bit_cast(bf16x2, aj), acc,
+                                          false);
+  }
+  return acc;
+}
+
+// a = bf16(fl(fl(x * rstd) * g)) for 8 elements (g = 1 without gamma)
+template <bool GAMMA>
+__device__ __forceinline__ u32x4 norm8(u32x4 x, u32x4 g, float rstd) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float lo = __fmul_rn(bf16lo(x[j]), rstd), hi = __fmul_rn(bf16hi(x[j]), rstd);
+    if constexpr (GAMMA) {
+      lo = __fmul_rn(lo, bf16lo(g[j]));
+      hi = __fmul_rn(hi, bf16hi(g[j]));
+    }
+    o[j] = pack_bf16x2(lo, hi);
+  }
+  return o;
+}
+
+__device__ __forceinline__ float sumsq8(u32x4 w) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = bf16lo(w[j]), b = bf16hi(w[j]);
+    s += a * a;
+    s += b * b;
+  }
+  return s;
+}
+
+// KC: 16-byte chunks per lane and row (K <= 512 * KC); RW: rows per wavefront
+template <int KC, int RW>
+__global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ gamma, float eps,
+                                                           float inv_k, const uint16_t* __restrict__ W,
+                                                           void* __restrict__ C, bool out_bf16,
+                                                           float* __restrict__ rstd_out, int K, int N) {
+  const int lane = threadIdx.x & 63;
+  const int wv = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = wv * RW;
+  if (n0 >= N) return;  // whole wavefront; there is no barrier
+  const int rows = min(RW, N - n0);
+  const bool has_g = gamma != nullptr;
+  const uint32_t kbytes = (uint32_t)K * 2u;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, kbytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(has_g ? gamma : X, has_g ? kbytes : 0u);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * K, (uint32_t)rows * kbytes);
+
+  u32x4 xv[KC], gv[KC], w[RW][KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    const uint32_t o = (uint32_t)(c * 64 + lane) * 16u;
+    const uint32_t oo = o < kbytes ? o : kOOB;
+    xv[c] = buf_load16(rx, oo);
+    gv[c] = buf_load16(rg, oo);  // zeros without gamma (an empty resource), not used then
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const uint32_t o = (uint32_t)(c * 64 + lane) * 16u;
+      w[r][c] = buf_load16(rw, (o < kbytes && r < rows) ? o + (uint32_t)r * kbytes : kOOB);
+    }
+  // keep every load above issued before the norm arithmetic waits on the first
+  __builtin_amdgcn_sched_barrier(0);
+
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < KC; ++c) ss += sumsq8(xv[c]);
+  ss = wave_sum(ss);
+  const float rstd = rstd_from_sumsq(ss, inv_k, eps);
+  if (wv == 0 && lane == 0 && rstd_out != nullptr) rstd_out[0] = rstd;
+  u32x4 a[KC];
+  if (has_g) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) a[c] = norm8<true>(xv[c], gv[c], rstd);
+  } else {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) a[c] = norm8<false>(xv[c], gv[c], rstd);
+  }
+
+  float acc[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) acc[r] = dot8(w[r][c], a[c], acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    if (r >= rows) break;
+    const float v = wave_sum(acc[r]);
+    if (lane == r) {
+      if (out_bf16)
+        static_cast<uint16_t*>(C)[n0 + r] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+      else
+        static_cast<float*>(C)[n0 + r] = v;
+    }
+  }
+}
+
+// Most rows per wavefront for KC chunks per lane and row (K = 512 * KC).
+// Measured at T = 1 (rotated weights, same box): K = 1536, N = 24576: RW = 4
+// 14.0 us, 6 14.7, 8 15.0; K = 2048, N = 4096: 4 rows 5.0 us against 6.6 at 2;
+// K = 512, N = 4096: 4 rows 3.3 us, 8 rows 3.9; K = 4096, N = 6144: 3 rows
+// 11.0 us, 2 rows 12.2.  Past 8 chunks the cap keeps the weight registers
+// near 24 chunks (96 VGPRs).
+constexpr int rw_cap(int kc) { return kc <= 6 ? 4 : kc <= 8 ? 3 : kc <= 12 ? 2 : 1; }
+
+}  // namespace
+
+bool row_gemv_fits(int64_t K) { return K >= 8 && K <= kRowGemvMaxK; }
+
+int row_gemv_rows(int64_t N, int kc) {
+  const int64_t rw = (N + kRowGemvWaves - 1) / kRowGemvWaves;
+  const int cap = rw_cap(kc);
+  return (int)(rw < cap ? rw : cap);
+}
+
+hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
+                                     void* C, int out_kind, float* rstd_out, int64_t N, int64_t K,
+                                     hipStream_t s) {
+  if (!row_gemv_fits(K) || N < 1 || N > 0x7fffffff) return hipErrorInvalidValue;
+  const int kc = (int)((K + 511) / 512);
+  const bool ob = out_kind == OUT_BF16;
+  const float inv_k = 1.0f / (float)K;
+  const int rw = row_gemv_rows(N, kc);
+  const int64_t waves = (N + rw - 1) / rw;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+#define RNL_ROW_GEMV(KC, RW)                                                                                  \
+  hipLaunchKernelGGL((row_gemv_norm_kernel<KC, RW>), grid, block, 0, s, X, gamma, eps, inv_k, W, C, ob,      \
+                     rstd_out, (int)K, (int)N)
+#define RNL_ROW_GEMV_KC(KC)                                                          \
+  case KC:                                                                           \
+    if (rw == 1) RNL_ROW_GEMV(KC, 1);                                                \
+    else if constexpr (rw_cap(KC) >= 2) {                                            \
+      if (rw == 2) RNL_ROW_GEMV(KC, 2);                                              \
+      else if constexpr (rw_cap(KC) >= 3) {                                          \
+        if (rw == 3) RNL_ROW_GEMV(KC, 3);                                            \
+        else if constexpr (rw_cap(KC) >= 4) RNL_ROW_GEMV(KC, 4);                     \
+      }                                                                              \
+    }                                                                                \
+    break
+  switch (kc) {
+    RNL_ROW_GEMV_KC(1); RNL_ROW_GEMV_KC(2); RNL_ROW_GEMV_KC(3); RNL_ROW_GEMV_KC(4);
+    RNL_ROW_GEMV_KC(5); RNL_ROW_GEMV_KC(6); RNL_ROW_GEMV_KC(7); RNL_ROW_GEMV_KC(8);
+    RNL_ROW_GEMV_KC(9); RNL_ROW_GEMV_KC(10); RNL_ROW_GEMV_KC(11); RNL_ROW_GEMV_KC(12);
+    RNL_ROW_GEMV_KC(13); RNL_ROW_GEMV_KC(14); RNL_ROW_GEMV_KC(15); RNL_ROW_GEMV_KC(16);
+    default: return hipErrorInvalidValue;
+  }
+#undef RNL_ROW_GEMV_KC
+#undef RNL_ROW_GEMV
+  return hipGetLastError();
+}
+
+}  // namespace rnl

@@ -124,6 +124,14 @@ BF16_SMALL = [
     (4, 8192, 200),  # four normed rows filling the 64 KiB LDS budget exactly
     (4, 64, 9),  # two k-steps: two of the four wavefronts have no part of K
     (8, 4096, 200),  # more rows than the fused norm takes: pre-pass
+    # one token: whole weight rows per wavefront, each K bucket of the chunk count
+    (1, 8, 1),
+    (1, 512, 2049),  # one chunk per lane, two rows per wavefront, the last wavefront one row
+    (1, 520, 300),  # two chunks, K tail
+    (1, 2048, 30001),  # four chunks, six rows per wavefront, ragged last wavefront
+    (1, 4104, 333),  # sixteen chunks (nine used), K tail
+    (1, 8192, 100),  # the longest row it takes
+    (1, 4096, 6144),  # pre-attention QKV shape, one decode token
 ]
 
 
