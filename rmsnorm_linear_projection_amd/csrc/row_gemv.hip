@@ -21,8 +21,8 @@
 //     no LDS, no barrier), keeping its own chunks of a in registers;
 //   * the products run on the VALU (v_dot2c_f32_bf16: two bf16 products added
 //     to an fp32 accumulator per instruction); one token needs no matrix core;
-//   * each row's 64 lane partials are summed across the wavefront and lane r
-//     stores row r.
+//   * each row's 64 lane partials are summed across the wavefront (DPP, no
+//     LDS) and lane r stores row r.
 // Rows past N and chunks past K read as zero through the buffer resource.
 #include "common.cuh"
 #include "launch.h"
@@ -70,6 +70,23 @@ __device__ __forceinline__ float sumsq8(u32x4 w) {
   return s;
 }
 
+// the sum of v over the 64 lanes, on every lane: DPP adds within rows of 16
+// lanes, two row broadcasts carry the partial sums up to lane 63, which is
+// read out.  No LDS round trips, so the sums of several rows interleave.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm 1,0,3,2: lane ^ 1
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm 2,3,0,1: lane ^ 2
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror: the two quads of 8 lanes
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror: the two halves of 16 lanes
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3: rows 0+1 and 2+3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 holds all four
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // KC: 16-byte chunks per lane and row (K <= 512 * KC); RW: rows per wavefront
 template <int KC, int RW>
 __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __restrict__ X,
@@ -109,7 +126,7 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < KC; ++c) ss += sumsq8(xv[c]);
-  ss = wave_sum(ss);
+  ss = wave_total(ss);
   const float rstd = rstd_from_sumsq(ss, inv_k, eps);
   if (wv == 0 && lane == 0 && rstd_out != nullptr) rstd_out[0] = rstd;
   u32x4 a[KC];
@@ -131,7 +148,7 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     if (r >= rows) break;
-    const float v = wave_sum(acc[r]);
+    const float v = wave_total(acc[r]);
     if (lane == r) {
       if (out_bf16)
         static_cast<uint16_t*>(C)[n0 + r] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);

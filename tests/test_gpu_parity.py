@@ -132,6 +132,12 @@ BF16_SMALL = [
     (1, 4104, 333),  # sixteen chunks (nine used), K tail
     (1, 8192, 100),  # the longest row it takes
     (1, 4096, 6144),  # pre-attention QKV shape, one decode token
+    # a few tokens: the fused MFMA kernel (T <= 4) or the pre-pass and weight streaming
+    (2, 4096, 6144),
+    (3, 1024, 3000),  # ragged N
+    (6, 512, 5000),
+    (8, 1024, 2049),
+    (7, 1032, 77),  # K tail
 ]
 
 
