@@ -15,10 +15,13 @@
 //     still cost load slots and registers);
 //   * lane l owns the 16-byte chunks c * 64 + l (c < KC) of every row, so each
 //     load instruction reads 1 KiB of one row, contiguous; all RW x KC weight
-//     chunks are requested at once, after the token row and gamma, which come
-//     from L2 once the first wavefront has brought them in;
-//   * every wavefront norms the token row itself (a wavefront sum of squares,
-//     no LDS, no barrier), keeping its own chunks of a in registers;
+//     chunks are requested at once, right after the wavefront's share of the
+//     token row and gamma;
+//   * the four wavefronts of a workgroup share the norm: wavefront v loads the
+//     chunks c = v, v + 4, ... of x and gamma, the four partial sums of squares
+//     meet in LDS and are added in a fixed order, and each wavefront writes its
+//     normed chunks of a to LDS, from which every wavefront reads the whole
+//     row (wavefronts with no weight rows past N still take part);
 //   * the products run on the VALU (v_dot2c_f32_bf16: two bf16 products added
 //     to an fp32 accumulator per instruction); one token needs no matrix core;
 //   * each row's 64 lane partials are summed across the wavefront (DPP, no
@@ -94,24 +97,28 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
                                                            float inv_k, const uint16_t* __restrict__ W,
                                                            void* __restrict__ C, bool out_bf16,
                                                            float* __restrict__ rstd_out, int K, int N) {
+  constexpr int XC = (KC + 3) / 4;  // chunks of x and gamma each wavefront norms
+  __shared__ u32x4 as[KC * 64];     // the normed row, chunk c of lane l at c * 64 + l
+  __shared__ float red[4];
   const int lane = threadIdx.x & 63;
-  const int wv = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = blockIdx.x * 4 + wave;
   const int n0 = wv * RW;
-  if (n0 >= N) return;  // whole wavefront; there is no barrier
-  const int rows = min(RW, N - n0);
+  const int rows = n0 < N ? min(RW, N - n0) : 0;  // 0: the wavefront only helps with the norm
   const bool has_g = gamma != nullptr;
   const uint32_t kbytes = (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, kbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(has_g ? gamma : X, has_g ? kbytes : 0u);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * K, (uint32_t)rows * kbytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)min(n0, N - 1) * K, (uint32_t)rows * kbytes);
 
-  u32x4 xv[KC], gv[KC], w[RW][KC];
+  u32x4 xv[XC], gv[XC], w[RW][KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
+  for (int i = 0; i < XC; ++i) {
+    const int c = wave + 4 * i;
     const uint32_t o = (uint32_t)(c * 64 + lane) * 16u;
-    const uint32_t oo = o < kbytes ? o : kOOB;
-    xv[c] = buf_load16(rx, oo);
-    gv[c] = buf_load16(rg, oo);  // zeros without gamma (an empty resource), not used then
+    const uint32_t oo = (c < KC && o < kbytes) ? o : kOOB;
+    xv[i] = buf_load16(rx, oo);
+    gv[i] = buf_load16(rg, oo);  // zeros without gamma (an empty resource), not used then
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -125,25 +132,29 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
 
   float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) ss += sumsq8(xv[c]);
+  for (int i = 0; i < XC; ++i) ss += sumsq8(xv[i]);
   ss = wave_total(ss);
-  const float rstd = rstd_from_sumsq(ss, inv_k, eps);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float S = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rstd = rstd_from_sumsq(S, inv_k, eps);
   if (wv == 0 && lane == 0 && rstd_out != nullptr) rstd_out[0] = rstd;
-  u32x4 a[KC];
-  if (has_g) {
 #pragma unroll
-    for (int c = 0; c < KC; ++c) a[c] = norm8<true>(xv[c], gv[c], rstd);
-  } else {
-#pragma unroll
-    for (int c = 0; c < KC; ++c) a[c] = norm8<false>(xv[c], gv[c], rstd);
+  for (int i = 0; i < XC; ++i) {
+    const int c = wave + 4 * i;
+    if (c < KC) as[c * 64 + lane] = has_g ? norm8<true>(xv[i], gv[i], rstd) : norm8<false>(xv[i], gv[i], rstd);
   }
+  __syncthreads();
+  if (rows == 0) return;  // after the last barrier
 
   float acc[RW];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    acc[r] = 0.f;
+  for (int r = 0; r < RW; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) acc[r] = dot8(w[r][c], a[c], acc[r]);
+  for (int c = 0; c < KC; ++c) {
+    const u32x4 a = as[c * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = dot8(w[r][c], a, acc[r]);
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -163,7 +174,9 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
 // 14.0 us, 6 14.7, 8 15.0; K = 2048, N = 4096: 4 rows 5.0 us against 6.6 at 2;
 // K = 512, N = 4096: 4 rows 3.3 us, 8 rows 3.9; K = 4096, N = 6144: 3 rows
 // 11.0 us, 2 rows 12.2.  Past 8 chunks the cap keeps the weight registers
-// near 24 chunks (96 VGPRs).
+// near 24 chunks (96 VGPRs).  With the norm shared through LDS the registers
+// would allow more, but caps of 4, 3 and 2 rows up to 8, 12 and 16 chunks were
+// slower: K = 4096, N = 6144 11.0 us against 10.1.
 constexpr int rw_cap(int kc) { return kc <= 6 ? 4 : kc <= 8 ? 3 : kc <= 12 ? 2 : 1; }
 
 }  // namespace

@@ -56,7 +56,7 @@ def ws_for(kind, *shape, **kw):
     return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("T,K,N", [(300, 1032, 200), (16, 4096, 512), (1, 256, 64)])
+@pytest.mark.parametrize("T,K,N", [(300, 1032, 200), (16, 4096, 512), (1, 256, 64), (1, 4104, 333)])
 def test_graph_bf16(T, K, N):
     t = dev(synthetic.norm_linear_case(T, K, N, seed=1))
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")

@@ -163,6 +163,21 @@ def test_bf16_large_tiles_ragged(T, K, N):
     check_bf16_case(case, rows=sample_rows(T))
 
 
+@pytest.mark.parametrize("scale", [0.0, 1024.0, 1.0 / 4096])
+@pytest.mark.parametrize("K", [4096, 7168])
+def test_bf16_single_token_scaled(scale, K):
+    """One token (the whole-row kernel): a zero row gives y = 0 and rstd = 1/sqrt(eps); scaled rows keep parity."""
+    case = synthetic.norm_linear_case(1, K, 130, seed=K)
+    case.tensors["x"] = (case.tensors["x"].float() * scale).to(torch.bfloat16)
+    y = check_bf16_case(case)
+    if scale == 0.0:
+        assert (f32(y) == 0).all()
+
+
+def test_bf16_single_token_no_gamma_fp32_output():
+    check_bf16_case(synthetic.norm_linear_case(1, 2056, 517, seed=9, gamma=False), out_dtype=torch.float32)
+
+
 def test_bf16_zero_and_scaled_rows():
     case = synthetic.norm_linear_case(40, 512, 96, seed=3)
     x = case.tensors["x"].clone()
