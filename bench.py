@@ -116,9 +116,9 @@ def fused_small_norm(w):
 
 
 def row_gemv(w):
-    """True when one token goes to the whole-row VALU kernel: T = 1, no
+    """True when the tokens go to the whole-row VALU kernel: T at most 2, no
     residual, K at most 8192."""
-    return w["kind"] == "bf16" and not w.get("add") and w["T"] == 1 and w["K"] <= 8192
+    return w["kind"] == "bf16" and not w.get("add") and w["T"] <= 2 and w["K"] <= 8192
 
 
 def kernel_key_of(w):

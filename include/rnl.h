@@ -33,7 +33,7 @@
  *     is needed and the pointer may be NULL).  Its contents on entry do not
  *     matter and are undefined afterwards.
  *   - bf16 projections with at most 16 activation rows run a weight-streaming
- *     kernel (one row with K <= 8192 and no residual: a kernel that streams
+ *     kernel (one or two rows with K <= 8192 and no residual: a kernel that streams
  *     whole weight rows and multiplies on the vector units), larger ones the
  *     tiled GEMM.  Environment variable RNL_VARIANT
  *     (read at every call) set to "gemm" forces the tiled GEMM for any size,

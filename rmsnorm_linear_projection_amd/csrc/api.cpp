@@ -157,8 +157,8 @@ int bf16_path(const void* x, const void* residual, void* x_add, const void* gamm
   }
   const uint16_t* wb = static_cast<const uint16_t*>(W);
   // one token: each wavefront norms the row and streams whole weight rows
-  if (rb == nullptr && T == 1 && use_small_m(T) && rnl::row_gemv_fits(K))
-    return hip_status(rnl::launch_row_gemv_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, N, K, s),
+  if (rb == nullptr && use_small_m(T) && rnl::row_gemv_fits(T, K))
+    return hip_status(rnl::launch_row_gemv_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
                       "single-token norm + projection launch");
   // a few tokens whose normed rows fit LDS: the norm runs inside the weight-streaming kernel
   if (rb == nullptr && T <= kFusedNormM && use_small_m(T) && rnl::small_m_norm_lds(T, K) <= rnl::kSmallNormLds)

@@ -1,8 +1,8 @@
-// Single-token RMSNorm -> projection (decode at T = 1) for gfx950.
+// One- and two-token RMSNorm -> projection (decode at T <= 2) for gfx950.
 //
 // What it computes is the fused RMSNorm -> Linear of the AT-10 page (compute
 // flow, section 2; the AT-03 norm of section 3; bf16 operands with the weight
-// stored [N, K], section 4) for one activation row:
+// stored [N, K], section 4) for each of the M <= 2 activation rows:
 //   rstd = 1 / sqrt(fl(fl(S / K) + eps)),  S = fp32 sum of x[k]^2,
 //   a[k] = bf16(fl(fl(x[k] * rstd) * gamma[k])),
 //   y[n] = sum_k a[k] * W[n, k]  (fp32 accumulation, then bf16 or fp32).
@@ -17,15 +17,18 @@
 //     load instruction reads 1 KiB of one row, contiguous; all RW x KC weight
 //     chunks are requested at once, right after the wavefront's share of the
 //     token row and gamma;
-//   * the four wavefronts of a workgroup share the norm: wavefront v loads the
+//   * the four wavefronts of a workgroup share the norm of each token row:
+//     wavefront v loads the
 //     chunks c = v, v + 4, ... of x and gamma, the four partial sums of squares
 //     meet in LDS and are added in a fixed order, and each wavefront writes its
 //     normed chunks of a to LDS, from which every wavefront reads the whole
 //     row (wavefronts with no weight rows past N still take part);
 //   * the products run on the VALU (v_dot2c_f32_bf16: two bf16 products added
 //     to an fp32 accumulator per instruction); one token needs no matrix core;
-//   * each row's 64 lane partials are summed across the wavefront (DPP, no
-//     LDS) and lane r stores row r.
+//   * each output's 64 lane partials are summed across the wavefront (DPP, no
+//     LDS) and lane t * RW + r stores token t's output r.  Measured at K = 4096,
+//     N = 6144: 10.1 us at T = 1, 11.4 at T = 2 (against 12.5 for the MFMA
+//     kernel); at T = 3 and 4 (13.5, 14.0 against 12.4) the MFMA kernel stays.
 // Rows past N and chunks past K read as zero through the buffer resource.
 #include "common.cuh"
 #include "launch.h"
@@ -91,15 +94,15 @@ __device__ __forceinline__ float wave_total(float v) {
 }
 
 // KC: 16-byte chunks per lane and row (K <= 512 * KC); RW: rows per wavefront
-template <int KC, int RW>
+template <int MT, int KC, int RW>
 __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ gamma, float eps,
                                                            float inv_k, const uint16_t* __restrict__ W,
                                                            void* __restrict__ C, bool out_bf16,
-                                                           float* __restrict__ rstd_out, int K, int N) {
+                                                           float* __restrict__ rstd_out, int M, int K, int N) {
   constexpr int XC = (KC + 3) / 4;  // chunks of x and gamma each wavefront norms
-  __shared__ u32x4 as[KC * 64];     // the normed row, chunk c of lane l at c * 64 + l
-  __shared__ float red[4];
+  __shared__ u32x4 as[MT * KC * 64];  // normed rows: token t, chunk c of lane l at (t * KC + c) * 64 + l
+  __shared__ float red[MT][4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wv = blockIdx.x * 4 + wave;
@@ -107,18 +110,19 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
   const int rows = n0 < N ? min(RW, N - n0) : 0;  // 0: the wavefront only helps with the norm
   const bool has_g = gamma != nullptr;
   const uint32_t kbytes = (uint32_t)K * 2u;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, kbytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(has_g ? gamma : X, has_g ? kbytes : 0u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)min(n0, N - 1) * K, (uint32_t)rows * kbytes);
 
-  u32x4 xv[XC], gv[XC], w[RW][KC];
+  u32x4 xv[MT][XC], gv[XC], w[RW][KC];
 #pragma unroll
   for (int i = 0; i < XC; ++i) {
     const int c = wave + 4 * i;
     const uint32_t o = (uint32_t)(c * 64 + lane) * 16u;
-    const uint32_t oo = (c < KC && o < kbytes) ? o : kOOB;
-    xv[i] = buf_load16(rx, oo);
-    gv[i] = buf_load16(rg, oo);  // zeros without gamma (an empty resource), not used then
+    const bool in = c < KC && o < kbytes;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xv[t][i] = buf_load16(rx, (in && t < M) ? o + (uint32_t)t * kbytes : kOOB);
+    gv[i] = buf_load16(rg, in ? o : kOOB);  // zeros without gamma (an empty resource), not used then
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -130,41 +134,58 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
   // keep every load above issued before the norm arithmetic waits on the first
   __builtin_amdgcn_sched_barrier(0);
 
-  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < XC; ++i) ss += sumsq8(xv[i]);
-  ss = wave_total(ss);
-  if (lane == 0) red[wave] = ss;
+  for (int t = 0; t < MT; ++t) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < XC; ++i) ss += sumsq8(xv[t][i]);
+    ss = wave_total(ss);
+    if (lane == 0) red[t][wave] = ss;
+  }
   __syncthreads();
-  const float S = (red[0] + red[1]) + (red[2] + red[3]);
-  const float rstd = rstd_from_sumsq(S, inv_k, eps);
-  if (wv == 0 && lane == 0 && rstd_out != nullptr) rstd_out[0] = rstd;
 #pragma unroll
-  for (int i = 0; i < XC; ++i) {
-    const int c = wave + 4 * i;
-    if (c < KC) as[c * 64 + lane] = has_g ? norm8<true>(xv[i], gv[i], rstd) : norm8<false>(xv[i], gv[i], rstd);
+  for (int t = 0; t < MT; ++t) {
+    const float S = (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]);
+    const float rstd = rstd_from_sumsq(S, inv_k, eps);
+    if (wv == 0 && lane == 0 && t < M && rstd_out != nullptr) rstd_out[t] = rstd;
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = wave + 4 * i;
+      if (c < KC)
+        as[(t * KC + c) * 64 + lane] =
+            has_g ? norm8<true>(xv[t][i], gv[i], rstd) : norm8<false>(xv[t][i], gv[i], rstd);
+    }
   }
   __syncthreads();
   if (rows == 0) return;  // after the last barrier
 
-  float acc[RW];
+  float acc[MT][RW];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    const u32x4 a = as[c * 64 + lane];
+    for (int r = 0; r < RW; ++r) acc[t][r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < RW; ++r) acc[r] = dot8(w[r][c], a, acc[r]);
-  }
+  for (int c = 0; c < KC; ++c)
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    if (r >= rows) break;
-    const float v = wave_total(acc[r]);
-    if (lane == r) {
-      if (out_bf16)
-        static_cast<uint16_t*>(C)[n0 + r] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
-      else
-        static_cast<float*>(C)[n0 + r] = v;
+    for (int t = 0; t < MT; ++t) {
+      const u32x4 a = as[(t * KC + c) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[t][r] = dot8(w[r][c], a, acc[t][r]);
+    }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (t >= M) break;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      if (r >= rows) break;
+      const float v = wave_total(acc[t][r]);
+      if (lane == t * RW + r) {
+        const size_t o = (size_t)t * (size_t)N + (size_t)(n0 + r);
+        if (out_bf16)
+          static_cast<uint16_t*>(C)[o] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+        else
+          static_cast<float*>(C)[o] = v;
+      }
     }
   }
 }
@@ -181,7 +202,7 @@ constexpr int rw_cap(int kc) { return kc <= 6 ? 4 : kc <= 8 ? 3 : kc <= 12 ? 2 :
 
 }  // namespace
 
-bool row_gemv_fits(int64_t K) { return K >= 8 && K <= kRowGemvMaxK; }
+bool row_gemv_fits(int64_t M, int64_t K) { return M >= 1 && M <= kRowGemvMaxM && K >= 8 && K <= kRowGemvMaxK; }
 
 int row_gemv_rows(int64_t N, int kc) {
   const int64_t rw = (N + kRowGemvWaves - 1) / kRowGemvWaves;
@@ -190,18 +211,24 @@ int row_gemv_rows(int64_t N, int kc) {
 }
 
 hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
-                                     void* C, int out_kind, float* rstd_out, int64_t N, int64_t K,
+                                     void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
                                      hipStream_t s) {
-  if (!row_gemv_fits(K) || N < 1 || N > 0x7fffffff) return hipErrorInvalidValue;
+  if (!row_gemv_fits(M, K) || N < 1 || N > 0x7fffffff) return hipErrorInvalidValue;
+  const int mt = M <= 1 ? 1 : 2;
   const int kc = (int)((K + 511) / 512);
   const bool ob = out_kind == OUT_BF16;
   const float inv_k = 1.0f / (float)K;
   const int rw = row_gemv_rows(N, kc);
   const int64_t waves = (N + rw - 1) / rw;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-#define RNL_ROW_GEMV(KC, RW)                                                                                  \
-  hipLaunchKernelGGL((row_gemv_norm_kernel<KC, RW>), grid, block, 0, s, X, gamma, eps, inv_k, W, C, ob,      \
-                     rstd_out, (int)K, (int)N)
+#define RNL_ROW_GEMV1(MT, KC, RW)                                                                           \
+  hipLaunchKernelGGL((row_gemv_norm_kernel<MT, KC, RW>), grid, block, 0, s, X, gamma, eps, inv_k, W, C, ob, \
+                     rstd_out, (int)M, (int)K, (int)N)
+#define RNL_ROW_GEMV(KC, RW)                                     \
+  do {                                                           \
+    if (mt == 1) RNL_ROW_GEMV1(1, KC, RW);                       \
+    else RNL_ROW_GEMV1(2, KC, RW);                               \
+  } while (0)
 #define RNL_ROW_GEMV_KC(KC)                                                          \
   case KC:                                                                           \
     if (rw == 1) RNL_ROW_GEMV(KC, 1);                                                \
@@ -222,6 +249,7 @@ hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* gamma, f
   }
 #undef RNL_ROW_GEMV_KC
 #undef RNL_ROW_GEMV
+#undef RNL_ROW_GEMV1
   return hipGetLastError();
 }
 
