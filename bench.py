@@ -64,12 +64,12 @@ WORKLOADS = {
 }
 DEFAULT = "preattn_qkv_T4096"
 KERNEL_SOURCES = {
-    "gemm": ["gemm_kernel.cuh", "gemm_bf16.hip", "gemm_int8.hip", "common.cuh"],
-    "small_m": ["small_m.hip", "common.cuh", "rows.cuh"],
-    "small_m_norm": ["small_m.hip", "common.cuh", "rows.cuh"],
-    "row_gemv": ["row_gemv.hip", "common.cuh"],
-    "gemm_mx": ["gemm_mx.hip", "common.cuh"],
-    "skinny": ["skinny.hip", "common.cuh"],
+    "gemm": ["gemm_kernel.hpp", "gemm_bf16.hip", "gemm_int8.hip", "common.hpp"],
+    "small_m": ["small_m.hip", "common.hpp", "rows.hpp"],
+    "small_m_norm": ["small_m.hip", "common.hpp", "rows.hpp"],
+    "row_gemv": ["row_gemv.hip", "common.hpp"],
+    "gemm_mx": ["gemm_mx.hip", "common.hpp"],
+    "skinny": ["skinny.hip", "common.hpp"],
 }
 
 
@@ -304,26 +304,85 @@ class Setup:
         torch.cuda.synchronize()
 
 
-def time_loop(fn, steps, warmup, graph=True):
-    """(ms per call, untimed calls made) for fn(i) over `steps` timed calls
-    after about `warmup` untimed ones.
+class ClockSampler:
+    """Samples the graphics (sclk) and memory (mclk) clocks of GPU 0 through amdsmi
+    in a background thread while the timed work runs.  summary() is None when
+    amdsmi is not available or reports nothing."""
 
-    With graph=True the `steps` calls are captured once into a HIP graph; a few
-    eager calls run before the capture, and the rest of the warm-up is made of
-    untimed replays of the same graph, which keep the GPU busy the way the
-    timed region does (the clocks settle under sustained load).  The timed
-    region is one replay, so host-side launch overhead (Python, ctypes) does
-    not leak into the device time; the captured work is exactly the eager
-    calls' kernels.  Events bracket the region on the stream the kernels run
-    on, after a device synchronisation.
+    def __init__(self, period_s=0.0002):
+        self.period, self.samples, self._stop, self._thread, self._h = period_s, [], False, None, None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._amdsmi, self._h = amdsmi, (handles[0] if handles else None)
+        except Exception:  # no amdsmi, or no permission: clocks stay unrecorded
+            self._amdsmi = None
+
+    def _read(self):
+        a = self._amdsmi
+        g = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.GFX)
+        m = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.MEM)
+        return (float(g["clk"]), float(m["clk"]))
+
+    def _run(self):
+        while not self._stop:
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            import threading
+
+            self._stop = False
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop = True
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        import statistics
+
+        sc = [a for a, _ in self.samples]
+        mc = [b for _, b in self.samples]
+        return {"sclk_mhz": {"min": min(sc), "median": statistics.median(sc), "max": max(sc)},
+                "mclk_mhz": {"min": min(mc), "median": statistics.median(mc), "max": max(mc)},
+                "samples": len(self.samples), "source": "amdsmi, sampled during the timed replays"}
+
+
+def time_loop(fn, steps, warmup, graph=True, repeats=1, clocks=None):
+    """Median ms per call of fn(i) over `repeats` timed runs of `steps` calls,
+    after exactly `warmup` untimed calls; also returns every run's ms per call.
+
+    With graph=True the `steps` calls are captured once into a HIP graph after
+    the warm-up calls (capturing runs nothing), and each timed run is one
+    replay, so host-side launch overhead (Python, ctypes) does not leak into
+    the device time; the captured work is exactly the eager calls' kernels.
+    Events bracket each replay on the stream it runs on, after a device
+    synchronisation.  `clocks` (a ClockSampler) samples the clocks during the
+    timed runs.
     """
+    import contextlib
+    import statistics
+
     import torch
 
-    eager = min(warmup, 3) if graph else warmup
-    for i in range(eager):
+    for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    runs = []
     if graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -331,26 +390,27 @@ def time_loop(fn, steps, warmup, graph=True):
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
                 for i in range(steps):
-                    fn(eager + i)
+                    fn(warmup + i)
         torch.cuda.current_stream().wait_stream(s)
-        replays = max(1, -(-(warmup - eager) // steps))
-        for _ in range(replays):
-            g.replay()
         torch.cuda.synchronize()
-        start.record()
-        g.replay()
-        end.record()
-        torch.cuda.synchronize()
+        with clocks if clocks is not None else contextlib.nullcontext():
+            for _ in range(repeats):
+                start.record()
+                g.replay()
+                end.record()
+                torch.cuda.synchronize()
+                runs.append(start.elapsed_time(end) / steps)
         del g
-        done = eager + replays * steps
     else:
-        start.record()
-        for i in range(steps):
-            fn(eager + i)
-        end.record()
-        torch.cuda.synchronize()
-        done = eager
-    return start.elapsed_time(end) / steps, done  # ms
+        with clocks if clocks is not None else contextlib.nullcontext():
+            for r in range(repeats):
+                start.record()
+                for i in range(steps):
+                    fn(warmup + r * steps + i)
+                end.record()
+                torch.cuda.synchronize()
+                runs.append(start.elapsed_time(end) / steps)
+    return statistics.median(runs), runs  # ms
 
 
 def cpu_baseline(setup, target_s=8.0):
@@ -422,13 +482,14 @@ def cpu_baseline(setup, target_s=8.0):
             "sample": f"first {rows} of {T} token rows, {calls} call(s), {per_call:.3f} s per call"}
 
 
-def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False):
+def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False, repeats=1):
     import torch
 
     w = WORKLOADS[name]
     s = Setup(name, w)
-    ms, warm_done = time_loop(s.step, steps, warmup, graph)
-    kms = time_loop(s.kern, steps, warmup, graph)[0] if s.kern is not s.step else ms
+    clocks = ClockSampler()
+    ms, runs = time_loop(s.step, steps, warmup, graph, repeats, clocks)
+    kms = time_loop(s.kern, steps, warmup, graph, repeats)[0] if s.kern is not s.step else ms
     if w["bound"] == "hbm":
         value, unit = bytes_of(w) / (ms * 1e-3) / 1e9, "GB/s"
     else:
@@ -446,7 +507,7 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False):
         "unit": unit,
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warm_done,
+        "warmup": warmup,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -456,12 +517,30 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False):
         "config": {"workload": s.case.name, "description": w["desc"],
                    **{k: w[k] for k in ("T", "K", "R", "Rkv", "N", "Hq", "Hkv", "D") if k in w},
                    "parallelism": "none (1 GPU)", "input_copies": s.copies,
-                   "timing": "hip graph of the timed steps" if graph else "eager launches"},
+                   "timing": ("hip graph of the timed steps" if graph else "eager launches")
+                   + (f", median of {repeats} timed runs" if repeats > 1 else "")},
         "roofline": {"bound": bound, "kernel": s.kernel, "achieved": round(achieved, 3), "peak": PEAK[peak_key],
                      "unit": ru, "frac": round(achieved / PEAK[peak_key], 4),
                      "kernel_ms": round(kms, 6),
                      "traffic": None if traffic is None else int(traffic)},
     }
+    if repeats > 1:
+        line["ms_per_step_runs"] = [round(r, 6) for r in runs]
+    line["clocks"] = clocks.summary()
+    if w["kind"] in ("chain", "mla"):
+        # stage 2 is timed alone (the GEMM on the step's own qr); stage 1 with its reduce
+        # and norm is the rest of the step
+        f2 = 2.0 * w["T"] * w["R"] * w["N"]
+        f1 = flops_of(w) - f2
+        ms1 = ms - kms
+        line["stages"] = [
+            {"stage": "x . W^T (split-K) + reduce + norm (step minus stage 2)", "ms": round(ms1, 6),
+             "achieved": round(f1 / (ms1 * 1e-3) / 1e12, 3), "peak": PEAK["bf16"], "unit": "TFLOP/s",
+             "frac": round(f1 / (ms1 * 1e-3) / 1e12 / PEAK["bf16"], 4)},
+            {"stage": "qr . W_b^T (timed alone)", "ms": round(kms, 6),
+             "achieved": round(f2 / (kms * 1e-3) / 1e12, 3), "peak": PEAK["bf16"], "unit": "TFLOP/s",
+             "frac": round(f2 / (kms * 1e-3) / 1e12 / PEAK["bf16"], 4)},
+        ]
     if vendor and s.vendor is not None:
         # context, not a target: the vendor library (hipBLASLt / rocBLAS through torch) timed the same
         # way on the same operands as the dominant kernel, in the same process
@@ -546,8 +625,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed steps before the timed ones (graph replays after 3 eager calls)")
+    ap.add_argument("--warmup", type=int, default=1000, help="untimed calls before the timed ones")
+    ap.add_argument("--repeats", type=int, default=1,
+                    help="timed runs of --steps calls each; the line reports their median")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -583,7 +663,7 @@ def main():
     names = sorted(WORKLOADS, key=lambda n: n != DEFAULT) if args.all else [args.workload]
     for n in names:
         print(json.dumps(bench_one(n, args.steps, args.warmup, with_cpu=not args.no_cpu, graph=not args.eager,
-                                   vendor=args.vendor)),
+                                   vendor=args.vendor, repeats=args.repeats)),
               flush=True)
 
 

@@ -217,10 +217,11 @@ RNL_API size_t rmsnorm_linear_mxfp8_workspace_bytes(int64_t T, int64_t K, int64_
  *   qr_out  [T, R] bf16, required (the normed low-rank query).
  *   y       [T, N] bf16.
  *   rstd_out [T] fp32 rstd of the q_a rows, or NULL.
- *   R must be a multiple of 8.
+ *   qa_out  [T, R] bf16 q_a, the rows the norm reads, or NULL.
+ *   R must be a multiple of 8.  Outputs must not overlap inputs or each other.
  */
 RNL_API int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps, const void* W_b,
-                    void* qr_out, void* y, float* rstd_out, int64_t T, int64_t K, int64_t R,
+                    void* qr_out, void* y, float* rstd_out, void* qa_out, int64_t T, int64_t K, int64_t R,
                     int64_t N, void* workspace, size_t workspace_bytes, void* stream);
 
 RNL_API size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t N);
@@ -242,14 +243,15 @@ RNL_API size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, 
  *   y         [T, N]   = round_bf16(qr . W_b^T), W_b [N, R] bf16.
  *   gamma_cq [R], gamma_ckv [Rkv] bf16 or NULL; one eps for both norms.
  *   rstd_q_out, rstd_kv_out [T] fp32 or NULL.
+ *   qakv_out  [T, R + Rkv] bf16 [q_a | kv], the rows the two norms read, or NULL.
  *   R and Rkv must be multiples of 8.  Outputs must not overlap inputs.
  *
  * Errors: as norm_proj_chain.
  */
 RNL_API int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, const void* gamma_ckv, float eps,
                             const void* W_b, void* qr_out, void* kv_out, void* y, float* rstd_q_out,
-                            float* rstd_kv_out, int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            float* rstd_kv_out, void* qakv_out, int64_t T, int64_t K, int64_t R, int64_t Rkv,
+                            int64_t N, void* workspace, size_t workspace_bytes, void* stream);
 
 RNL_API size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N);
 

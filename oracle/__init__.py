@@ -19,6 +19,7 @@ from .rmsnorm_linear import (  # noqa: F401
     quant_rows,
     quant_values,
     int8_gemm,
+    int8_gemm_int64,
     dequant,
     rmsnorm_linear_bf16,
     rmsnorm_linear_fp32w,

@@ -217,12 +217,29 @@ def quant_rows(n: np.ndarray):
 
 
 def int8_gemm(q: np.ndarray, Wq: np.ndarray) -> np.ndarray:
-    """acc[t, j] = sum_k q[t,k] * Wq[j,k], exact in int64 (AT-09 INT8 mode:
-    int8 x int8 -> INT32 matmul with b_trans).  Raises if a sum leaves int32."""
-    acc = q.astype(np.int64) @ np.asarray(Wq, dtype=np.int8).astype(np.int64).T
+    """acc[t, j] = sum_k q[t,k] * Wq[j,k], exact (AT-09 INT8 mode: int8 x int8
+    -> INT32 matmul with b_trans).  Raises if a sum leaves int32.
+
+    Every product is an integer of magnitude at most 128^2, so every partial
+    sum is an integer of magnitude at most K * 128^2.  While that bound is
+    below 2^53 each partial sum is exactly representable in fp64, so an fp64
+    accumulation gives the exact integer in any summation order; that form is
+    used then (numpy has no fast integer product).  Beyond it the sum is formed
+    in int64 (int8_gemm_int64)."""
+    Wq = np.asarray(Wq, dtype=np.int8)
+    K = q.shape[-1]
+    if K * 128 * 128 < 2**53:
+        acc = (q.astype(F64) @ Wq.astype(F64).T).astype(np.int64)
+    else:
+        acc = int8_gemm_int64(q, Wq)
     if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -(2**31)):
         raise OverflowError("int8 GEMM result does not fit int32")
     return acc
+
+
+def int8_gemm_int64(q: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+    """The same sum in int64 arithmetic (slow; the reference for the fp64 form)."""
+    return q.astype(np.int64) @ np.asarray(Wq, dtype=np.int8).astype(np.int64).T
 
 
 def dequant(acc: np.ndarray, x_scale: np.ndarray, w_scale: np.ndarray) -> np.ndarray:

@@ -92,8 +92,8 @@ def load_library() -> ctypes.CDLL:
     lib.rmsnorm_linear_int8.restype = ctypes.c_int
     lib.rmsnorm_linear_int8_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.c_int]
     lib.rmsnorm_linear_int8_workspace_bytes.restype = ctypes.c_size_t
-    lib.norm_proj_chain.argtypes = [_c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
-                                    _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+    lib.norm_proj_chain.argtypes = [_c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                    _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
     lib.norm_proj_chain.restype = ctypes.c_int
     lib.norm_proj_chain_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64]
     lib.norm_proj_chain_workspace_bytes.restype = ctypes.c_size_t
@@ -123,7 +123,7 @@ def load_library() -> ctypes.CDLL:
                                        _c_i64, _c_i64, _c_p]
     lib.head_rms_norm_bf16.restype = ctypes.c_int
     lib.mla_prolog_bf16.argtypes = [_c_p, _c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
-                                    _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+                                    _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_size_t, _c_p]
     lib.mla_prolog_bf16.restype = ctypes.c_int
     lib.mla_prolog_bf16_workspace_bytes.argtypes = [_c_i64] * 5
     lib.mla_prolog_bf16_workspace_bytes.restype = ctypes.c_size_t
@@ -327,8 +327,9 @@ def add_rmsnorm_linear_int8(x, residual, gamma, eps, Wq, w_scale, out_dtype=torc
     return y, x_add_out
 
 
-def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None, workspace=None):
-    """q_a_proj -> RMSNorm -> q_b_proj (MLA low-rank query).  Returns (y, qr_out)."""
+def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None, qa_out=None, workspace=None):
+    """q_a_proj -> RMSNorm -> q_b_proj (MLA low-rank query).  Returns (y, qr_out).
+    ``qa_out`` (bf16 [T, R]) receives q_a, the rows the norm reads."""
     lib = load_library()
     _dev_tensor(x, "x", torch.bfloat16, 2)
     _dev_tensor(W_a, "W_a", torch.bfloat16, 2)
@@ -348,13 +349,15 @@ def norm_proj_chain(x, W_a, gamma, eps, W_b, qr_out=None, y=None, rstd_out=None,
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     _dev_tensor(qr_out, "qr_out", torch.bfloat16)
     _dev_tensor(y, "y", torch.bfloat16)
+    _dev_tensor(qa_out, "qa_out", torch.bfloat16)
     _shape(tuple(qr_out.shape) == (T, R), "qr_out must be [T, R]")
     _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
+    _shape(qa_out is None or tuple(qa_out.shape) == (T, R), "qa_out must be [T, R]")
     with torch.cuda.device(x.device):
         need = int(lib.norm_proj_chain_workspace_bytes(T, K, R, N))
         ws, ws_bytes = _workspace(need, x.device, workspace)
         rc = lib.norm_proj_chain(_ptr(x), _ptr(W_a), _ptr(gamma), float(eps), _ptr(W_b), _ptr(qr_out), _ptr(y),
-                                 _ptr(rstd_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
+                                 _ptr(rstd_out), _ptr(qa_out), T, K, R, N, _ptr(ws), ws_bytes, _stream(x.device))
     _check(rc)
     return y, qr_out
 
@@ -438,9 +441,10 @@ def linear_mxfp8(xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, y=None):
 
 
 def mla_prolog_bf16(x, W_akv, R, gamma_cq, gamma_ckv, eps, W_b, qr_out=None, kv_out=None, y=None, rstd_q_out=None,
-                    rstd_kv_out=None, workspace=None):
+                    rstd_kv_out=None, qakv_out=None, workspace=None):
     """MLA prolog query chain + KV branch (AT-10 page section 5).  W_akv stacks the
     query down-projection (rows [0, R)) and the KV projection (rows [R, R + Rkv)).
+    ``qakv_out`` (bf16 [T, R + Rkv]) receives [q_a | kv], the rows the norms read.
     Returns (y [T, N], qr [T, R], kv [T, Rkv])."""
     lib = load_library()
     for t, n in ((x, "x"), (W_akv, "W_akv"), (W_b, "W_b")):
@@ -466,12 +470,14 @@ def mla_prolog_bf16(x, W_akv, R, gamma_cq, gamma_ckv, eps, W_b, qr_out=None, kv_
         _shape(tuple(t.shape) == shp, f"{n} must be {list(shp)}")
         outs.append(t)
     qr_out, kv_out, y = outs
+    _dev_tensor(qakv_out, "qakv_out", torch.bfloat16)
+    _shape(qakv_out is None or tuple(qakv_out.shape) == (T, R + Rkv), "qakv_out must be [T, R + Rkv]")
     with torch.cuda.device(x.device):
         need = int(lib.mla_prolog_bf16_workspace_bytes(T, K, R, Rkv, N))
         ws, ws_bytes = _workspace(need, x.device, workspace)
         rc = lib.mla_prolog_bf16(_ptr(x), _ptr(W_akv), _ptr(gamma_cq), _ptr(gamma_ckv), float(eps), _ptr(W_b),
-                                 _ptr(qr_out), _ptr(kv_out), _ptr(y), _ptr(rstd_q_out), _ptr(rstd_kv_out), T, K, R,
-                                 Rkv, N, _ptr(ws), ws_bytes, _stream(x.device))
+                                 _ptr(qr_out), _ptr(kv_out), _ptr(y), _ptr(rstd_q_out), _ptr(rstd_kv_out),
+                                 _ptr(qakv_out), T, K, R, Rkv, N, _ptr(ws), ws_bytes, _stream(x.device))
     _check(rc)
     return y, qr_out, kv_out
 

@@ -316,7 +316,7 @@ size_t norm_proj_chain_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t 
 }
 
 int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps, const void* W_b,
-                    void* qr_out, void* y, float* rstd_out, int64_t T, int64_t K, int64_t R,
+                    void* qr_out, void* y, float* rstd_out, void* qa_out, int64_t T, int64_t K, int64_t R,
                     int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
   if (x == nullptr || W_a == nullptr || W_b == nullptr || qr_out == nullptr || y == nullptr)
     return fail(RNL_ERR_NULL, "x, W_a, W_b, qr_out and y are required");
@@ -330,6 +330,7 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
   RNL_ALIGN(qr_out, 16, "qr_out");
   RNL_ALIGN(y, 16, "y");
   RNL_ALIGN(rstd_out, 4, "rstd_out");
+  RNL_ALIGN(qa_out, 16, "qa_out");
   RNL_ALIGN(workspace, 256, "workspace");
   const size_t need = norm_proj_chain_workspace_bytes(T, K, R, N);
   if (workspace == nullptr || workspace_bytes < need)
@@ -340,6 +341,7 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
   const uint16_t* wa = static_cast<const uint16_t*>(W_a);
   const uint16_t* gb = static_cast<const uint16_t*>(gamma);
   uint16_t* qr = static_cast<uint16_t*>(qr_out);
+  uint16_t* qa_keep = static_cast<uint16_t*>(qa_out);
   const int ks = chain_splits(T, R, K);
   hipError_t e;
   if (ks > 1) {
@@ -348,10 +350,11 @@ int norm_proj_chain(const void* x, const void* W_a, const void* gamma, float eps
     float* part = static_cast<float*>(workspace);
     e = rnl::launch_gemm_bf16_splitk(xb, wa, part, T, R, K, ks, s);
     if (e != hipSuccess) return hip_status(e, "chain stage-1 split-K GEMM launch");
-    e = rnl::launch_reduce_norm_bf16(part, ks, R, gb, eps, T, R, qr, rstd_out, s);
+    e = rnl::launch_reduce_norm_bf16(part, ks, R, gb, eps, T, R, qr, rstd_out, qa_keep, R, s);
     if (e != hipSuccess) return hip_status(e, "chain reduce+norm launch");
   } else {
-    uint16_t* qa = static_cast<uint16_t*>(workspace);
+    // the stage-1 rows go to qa_out when the caller asks for them
+    uint16_t* qa = qa_keep != nullptr ? qa_keep : static_cast<uint16_t*>(workspace);
     e = project_bf16(xb, wa, qa, rnl::OUT_BF16, T, R, K, s);
     if (e != hipSuccess) return hip_status(e, "chain stage-1 projection launch");
     e = rnl::launch_norm_rows_bf16(qa, gb, eps, T, R, qr, rstd_out, s);
@@ -413,8 +416,8 @@ size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, int64_t 
 
 int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, const void* gamma_ckv, float eps,
                     const void* W_b, void* qr_out, void* kv_out, void* y, float* rstd_q_out, float* rstd_kv_out,
-                    int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    void* qakv_out, int64_t T, int64_t K, int64_t R, int64_t Rkv, int64_t N, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (x == nullptr || W_akv == nullptr || W_b == nullptr || qr_out == nullptr || kv_out == nullptr || y == nullptr)
     return fail(RNL_ERR_NULL, "x, W_akv, W_b, qr_out, kv_out and y are required");
   RNL_TRY(check_dims(T, K, N, kMaxK));
@@ -432,6 +435,7 @@ int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, cons
   RNL_ALIGN(y, 16, "y");
   RNL_ALIGN(rstd_q_out, 4, "rstd_q_out");
   RNL_ALIGN(rstd_kv_out, 4, "rstd_kv_out");
+  RNL_ALIGN(qakv_out, 16, "qakv_out");
   RNL_ALIGN(workspace, 256, "workspace");
   const size_t need = mla_prolog_bf16_workspace_bytes(T, K, R, Rkv, N);
   if (workspace == nullptr || workspace_bytes < need)
@@ -445,6 +449,7 @@ int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, cons
   uint16_t* qr = static_cast<uint16_t*>(qr_out);
   uint16_t* kvo = static_cast<uint16_t*>(kv_out);
   const int64_t Rt = R + Rkv;
+  uint16_t* keep = static_cast<uint16_t*>(qakv_out);
   const int ks = chain_splits(T, Rt, K);
   hipError_t e;
   // one pass over x for both branches: [q_a | kv] = x . [W_a; W_kv]^T, then each
@@ -453,12 +458,14 @@ int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, cons
     float* part = static_cast<float*>(workspace);
     e = rnl::launch_gemm_bf16_splitk(xb, w, part, T, Rt, K, ks, s);
     if (e != hipSuccess) return hip_status(e, "stage-1 split-K GEMM launch");
-    e = rnl::launch_reduce_norm_bf16(part, ks, Rt, gq, eps, T, R, qr, rstd_q_out, s);
+    e = rnl::launch_reduce_norm_bf16(part, ks, Rt, gq, eps, T, R, qr, rstd_q_out, keep, Rt, s);
     if (e != hipSuccess) return hip_status(e, "query reduce+norm launch");
-    e = rnl::launch_reduce_norm_bf16(part + R, ks, Rt, gkv, eps, T, Rkv, kvo, rstd_kv_out, s);
+    e = rnl::launch_reduce_norm_bf16(part + R, ks, Rt, gkv, eps, T, Rkv, kvo, rstd_kv_out,
+                                     keep == nullptr ? nullptr : keep + R, Rt, s);
     if (e != hipSuccess) return hip_status(e, "kv reduce+norm launch");
   } else {
-    uint16_t* qakv = static_cast<uint16_t*>(workspace);
+    // the stage-1 rows go to qakv_out when the caller asks for them
+    uint16_t* qakv = keep != nullptr ? keep : static_cast<uint16_t*>(workspace);
     e = project_bf16(xb, w, qakv, rnl::OUT_BF16, T, Rt, K, s);
     if (e != hipSuccess) return hip_status(e, "stage-1 projection launch");
     e = rnl::launch_norm_rows_bf16_strided(qakv, Rt, gq, eps, T, R, qr, rstd_q_out, s);

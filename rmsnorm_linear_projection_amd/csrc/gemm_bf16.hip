@@ -1,5 +1,5 @@
-// bf16 instantiations of the projection GEMM (kernel in gemm_kernel.cuh).
-#include "gemm_kernel.cuh"
+// bf16 instantiations of the projection GEMM (kernel in gemm_kernel.hpp).
+#include "gemm_kernel.hpp"
 
 namespace rnl {
 using namespace gemm_detail;

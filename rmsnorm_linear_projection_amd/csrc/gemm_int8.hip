@@ -1,8 +1,8 @@
-// int8 instantiations of the projection GEMM (kernel in gemm_kernel.cuh).  This unit
+// int8 instantiations of the projection GEMM (kernel in gemm_kernel.hpp).  This unit
 // is compiled with the MFMA accumulators in VGPRs (-amdgpu-mfma-vgpr-form): with
 // AGPR accumulators the int32 MFMA loop gets its accumulators re-shuffled every
 // iteration by the register allocator.
-#include "gemm_kernel.cuh"
+#include "gemm_kernel.hpp"
 
 namespace rnl {
 using namespace gemm_detail;

@@ -42,7 +42,7 @@
 // int32) to slice z of a [KSPLIT, M, N] buffer; the caller reduces the slices.
 #pragma once
 
-#include "common.cuh"
+#include "common.hpp"
 #include "launch.h"
 
 namespace rnl {

@@ -29,7 +29,7 @@
 // is read.  Both phases run weight fragment by weight fragment, and phase B
 // reloads weight fragment j for the next k-step right after its last MFMA, so
 // the weight fragments need no second register set.
-#include "common.cuh"
+#include "common.hpp"
 #include "launch.h"
 
 namespace rnl {

@@ -21,7 +21,7 @@
 // together.  The sum of squares is reduced inside the group with DPP moves;
 // each chunk is written back by the lane that read it, so y_out may be y_in.
 #include "launch.h"
-#include "rows.cuh"
+#include "rows.hpp"
 
 namespace rnl {
 namespace {

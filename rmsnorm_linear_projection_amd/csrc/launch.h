@@ -32,9 +32,12 @@ hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t
                            hipStream_t s);
 // Same norm (bf16 out) applied to rows that are the bf16 rounding of the sum of S
 // fp32 split-K partials, added in split order: row t of slice z starts at
-// part + z * T * ld + t * ld (ld >= K, a multiple of 8); out is [T, K].
+// part + z * T * ld + t * ld (ld >= K, a multiple of 8); out is [T, K].  When
+// sum_out is not null the bf16 row sums (the rows the norm reads) are also
+// written, row t at sum_out + t * sum_ld (sum_ld a multiple of 8).
 hipError_t launch_reduce_norm_bf16(const float* part, int S, int64_t ld, const uint16_t* gamma, float eps,
-                                   int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s);
+                                   int64_t T, int64_t K, uint16_t* out, float* rstd_out, uint16_t* sum_out,
+                                   int64_t sum_ld, hipStream_t s);
 // The bf16 norm of K values of rows with stride ld (x + t * ld; ld a multiple of
 // 8); out is [T, K].
 hipError_t launch_norm_rows_bf16_strided(const uint16_t* x, int64_t ld, const uint16_t* gamma, float eps, int64_t T,

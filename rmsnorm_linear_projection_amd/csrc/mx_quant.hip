@@ -15,7 +15,7 @@
 // Every lane runs the same number of iterations, so the cross-lane moves never
 // run in divergent code.
 #include "launch.h"
-#include "rows.cuh"
+#include "rows.hpp"
 
 namespace rnl {
 namespace {

@@ -20,7 +20,7 @@
 #include <algorithm>
 
 #include "launch.h"
-#include "rows.cuh"
+#include "rows.hpp"
 
 namespace rnl {
 namespace {
@@ -117,6 +117,8 @@ struct RowPartials {
   int64_t TK;         // slice stride
   int64_t ld;         // row stride
   int S;
+  uint16_t* sum_out;  // when not null, the bf16 row sums go to row t at sum_out + t * sum_ld
+  int64_t sum_ld;
   __device__ u32x4 operator()(int64_t t, int idx) const {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
     for (int z = 0; z < S; ++z) {
@@ -127,7 +129,9 @@ struct RowPartials {
     return u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
                  pack_bf16x2(hi[2], hi[3])};
   }
-  __device__ void keep(int64_t, int, u32x4) const {}
+  __device__ void keep(int64_t t, int idx, u32x4 v) const {
+    if (sum_out != nullptr) reinterpret_cast<u32x4*>(sum_out + t * sum_ld)[idx] = v;
+  }
 };
 
 // CPT > 0: each thread keeps CPT 16-byte chunks of the row in registers.
@@ -430,8 +434,10 @@ hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t
 }
 
 hipError_t launch_reduce_norm_bf16(const float* part, int S, int64_t ld, const uint16_t* gamma, float eps,
-                                   int64_t T, int64_t K, uint16_t* out, float* rstd_out, hipStream_t s) {
-  return launch_norm<false>(RowPartials{part, T * ld, ld, S}, gamma, eps, T, K, out, nullptr, rstd_out, s);
+                                   int64_t T, int64_t K, uint16_t* out, float* rstd_out, uint16_t* sum_out,
+                                   int64_t sum_ld, hipStream_t s) {
+  return launch_norm<false>(RowPartials{part, T * ld, ld, S, sum_out, sum_ld}, gamma, eps, T, K, out, nullptr,
+                            rstd_out, s);
 }
 
 }  // namespace rnl

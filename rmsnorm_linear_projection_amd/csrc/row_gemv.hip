@@ -30,7 +30,7 @@
 //     N = 6144: 10.1 us at T = 1, 11.4 at T = 2 (against 12.5 for the MFMA
 //     kernel); at T = 3 and 4 (13.5, 14.0 against 12.4) the MFMA kernel stays.
 // Rows past N and chunks past K read as zero through the buffer resource.
-#include "common.cuh"
+#include "common.hpp"
 #include "launch.h"
 
 namespace rnl {

@@ -1,7 +1,7 @@
 // Row helpers shared by the norm kernels (the pre-pass and the per-head stage).
 #pragma once
 
-#include "common.cuh"
+#include "common.hpp"
 
 namespace rnl {
 

@@ -22,7 +22,7 @@
 // ([N, K] fp32, a few MB) is re-read by every token group and stays in L2.
 #include <algorithm>
 
-#include "common.cuh"
+#include "common.hpp"
 #include "launch.h"
 
 namespace rnl {

@@ -22,7 +22,7 @@
 // with KU = 4, 14.5 with 3 and 15.4 with 1).
 // The four wavefront accumulators are added through LDS in a fixed order.
 #include "launch.h"
-#include "rows.cuh"
+#include "rows.hpp"
 
 namespace rnl {
 namespace {

@@ -242,8 +242,8 @@ def test_head_norm_validation(lib, kw, code):
 
 
 def mla_call(lib, x=FAKE, W=FAKE, gq=NULL, gkv=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, kv=FAKE, y=FAKE, rq=NULL, rkv=NULL,
-             T=4, K=64, R=32, Rkv=16, N=8, ws=FAKE, wsb=1 << 30):
-    return lib.mla_prolog_bf16(x, W, gq, gkv, eps, Wb, qr, kv, y, rq, rkv, T, K, R, Rkv, N, ws, wsb, NULL)
+             qakv=NULL, T=4, K=64, R=32, Rkv=16, N=8, ws=FAKE, wsb=1 << 30):
+    return lib.mla_prolog_bf16(x, W, gq, gkv, eps, Wb, qr, kv, y, rq, rkv, qakv, T, K, R, Rkv, N, ws, wsb, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -254,6 +254,7 @@ def mla_call(lib, x=FAKE, W=FAKE, gq=NULL, gkv=NULL, eps=1e-6, Wb=FAKE, qr=FAKE,
     (dict(R=20), "RNL_ERR_SHAPE"),
     (dict(gkv=ODD), "RNL_ERR_ALIGN"),
     (dict(rkv=ctypes.c_void_p(0x10001)), "RNL_ERR_ALIGN"),
+    (dict(qakv=ODD), "RNL_ERR_ALIGN"),
     (dict(ws=NULL), "RNL_ERR_WORKSPACE"),
     (dict(eps=-1.0), "RNL_ERR_ARG"),
 ])
@@ -298,9 +299,9 @@ def test_mxfp8_workspace_and_atoms(lib):
     assert lib.linear_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 128, 8, NULL) == E["RNL_ERR_DTYPE"]
 
 
-def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, T=4, K=64, R=32,
-               N=8, ws=FAKE, wsb=1 << 30):
-    return lib.norm_proj_chain(x, Wa, g, eps, Wb, qr, y, rstd, T, K, R, N, ws, wsb, NULL)
+def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE, rstd=NULL, qa=NULL, T=4, K=64,
+               R=32, N=8, ws=FAKE, wsb=1 << 30):
+    return lib.norm_proj_chain(x, Wa, g, eps, Wb, qr, y, rstd, qa, T, K, R, N, ws, wsb, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -310,6 +311,7 @@ def chain_call(lib, x=FAKE, Wa=FAKE, g=NULL, eps=1e-6, Wb=FAKE, qr=FAKE, y=FAKE,
     (dict(K=0), "RNL_ERR_SHAPE"),
     (dict(eps=-0.5), "RNL_ERR_ARG"),
     (dict(Wa=ODD), "RNL_ERR_ALIGN"),
+    (dict(qa=ODD), "RNL_ERR_ALIGN"),
     (dict(ws=NULL), "RNL_ERR_WORKSPACE"),
 ])
 def test_chain_validation(lib, kw, code):

@@ -95,13 +95,15 @@ def test_graph_chain_and_mla():
     qr = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((T, Rkv), dtype=torch.bfloat16, device="cuda")
     ws = ws_for("mla", T, K, R, Rkv, N)
+    qakv = torch.empty((T, R + Rkv), dtype=torch.bfloat16, device="cuda")
     check_replays(lambda: rnl.mla_prolog_bf16(t["x"], W_akv, R, t["gamma"], t["gamma_ckv"], EPS, t["W_b"], qr_out=qr,
-                                              kv_out=kv, y=y, workspace=ws), [y, qr, kv])
+                                              kv_out=kv, y=y, qakv_out=qakv, workspace=ws), [y, qr, kv, qakv])
     y2 = torch.empty_like(y)
     qr2 = torch.empty_like(qr)
+    qa2 = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
     ws2 = ws_for("chain", T, K, R, N)
     check_replays(lambda: rnl.norm_proj_chain(t["x"], t["W_a"], t["gamma"], EPS, t["W_b"], qr_out=qr2, y=y2,
-                                              workspace=ws2), [y2, qr2])
+                                              qa_out=qa2, workspace=ws2), [y2, qr2, qa2])
 
 
 def test_graph_preattn_block():

@@ -12,8 +12,8 @@ oracle):
     of the oracle's dequant of those accumulators;
   * fp32 weights (no bf16 cast): |y - y_ref| <= 1e-5 * max(|y_ref|, rms(y_ref));
   * every path is deterministic: two runs give identical bits.
-Large workloads are checked on sampled rows (rows are independent in every
-entry point), at the sizes and launch configuration the benchmark times.
+Every output row is checked, at full size too, in the launch configuration the
+benchmark times.
 """
 from __future__ import annotations
 
@@ -55,14 +55,6 @@ def dev(t):
     return None if t is None else t.cuda()
 
 
-def sample_rows(T, n=24, seed=0):
-    if T <= 64:
-        return np.arange(T)
-    rng = np.random.default_rng(seed)
-    fixed = [0, 1, T // 2, T - 2, T - 1]
-    return np.unique(np.concatenate([fixed, rng.choice(T, n, replace=False)]))
-
-
 def assert_bf16_close(y, y_ref, what):
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
@@ -71,6 +63,18 @@ def assert_bf16_close(y, y_ref, what):
     bad = err > bound
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
                            f"worst err {err.max():.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def assert_bf16_two_roundings(y, y_ref, what):
+    """End-to-end bound for a bf16 value normed from a bf16 intermediate that the oracle forms on its own (the
+    chain's q_a): that input may differ from the oracle's by one bf16 ulp (at most 2^-7 relative) where its fp32
+    accumulation sits next to a rounding boundary; the norm carries the relative difference through and both sides
+    round once more to bf16 (at most 2^-8 relative each), so |y - y_ref| <= 2^-6 (|y_ref| + 1e-2)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    bad = err > 2.0 ** -6 * (np.abs(y_ref) + 1e-2)
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outside 2^-6 (|y_ref| + 1e-2); worst {err.max():.3g}"
 
 
 def assert_rstd(rstd_gpu, rstd_ref, what, ulps=8):
@@ -160,7 +164,7 @@ def test_bf16_fp32_output(T, K, N):
 ])
 def test_bf16_large_tiles_ragged(T, K, N):
     case = synthetic.norm_linear_case(T, K, N, seed=11)
-    check_bf16_case(case, rows=sample_rows(T))
+    check_bf16_case(case)
 
 
 @pytest.mark.parametrize("scale", [0.0, 1024.0, 1.0 / 4096])
@@ -193,7 +197,7 @@ def test_bf16_zero_and_scaled_rows():
 def test_bf16_preattn_qkv_full_size(T):
     """Pre-attention norm + fused QKV projection, K=4096, N=6144, at full size."""
     case = synthetic.preattn_qkv(T)
-    y1 = check_bf16_case(case, rows=sample_rows(T, 40))
+    y1 = check_bf16_case(case)
     y2, _ = run_bf16(case)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
 
@@ -258,7 +262,7 @@ def test_int8_small(T, K, N, gamma):
 
 def test_int8_tiles_ragged():
     case = synthetic.int8_case(2000, 144, 4000, seed=17)  # 256 x 128 tiles
-    check_int8_case(case, rows=sample_rows(2000))
+    check_int8_case(case)
 
 
 def test_int8_zero_row():
@@ -270,12 +274,28 @@ def test_int8_zero_row():
     assert (f32(yb)[4] == 0).all()
 
 
-def test_int8_w8a8_full_size():
-    """INT8 W8A8 norm + linear, T=2048, K=4096, N=4096, at full size."""
+def xq_mismatch_own_rstd(case, xq):
+    """End-to-end codes against the oracle's quantisation with its own rstd (informational).  The device's rstd
+    may differ from the oracle's by a few ulps (a different fp32 summation order), which moves fl(n * s) by far
+    less than one unit; a code can then only differ by one, where that product sits within the shift of a .5 tie.
+    Returns (count of differing codes, largest difference)."""
+    gb = None if case["gamma"] is None else bits(case["gamma"])
+    n_own, _ = O.rms_norm_rows(bits(case["x"]), gb, EPS)
+    q_own, _, _ = O.quant_rows(n_own)
+    d = np.abs(xq.astype(np.int16) - q_own.astype(np.int16))
+    return int((d != 0).sum()), int(d.max())
+
+
+def test_int8_w8a8_full_size(record_property):
+    """INT8 W8A8 norm + linear, T=2048, K=4096, N=4096, every row."""
     case = synthetic.int8_w8a8()
-    y1 = check_int8_case(case, rows=sample_rows(2048, 32))
-    y2, _, _, _ = run_int8(case, torch.bfloat16)
+    y1 = check_int8_case(case)
+    y2, xq, _, _ = run_int8(case, torch.bfloat16)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    count, worst = xq_mismatch_own_rstd(case, xq)
+    record_property("xq_mismatch_vs_oracle_own_rstd", count)
+    print(f"int8 W8A8: {count} of {xq.size} codes differ from the oracle's own-rstd quantisation (max |diff| {worst})")
+    assert worst <= 1
 
 
 # ---------------------------------------------------------------------------
@@ -339,29 +359,41 @@ def test_skinny_fp32_full_size():
 # ---------------------------------------------------------------------------
 def run_chain(case):
     x, Wa, g, Wb = (dev(case[k]) for k in ("x", "W_a", "gamma", "W_b"))
-    T = x.shape[0]
+    T, R = x.shape[0], Wa.shape[0]
     rstd = torch.empty(T, dtype=torch.float32, device="cuda")
-    y, qr = rnl.norm_proj_chain(x, Wa, g, EPS, Wb, rstd_out=rstd)
+    qa = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    y, qr = rnl.norm_proj_chain(x, Wa, g, EPS, Wb, rstd_out=rstd, qa_out=qa)
     torch.cuda.synchronize()
-    return y.cpu(), qr.cpu(), rstd.cpu().numpy()
+    return y.cpu(), qr.cpu(), qa.cpu(), rstd.cpu().numpy()
 
 
-def check_chain_case(case, rows=None):
-    y, qr, rstd = run_chain(case)
-    T = case["x"].shape[0]
-    rows = np.arange(T) if rows is None else rows
-    xb = bits(case["x"])[rows]
+def check_normed_stage(rows_in, gamma_bits, rstd, out_bits, what):
+    """The norm step of the chain on the device's own input rows (bf16 bits):
+    rstd within 8 ulps of the oracle's rstd of those rows, and the normed bf16
+    rows bit-exact given the device's rstd."""
+    _, r_own = O.rms_norm_rows(rows_in, gamma_bits, EPS)
+    assert_rstd(rstd, r_own, what)
+    n, _ = O.rms_norm_rows(rows_in, gamma_bits, EPS, rstd=rstd)
+    want = O.f32_to_bf16_bits(n)
+    bad = out_bits != want
+    assert not bad.any(), f"{what}: {int(bad.sum())} normed values not bit-exact given the device's input and rstd"
+
+
+def check_chain_case(case):
+    y, qr, qa, rstd = run_chain(case)
+    xb = bits(case["x"])
     Wa, Wb = bits(case["W_a"]), bits(case["W_b"])
     gb = None if case["gamma"] is None else bits(case["gamma"])
-    ref = O.norm_proj_chain(xb, Wa, gb, EPS, Wb)
-    # stage 1 + norm: qr is a bf16 output; its input q_a is itself a rounded
-    # accumulation, so rstd is compared with a relative bound
-    rel = np.abs(rstd[rows].astype(np.float64) / ref["rstd"] - 1)
-    assert rel.max() < 1e-3, f"{case.name}: rstd rel err {rel.max():.3g}"
-    assert_bf16_close(f32(qr)[rows], O.bf16_bits_to_f32(ref["qr"]), case.name + " qr")
+    # stage 1: q_a is a bf16 output of an fp32 accumulation of x . W_a^T
+    qab = bits(qa)
+    assert_bf16_close(O.bf16_bits_to_f32(qab), O.project_bf16(O.bf16_bits_to_f32(xb), Wa), case.name + " q_a")
+    # the norm on the device's q_a (AT-10 page section 5: q_a -> rms_norm -> x gamma -> bf16 = qr)
+    check_normed_stage(qab, gb, rstd, bits(qr), case.name + " qr")
     # stage 2 from the device's qr: identical bf16 inputs
-    y_ref = O.project_bf16(O.bf16_bits_to_f32(bits(qr)[rows]), Wb)
-    assert_bf16_close(f32(y)[rows], y_ref, case.name + " y")
+    assert_bf16_close(f32(y), O.project_bf16(O.bf16_bits_to_f32(bits(qr)), Wb), case.name + " y")
+    # end to end against the oracle's own stage 1
+    ref = O.norm_proj_chain(xb, Wa, gb, EPS, Wb)
+    assert_bf16_two_roundings(f32(qr), O.bf16_bits_to_f32(ref["qr"]), case.name + " qr end to end")
     return y
 
 
@@ -379,10 +411,10 @@ def test_chain_small(T, K, R, N, gamma):
 
 
 def test_mla_q_chain_full_size():
-    """Low-rank query chain x[1024,7168] -> W_a[1536,7168] -> norm -> W_b[24576,1536]."""
+    """Low-rank query chain x[1024,7168] -> W_a[1536,7168] -> norm -> W_b[24576,1536], every row."""
     case = synthetic.mla_q_chain()
-    y1 = check_chain_case(case, rows=sample_rows(1024, 24))
-    y2, _, _ = run_chain(case)
+    y1 = check_chain_case(case)
+    y2 = run_chain(case)[0]
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
 
 
@@ -445,9 +477,8 @@ def test_atom_linear_bf16(M, K, N):
     W = synthetic.normal((N, K), 1.0 / np.sqrt(K), 3, 12)
     y = rnl.linear_bf16(dev(a), dev(W), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = sample_rows(M)
-    ref = O.project_bf16(O.bf16_bits_to_f32(bits(a)[rows]), bits(W))
-    assert_bf16_close(f32(y)[rows], ref, "linear_bf16")
+    ref = O.project_bf16(O.bf16_bits_to_f32(bits(a)), bits(W))
+    assert_bf16_close(f32(y), ref, "linear_bf16")
 
 
 @pytest.mark.parametrize("M,K,N", [
@@ -497,10 +528,9 @@ def test_atom_linear_int8_large_tiles():
     acc = rnl.linear_int8(dev(q), dev(xs), dev(W), dev(ws), out_dtype=torch.int32)
     y = rnl.linear_int8(dev(q), dev(xs), dev(W), dev(ws), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = sample_rows(M)
-    acc_ref = O.int8_gemm(q.numpy()[rows], W.numpy())
-    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), acc_ref)
-    assert np.array_equal(y.cpu().numpy()[rows], O.dequant(acc_ref, xs.numpy()[rows], ws.numpy()))
+    acc_ref = O.int8_gemm(q.numpy(), W.numpy())
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    assert np.array_equal(y.cpu().numpy(), O.dequant(acc_ref, xs.numpy(), ws.numpy()))
 
 
 # ---------------------------------------------------------------------------
@@ -588,7 +618,7 @@ def test_add_fp32w(T, K, N, gamma):
 def test_add_preattn_qkv_full_size(T):
     """Residual add -> pre-attention norm -> fused QKV projection, K=4096, N=6144, at full size."""
     case = synthetic.preattn_qkv_add(T)
-    y1 = check_add_bf16_case(case, rows=sample_rows(T, 40))
+    y1 = check_add_bf16_case(case)
     y2, _, _ = run_add_bf16(case)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
 
@@ -647,7 +677,7 @@ def test_add_int8(T, K, N, gamma):
 def test_add_int8_w8a8_full_size():
     """Residual add, then INT8 W8A8 norm + linear, T=2048, K=4096, N=4096, at full size."""
     case = synthetic.with_residual(synthetic.int8_w8a8())
-    check_add_int8_case(case, rows=sample_rows(2048, 32))
+    check_add_int8_case(case)
 
 
 # ---------------------------------------------------------------------------
@@ -771,7 +801,7 @@ def test_preattn_small(T, K, Hq, Hkv, D, residual, rope, head_gamma):
 def test_preattn_block_full_size(T):
     """Residual add -> norm -> fused QKV -> per-head norm -> RoPE, K=4096, 32 + 8 + 8 heads of 128."""
     case = synthetic.preattn_block(T)
-    y1 = check_preattn_case(case, rows=sample_rows(T, 24))
+    y1 = check_preattn_case(case)
     y2 = run_preattn(case)[0]
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"
 
@@ -784,30 +814,35 @@ def test_preattn_block_full_size(T):
 # ---------------------------------------------------------------------------
 def run_mla(case):
     x, Wa, Wkv, gq, gkv, Wb = (dev(case[k]) for k in ("x", "W_a", "W_kv", "gamma", "gamma_ckv", "W_b"))
-    T, R = x.shape[0], Wa.shape[0]
+    T, R, Rkv = x.shape[0], Wa.shape[0], Wkv.shape[0]
     W_akv = torch.cat([Wa, Wkv], dim=0).contiguous()
     rq = torch.empty(T, dtype=torch.float32, device="cuda")
     rkv = torch.empty(T, dtype=torch.float32, device="cuda")
-    y, qr, kv = rnl.mla_prolog_bf16(x, W_akv, R, gq, gkv, EPS, Wb, rstd_q_out=rq, rstd_kv_out=rkv)
+    qakv = torch.empty((T, R + Rkv), dtype=torch.bfloat16, device="cuda")
+    y, qr, kv = rnl.mla_prolog_bf16(x, W_akv, R, gq, gkv, EPS, Wb, rstd_q_out=rq, rstd_kv_out=rkv, qakv_out=qakv)
     torch.cuda.synchronize()
-    return y.cpu(), qr.cpu(), kv.cpu(), rq.cpu().numpy(), rkv.cpu().numpy()
+    return y.cpu(), qr.cpu(), kv.cpu(), rq.cpu().numpy(), rkv.cpu().numpy(), qakv.cpu()
 
 
-def check_mla_case(case, rows=None):
-    y, qr, kv, rq, rkv = run_mla(case)
-    T = case["x"].shape[0]
-    rows = np.arange(T) if rows is None else rows
-    xb = bits(case["x"])[rows]
+def check_mla_case(case):
+    y, qr, kv, rq, rkv, qakv = run_mla(case)
+    R = case["W_a"].shape[0]
+    xb = bits(case["x"])
     gq = None if case["gamma"] is None else bits(case["gamma"])
     gkv = None if case["gamma_ckv"] is None else bits(case["gamma_ckv"])
+    # stage 1 ([q_a | kv], one pass over x): bf16 outputs of fp32 accumulations
+    sb = bits(qakv)
+    W_akv = np.concatenate([bits(case["W_a"]), bits(case["W_kv"])], axis=0)
+    assert_bf16_close(O.bf16_bits_to_f32(sb), O.project_bf16(O.bf16_bits_to_f32(xb), W_akv), case.name + " [q_a | kv]")
+    # both norms on the device's stage-1 rows
+    check_normed_stage(np.ascontiguousarray(sb[:, :R]), gq, rq, bits(qr), case.name + " qr")
+    check_normed_stage(np.ascontiguousarray(sb[:, R:]), gkv, rkv, bits(kv), case.name + " kv")
+    # stage 2 from the device's qr
+    assert_bf16_close(f32(y), O.project_bf16(O.bf16_bits_to_f32(bits(qr)), bits(case["W_b"])), case.name + " y")
+    # end to end against the oracle's own stage 1
     ref = O.mla_prolog(xb, bits(case["W_a"]), gq, EPS, bits(case["W_b"]), bits(case["W_kv"]), gkv)
-    for got, want, what in ((rq[rows], ref["rstd"], "rstd_q"), (rkv[rows], ref["rstd_kv"], "rstd_kv")):
-        rel = np.abs(got.astype(np.float64) / want - 1)
-        assert rel.max() < 1e-3, f"{case.name}: {what} rel err {rel.max():.3g}"
-    assert_bf16_close(f32(qr)[rows], O.bf16_bits_to_f32(ref["qr"]), case.name + " qr")
-    assert_bf16_close(f32(kv)[rows], O.bf16_bits_to_f32(ref["kv_out"]), case.name + " kv")
-    y_ref = O.project_bf16(O.bf16_bits_to_f32(bits(qr)[rows]), bits(case["W_b"]))
-    assert_bf16_close(f32(y)[rows], y_ref, case.name + " y")
+    assert_bf16_two_roundings(f32(qr), O.bf16_bits_to_f32(ref["qr"]), case.name + " qr end to end")
+    assert_bf16_two_roundings(f32(kv), O.bf16_bits_to_f32(ref["kv_out"]), case.name + " kv end to end")
     return y, kv
 
 
@@ -823,10 +858,10 @@ def test_mla_prolog_small(T, K, R, Rkv, N, gamma):
 
 
 def test_mla_prolog_full_size():
-    """Query chain + KV branch, T=1024, K=7168, R=1536, Rkv=512, N=24576, at full size."""
+    """Query chain + KV branch, T=1024, K=7168, R=1536, Rkv=512, N=24576, every row."""
     case = synthetic.mla_prolog()
-    y1, kv1 = check_mla_case(case, rows=sample_rows(1024, 12))
-    y2, _, kv2, _, _ = run_mla(case)
+    y1, kv1 = check_mla_case(case)
+    y2, _, kv2, _, _, _ = run_mla(case)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and torch.equal(kv1.view(torch.int16),
                                                                                    kv2.view(torch.int16))
 
@@ -935,6 +970,6 @@ def test_rmsnorm_linear_mxfp8_small(T, K, N, gamma):
 def test_mxfp8_qkv_full_size():
     """Pre-attention norm + fused QKV in MXFP8, T=4096, K=4096, N=6144, at full size."""
     case = synthetic.mxfp8_qkv()
-    y1 = check_mx_case(case, rows=sample_rows(4096, 24))
+    y1 = check_mx_case(case)
     y2, _, _, _ = run_mx(case, torch.bfloat16)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "not deterministic"

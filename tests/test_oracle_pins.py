@@ -313,6 +313,21 @@ def test_int8_gemm_brute_force_and_unit_rows():
     assert np.array_equal(O.int8_gemm(q, E), q[:, sel].astype(np.int64))
 
 
+def test_int8_gemm_fp64_form_is_exact():
+    """The fp64 evaluation equals the int64 sum, also at the extremes: every product +-127^2 or -128 * 127 over
+    K = 132096, the longest row for which 128 * 127 * K still fits int32 (all partial sums stay far below 2^53),
+    and random codes at K = 4096."""
+    K = 132096
+    for a, b in ((127, 127), (-127, 127), (-128, 127), (127, -128)):
+        q = np.full((2, K), a, dtype=np.int8)
+        Wq = np.full((3, K), b, dtype=np.int8)
+        assert np.array_equal(O.int8_gemm(q, Wq), O.int8_gemm_int64(q, Wq))
+        assert O.int8_gemm(q, Wq)[0, 0] == a * b * K
+    q = RNG.integers(-127, 128, (40, 4096)).astype(np.int8)
+    Wq = RNG.integers(-128, 128, (70, 4096)).astype(np.int8)
+    assert np.array_equal(O.int8_gemm(q, Wq), O.int8_gemm_int64(q, Wq))
+
+
 def test_int8_gemm_overflow_detected():
     K = 133160  # K * 127 * 127 > 2^31 - 1
     q = np.full((1, K), 127, dtype=np.int8)
