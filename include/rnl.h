@@ -105,6 +105,33 @@ RNL_API size_t rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t
                                            int out_dtype);
 
 /*
+ * rmsnorm_linear_bf16_noalloc -- rmsnorm_linear_bf16 for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ * Same arguments, results and errors as rmsnorm_linear_bf16, without the
+ * workspace: the kernels use a fixed scratch array that the library holds on
+ * each GPU it runs on (allocated with the library's code, on that GPU, and
+ * kept until the process ends).  The call itself allocates nothing.
+ *   - Sizes whose rmsnorm_linear_bf16_workspace_bytes() exceeds
+ *     rnl_noalloc_scratch_bytes() (32 MiB; e.g. T * K <= 16 Mi with bf16
+ *     weights) are rejected with RNL_ERR_WORKSPACE before any HIP call.
+ *   - Every call on one GPU uses that GPU's one scratch array: calls that may
+ *     overlap on a GPU (different streams without ordering, or several host
+ *     threads) race and must be serialised by the caller.  Calls in one
+ *     stream are ordered and safe.
+ *   - The scratch's device is the device of `stream` (the current device for
+ *     the NULL stream); its address is looked up once per device, with the
+ *     runtime's symbol lookup, on the first call there.
+ */
+RNL_API int rmsnorm_linear_bf16_noalloc(const void* x, const void* gamma, float eps, const void* W, int w_dtype,
+                                        void* y, int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N,
+                                        void* stream);
+
+/* Bytes of the scratch array behind rmsnorm_linear_bf16_noalloc (per GPU). */
+RNL_API size_t rnl_noalloc_scratch_bytes(void);
+
+/*
  * rmsnorm_linear_int8 -- fused RMSNorm -> per-token int8 quant -> int8 GEMM ->
  * dequant (AT-11 = AT-10 with AT-09's INT8 W8A8 mode).
  *

@@ -31,6 +31,8 @@ import torch
 
 __all__ = [
     "rmsnorm_linear_bf16",
+    "rmsnorm_linear_bf16_noalloc",
+    "noalloc_scratch_bytes",
     "rmsnorm_linear_int8",
     "add_rmsnorm_linear_bf16",
     "add_rmsnorm_linear_int8",
@@ -135,6 +137,11 @@ def load_library() -> ctypes.CDLL:
     lib.rms_norm_quant_mxfp8.restype = ctypes.c_int
     lib.linear_mxfp8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
     lib.linear_mxfp8.restype = ctypes.c_int
+    lib.rmsnorm_linear_bf16_noalloc.argtypes = [_c_p, _c_p, ctypes.c_float, _c_p, ctypes.c_int, _c_p, ctypes.c_int,
+                                                _c_p, _c_i64, _c_i64, _c_i64, _c_p]
+    lib.rmsnorm_linear_bf16_noalloc.restype = ctypes.c_int
+    lib.rnl_noalloc_scratch_bytes.argtypes = []
+    lib.rnl_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -257,6 +264,36 @@ def rmsnorm_linear_bf16(x, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=Non
     may be None.  ``rstd_out`` (fp32 [T]) receives the per-token rstd.
     """
     return _bf16_call(x, None, None, gamma, eps, W, out_dtype, rstd_out, y, workspace)
+
+
+def rmsnorm_linear_bf16_noalloc(x, gamma, eps, W, y, rstd_out=None):
+    """rmsnorm_linear_bf16 without a workspace: the library's own per-GPU scratch
+    array serves instead, so the call allocates nothing (``y`` [T, N], bf16 or
+    fp32, is required; its dtype selects the output type).  Sizes that need more
+    scratch than ``noalloc_scratch_bytes()`` raise.  Calls that overlap on one GPU
+    share that scratch and race."""
+    lib = load_library()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, 1)
+    _dev_tensor(W, "W", (torch.bfloat16, torch.float32), 2)
+    _dev_tensor(y, "y", (torch.bfloat16, torch.float32), 2)
+    _dev_tensor(rstd_out, "rstd_out", torch.float32)
+    T, K = x.shape
+    N = W.shape[0]
+    _shape(W.shape[1] == K, "W must be [N, K]")
+    _shape(gamma is None or gamma.numel() == K, "gamma must be [K]")
+    _shape(tuple(y.shape) == (T, N), "y must be [T, N]")
+    _shape(rstd_out is None or rstd_out.numel() >= T, "rstd_out must hold T values")
+    with torch.cuda.device(x.device):
+        rc = lib.rmsnorm_linear_bf16_noalloc(_ptr(x), _ptr(gamma), float(eps), _ptr(W), _DTYPE_CODE[W.dtype], _ptr(y),
+                                             _DTYPE_CODE[y.dtype], _ptr(rstd_out), T, K, N, _stream(x.device))
+    _check(rc)
+    return y
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the per-GPU scratch array behind rmsnorm_linear_bf16_noalloc."""
+    return int(load_library().rnl_noalloc_scratch_bytes())
 
 
 def add_rmsnorm_linear_bf16(x, residual, gamma, eps, W, out_dtype=torch.bfloat16, rstd_out=None, y=None,

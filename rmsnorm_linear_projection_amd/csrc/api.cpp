@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -233,9 +234,68 @@ bool partial_overlap(const void* a, const void* b, int64_t T, int64_t ld) {
   return pa < pb + n && pb < pa + n;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (rmsnorm_linear_bf16_noalloc).
+// The array lives in the library's code object: every GPU the library runs on
+// holds its own copy from the first use until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory, so it is never
+// passed to a kernel: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+// The kernels fully write every scratch byte they later read, so nothing in it
+// has to start at zero.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+__attribute__((used)) static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of this device's scratch for work on stream s (the stream's
+// device; the current device for the null stream).
+int scratch_for(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = s != nullptr ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RNL_ERR_ARG, "device %d outside the supported range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (e2 != hipSuccess) return hip_status(e2, "hipSetDevice");
+    if (p == nullptr) return fail(RNL_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return RNL_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t rnl_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int rmsnorm_linear_bf16_noalloc(const void* x, const void* gamma, float eps, const void* W, int w_dtype, void* y,
+                                int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N, void* stream) {
+  // the size check runs before any HIP call, like every other validation
+  if (x == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "x, W and y are required");
+  RNL_TRY(check_dims(T, K, N, kMaxK));
+  if (w_dtype != RNL_BF16 && w_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "w_dtype must be RNL_BF16 or RNL_FP32");
+  if (w_dtype == RNL_FP32 && N > kMaxN_fp32w) return fail(RNL_ERR_SHAPE, "fp32 weights need N <= 2^20");
+  const size_t need = bf16_ws(T, K, N, w_dtype);
+  if (need > kScratchBytes)
+    return fail(RNL_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; the allocation-free entry point has %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  RNL_TRY(scratch_for(static_cast<hipStream_t>(stream), &ws));
+  return bf16_path(x, nullptr, nullptr, gamma, eps, W, w_dtype, y, out_dtype, rstd_out, T, K, N, ws, kScratchBytes,
+                   stream);
+}
 
 const char* rnl_status_str(int status) {
   switch (status) {

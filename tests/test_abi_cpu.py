@@ -323,3 +323,15 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         rnl.rmsnorm_linear_bf16(x, None, 1e-6, torch.zeros(8, 64, dtype=torch.bfloat16))
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free entry point validates before any HIP call: sizes whose workspace exceeds the fixed
+    scratch are rejected, like the other argument errors."""
+    assert lib.rnl_noalloc_scratch_bytes() == 32 << 20
+    f = lib.rmsnorm_linear_bf16_noalloc
+    assert f(FAKE, NULL, 1e-6, FAKE, 1, FAKE, 1, NULL, 4097, 4096, 8, NULL) == E["RNL_ERR_WORKSPACE"]
+    assert f(FAKE, NULL, 1e-6, FAKE, 2, FAKE, 2, NULL, 300000, 28672, 24, NULL) == E["RNL_ERR_WORKSPACE"]
+    assert f(NULL, NULL, 1e-6, FAKE, 1, FAKE, 1, NULL, 4, 64, 8, NULL) == E["RNL_ERR_NULL"]
+    assert f(FAKE, NULL, 1e-6, FAKE, 3, FAKE, 1, NULL, 4, 64, 8, NULL) == E["RNL_ERR_DTYPE"]
+    assert f(FAKE, NULL, 1e-6, FAKE, 1, FAKE, 1, NULL, 4, 60, 8, NULL) == E["RNL_ERR_SHAPE"]
