@@ -321,7 +321,18 @@ class ClockSampler:
             self._amdsmi = None
 
     def _read(self):
+        """(sclk, mclk) in MHz: the SMU metrics table's current clocks (the median over the
+        XCDs' graphics clocks), else the driver's clock info."""
         a = self._amdsmi
+        try:
+            m = a.amdsmi_get_gpu_metrics_info(self._h)
+            g = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 65535]
+            u = m.get("current_uclk")
+            if g and isinstance(u, (int, float)):
+                g.sort()
+                return (g[len(g) // 2], float(u))
+        except Exception:  # no metrics table: fall back to the clock info
+            pass
         g = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.GFX)
         m = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.MEM)
         return (float(g["clk"]), float(m["clk"]))
@@ -413,8 +424,47 @@ def time_loop(fn, steps, warmup, graph=True, repeats=1, clocks=None):
     return statistics.median(runs), runs  # ms
 
 
-def cpu_baseline(setup, target_s=8.0):
-    """The oracle as it stands, on a bounded row sample of the same inputs."""
+def oracle_threads():
+    """Threads the oracle's row loops get: every CPU this process may run on, at most
+    16 (the host CPU share one GPU of the box gets)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def config1_single_thread_ms(reps=20):
+    """The C oracle on the small configuration (bf16, T=8, K=256, N=128, seed 0),
+    single-threaded: median ms of `reps` whole calls (norm + bf16 projection)."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import oracle as O
+    import synthetic
+
+    case = synthetic.small_norm_linear(seed=0)
+
+    def bits(x):
+        return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    x, g, W = bits(case["x"]), bits(case["gamma"]), bits(case["W"])
+    prev = O.threads()
+    O.set_threads(1)
+    try:
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            O.rmsnorm_linear_bf16(x, g, case.eps, W)
+            times.append((time.perf_counter() - t0) * 1e3)
+    finally:
+        O.set_threads(prev)
+    return round(statistics.median(times), 4)
+
+
+def cpu_baseline(setup, target_s=10.0):
+    """The C oracle as it stands (plain loops, double accumulation, rows split over
+    threads), on a bounded row sample of the same inputs, plus the small
+    configuration single-threaded in ms."""
     import numpy as np
     import torch
 
@@ -427,6 +477,8 @@ def cpu_baseline(setup, target_s=8.0):
 
     kind = w["kind"]
     T = w["T"]
+    nthreads = oracle_threads()
+    O.set_threads(nthreads)
 
     def run(rows):
         x = bits(c["x"][:rows])
@@ -472,14 +524,12 @@ def cpu_baseline(setup, target_s=8.0):
         value, unit = bytes_of(sub) / per_call / 1e9, "GB/s"
     else:
         value, unit = flops_of(sub) / per_call / 1e12, "TOP/s" if kind == "int8" else "TFLOP/s"
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: BLAS thread count unknown
-        cores = None
-    return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"first {rows} of {T} token rows, {calls} call(s), {per_call:.3f} s per call"}
+    return {"value": round(value, 6), "unit": unit, "cores": nthreads, "kind": "oracle",
+            "sample": f"first {rows} of {T} token rows, {calls} call(s), {per_call:.3f} s per call",
+            "impl": "C (oracle/c/rnl_oracle.c): plain loops, double accumulation, gcc -O2 -ffp-contract=off",
+            "host_cpus": {"nproc": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+                          "online": O.cpu_count()},
+            "config1_single_thread_ms": config1_single_thread_ms()}
 
 
 def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False, repeats=1):

@@ -4,14 +4,19 @@ TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the entry
 script and the ``cpu_baseline`` leg of the benchmark may import this package.
 The product path never calls it and never falls back to it.
 
-Plain numpy, slow and obviously correct; it shares no code with the HIP path.
-See ``oracle/rmsnorm_linear.py`` for the definitions and their citations.
+The oracle is plain C (``oracle/c/rnl_oracle.c``, loops with double
+accumulation, built by ``oracle/build_oracle.py``), reached through the
+functions below (``oracle/c_oracle.py``).  ``oracle.numpy_ref`` is a second,
+independent implementation of the same definitions in numpy, kept as a
+cross-check: every pin runs against both.  Neither shares code with the HIP
+path.
 """
-from .rmsnorm_linear import (  # noqa: F401
+from . import rmsnorm_linear as numpy_ref  # noqa: F401
+from . import c_oracle as c  # noqa: F401
+from .c_oracle import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     rms_norm_rows,
-    rstd_variant_a,
     rms_norm_rows_mla_order,
     rms_norm_rows_golden_div,
     project_bf16,
@@ -39,4 +44,7 @@ from .rmsnorm_linear import (  # noqa: F401
     mx_quant_rows,
     mx_scaled_mm,
     rmsnorm_linear_mxfp8,
+    set_threads,
+    threads,
+    cpu_count,
 )

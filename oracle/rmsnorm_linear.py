@@ -1,4 +1,6 @@
-"""Plain numpy oracle for the fused RMSNorm -> Linear projection.
+"""numpy reference of the fused RMSNorm -> Linear projection: the same
+definitions as the C oracle (oracle/c/rnl_oracle.c), written independently in
+numpy and kept as its cross-check; every pin runs against both.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
 ``cpu_baseline`` leg of the benchmark; never by the product path.
@@ -430,7 +432,8 @@ def preattn_qkv(x_bits, r_bits, gamma_bits, eps, W_bits, Hq, Hkv, D, gq_bits, gk
     V as projected.
 
     Returns a dict: x_add (bits or None), y_proj (bf16 bits of the projection),
-    y (bf16 bits after the head stage), rstd [T], head_rstd [T, Hq + Hkv].
+    y32 (the projection in fp32), y (bf16 bits after the head stage), rstd [T],
+    head_rstd [T, Hq + Hkv].
     ``rstd`` / ``head_rstd`` replace the computed values when given (the
     device's own), so that downstream values can be compared bit for bit.
     """
@@ -438,11 +441,12 @@ def preattn_qkv(x_bits, r_bits, gamma_bits, eps, W_bits, Hq, Hkv, D, gq_bits, gk
     if r_bits is not None:
         xa = add_residual(x_bits, r_bits)
         x_bits = xa
-    _, yb, rstd = rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd)
+    y32, yb, rstd = rmsnorm_linear_bf16(x_bits, gamma_bits, eps, W_bits, rstd)
     hr = None if head_rstd is None else np.asarray(head_rstd, dtype=F32)
     y, rq = head_rms_norm(yb, 0, Hq, D, gq_bits, head_eps, cos, sin, None if hr is None else hr[:, :Hq])
     y, rk = head_rms_norm(y, Hq * D, Hkv, D, gk_bits, head_eps, cos, sin, None if hr is None else hr[:, Hq:])
-    return {"x_add": xa, "y_proj": yb, "y": y, "rstd": rstd, "head_rstd": np.concatenate([rq, rk], axis=1)}
+    return {"x_add": xa, "y_proj": yb, "y32": y32, "y": y, "rstd": rstd,
+            "head_rstd": np.concatenate([rq, rk], axis=1)}
 
 
 # ----------------------------------------------------------------------------
