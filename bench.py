@@ -109,10 +109,13 @@ def src_sha(names):
 
 
 def fused_small_norm(w):
-    """True when the library norms the rows inside the weight-streaming kernel:
-    at most 4 rows, no residual, normed rows within 64 KiB."""
+    """True when the library norms the rows inside the weight-streaming kernel (no
+    residual): normed rows within 64 KiB, and at most 4 rows, or 5 to 16 rows of
+    at most 4096 values."""
     T, K = w["T"], w["K"]
-    return w["kind"] == "bf16" and not w.get("add") and T <= 4 and T * ((K + 31) // 32) * 64 <= 64 * 1024
+    if w["kind"] != "bf16" or w.get("add"):
+        return False
+    return T * ((K + 31) // 32) * 64 <= 64 * 1024 and (T <= 4 or (T <= 16 and K <= 4096))
 
 
 def row_gemv(w):
@@ -671,6 +674,46 @@ def record_counters(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(data["workloads"][name]))
 
 
+CEILING_SIZES = [(512 * 28672 * 2, "x of the skinny fp32 workload (29 MiB)"),
+                 (6144 * 4096 * 2, "the decode QKV weight (48 MiB)"),
+                 (256 << 20, "256 MiB"), (1 << 30, "1 GiB"), (4 << 30, "4 GiB")]
+
+
+CEILING_SHAPES = [(256, 8), (256, 16), (512, 4), (512, 8), (512, 16), (768, 16), (1024, 4), (1024, 8), (1024, 16),
+                  (2048, 4), (2048, 8)]
+
+
+def hbm_ceiling(steps, warmup, repeats):
+    """HBM read ceiling: the library's read-only streaming probe (rnl_stream_read) on
+    buffers of the sizes above, rotated over enough copies (>= 640 MB in all) that
+    the 256 MB Infinity Cache cannot serve a read from the previous one; one JSON
+    line per size."""
+    import torch
+
+    import rmsnorm_linear_projection_amd as rnl
+
+    for nbytes, what in CEILING_SIZES:
+        copies = max(1, math.ceil(640e6 / nbytes))
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0") for _ in range(copies)]
+        sink = torch.empty(max(w for w, _ in CEILING_SHAPES), dtype=torch.int32, device="cuda:0")
+        shapes = {}
+        for wgs, unroll in CEILING_SHAPES:
+            ms, _ = time_loop(lambda i: rnl.stream_read(bufs[i % copies], wgs, unroll, sink), steps, warmup, True,
+                              repeats)
+            shapes[f"{wgs}x{unroll}"] = round(ms * 1e3, 3)
+        best = min(shapes, key=shapes.get)
+        us = shapes[best]
+        print(json.dumps({"probe": "rnl_stream_read (read-only HBM stream)", "buffer": what, "bytes": nbytes,
+                          "copies": copies, "best_shape": best, "us_per_read": us,
+                          "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "frac_of_8000_GB/s": round(nbytes / (us * 1e-6) / 1e9 / PEAK["hbm"], 4),
+                          "us_by_shape (workgroups x loads in flight per lane)": shapes,
+                          "timing": f"hip graph of {steps} reads, median of {repeats} runs, {warmup} untimed"}),
+              flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -684,6 +727,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured graph")
     ap.add_argument("--vendor", action="store_true",
                     help="also time the vendor library (torch.matmul / torch._int_mm) on the dominant kernel's operands")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="measure only the read-only HBM streaming ceiling at several buffer sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the plain copy that calibrates the HBM byte counters")
     ap.add_argument("--record-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -703,6 +748,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling(args.steps, args.warmup, args.repeats)
         return
     import rmsnorm_linear_projection_amd as rnl
 

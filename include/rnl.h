@@ -37,7 +37,9 @@
  *     whole weight rows and multiplies on the vector units), larger ones the
  *     tiled GEMM.  Environment variable RNL_VARIANT
  *     (read at every call) set to "gemm" forces the tiled GEMM for any size,
- *     for testing; anything else, or unset, lets the shape decide.
+ *     "prepass" forces the separate norm pre-pass (no norm fused into the
+ *     weight-streaming kernels), for testing; anything else, or unset, lets
+ *     the shape decide.
  */
 #ifndef RNL_H
 #define RNL_H
@@ -396,6 +398,20 @@ RNL_API int rms_norm_quant_mxfp8(const void* x, const void* gamma, float eps, ui
  */
 RNL_API int linear_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const uint8_t* Wq, const uint8_t* w_scale,
                          void* y, int out_dtype, int64_t M, int64_t K, int64_t N, void* stream);
+
+/*
+ * rnl_stream_read -- HBM streaming probe; not a step of the method.  Reads
+ * `bytes` (a positive multiple of 16) of device memory at src once with
+ * `workgroups` workgroups (1 to 65536) of 256 threads: 16-byte loads, 1 KiB
+ * contiguous per wavefront load instruction, `unroll` (1, 2, 4, 8 or 16) loads
+ * in flight per lane, grid-stride.  Each workgroup writes one word, a fold of
+ * what it read, to sink[workgroup] (so the reads cannot be elided).  Its
+ * duration gives the practical read bandwidth that the weight-bound paths are
+ * compared with.
+ * Errors: RNL_ERR_NULL, RNL_ERR_SHAPE (bytes, workgroups), RNL_ERR_ARG
+ * (unroll), RNL_ERR_ALIGN (src 16-byte, sink 4-byte), RNL_ERR_HIP.
+ */
+RNL_API int rnl_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll, void* stream);
 
 /* Static description of a status code. */
 RNL_API const char* rnl_status_str(int status);

@@ -33,6 +33,7 @@ __all__ = [
     "rmsnorm_linear_bf16",
     "rmsnorm_linear_bf16_noalloc",
     "noalloc_scratch_bytes",
+    "stream_read",
     "rmsnorm_linear_int8",
     "add_rmsnorm_linear_bf16",
     "add_rmsnorm_linear_int8",
@@ -142,6 +143,8 @@ def load_library() -> ctypes.CDLL:
     lib.rmsnorm_linear_bf16_noalloc.restype = ctypes.c_int
     lib.rnl_noalloc_scratch_bytes.argtypes = []
     lib.rnl_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.rnl_stream_read.argtypes = [_c_p, ctypes.c_size_t, _c_p, ctypes.c_int, ctypes.c_int, _c_p]
+    lib.rnl_stream_read.restype = ctypes.c_int
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -289,6 +292,24 @@ def rmsnorm_linear_bf16_noalloc(x, gamma, eps, W, y, rstd_out=None):
                                              _DTYPE_CODE[y.dtype], _ptr(rstd_out), T, K, N, _stream(x.device))
     _check(rc)
     return y
+
+
+def stream_read(src, workgroups=1024, unroll=8, sink=None):
+    """HBM streaming probe (not a step of the method): one read of every byte of
+    the device tensor ``src`` (size a multiple of 16 bytes) by ``workgroups``
+    workgroups with ``unroll`` loads in flight per lane; returns the int32 sink
+    (one word per workgroup) it folds the data into."""
+    lib = load_library()
+    _dev_tensor(src, "src")
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=src.device)
+    _dev_tensor(sink, "sink", torch.int32)
+    _shape(sink.numel() >= workgroups, "sink must hold one word per workgroup")
+    with torch.cuda.device(src.device):
+        rc = lib.rnl_stream_read(_ptr(src), nbytes, _ptr(sink), int(workgroups), int(unroll), _stream(src.device))
+    _check(rc)
+    return sink
 
 
 def noalloc_scratch_bytes() -> int:

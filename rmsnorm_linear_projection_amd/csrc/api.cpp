@@ -42,17 +42,17 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 
 constexpr int64_t kMaxHeads = (int64_t(1) << 31) - 1;  // T * heads: the per-head kernel divides in 32 bits
 constexpr int64_t kMaxN_fp32w = int64_t(1) << 20;  // fp32 weights: column blocks of 32 fit one grid axis
 constexpr int64_t kSmallM = 16;  // at most this many activation rows: weight-streaming kernel
-constexpr int64_t kFusedNormM = 4;  // at most this many (and no residual): the norm runs inside it
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-enum Variant { V_AUTO, V_GEMM };
+enum Variant { V_AUTO, V_GEMM, V_PREPASS };
 
 Variant forced_variant() {
   const char* v = std::getenv("RNL_VARIANT");
   if (v != nullptr && std::strcmp(v, "gemm") == 0) return V_GEMM;
+  if (v != nullptr && std::strcmp(v, "prepass") == 0) return V_PREPASS;
   return V_AUTO;
 }
 
@@ -157,12 +157,13 @@ int bf16_path(const void* x, const void* residual, void* x_add, const void* gamm
                       "skinny split-K launch");
   }
   const uint16_t* wb = static_cast<const uint16_t*>(W);
-  // one token: each wavefront norms the row and streams whole weight rows
-  if (rb == nullptr && use_small_m(T) && rnl::row_gemv_fits(T, K))
+  // one or two tokens: the workgroup norms the rows once and each wavefront streams whole weight rows
+  const bool fuse_ok = rb == nullptr && forced_variant() != V_PREPASS;
+  if (fuse_ok && use_small_m(T) && rnl::row_gemv_fits(T, K))
     return hip_status(rnl::launch_row_gemv_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
-                      "single-token norm + projection launch");
+                      "whole-row norm + projection launch (one or two tokens)");
   // a few tokens whose normed rows fit LDS: the norm runs inside the weight-streaming kernel
-  if (rb == nullptr && T <= kFusedNormM && use_small_m(T) && rnl::small_m_norm_lds(T, K) <= rnl::kSmallNormLds)
+  if (fuse_ok && use_small_m(T) && rnl::small_m_norm_fits(T, K))
     return hip_status(rnl::launch_small_m_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
                       "fused norm + projection launch");
   uint16_t* a = static_cast<uint16_t*>(workspace);
@@ -312,6 +313,18 @@ const char* rnl_status_str(int status) {
 }
 
 const char* rnl_last_error(void) { return g_last_error; }
+
+int rnl_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll, void* stream) {
+  if (src == nullptr || sink == nullptr) return fail(RNL_ERR_NULL, "src and sink are required");
+  if (bytes == 0 || bytes % 16 != 0) return fail(RNL_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (workgroups < 1 || workgroups > 65536) return fail(RNL_ERR_SHAPE, "workgroups must be in [1, 65536]");
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
+    return fail(RNL_ERR_ARG, "unroll must be 1, 2, 4, 8 or 16");
+  RNL_ALIGN(src, 16, "src");
+  RNL_ALIGN(sink, 4, "sink");
+  return hip_status(rnl::launch_stream_read(src, bytes, sink, workgroups, unroll, static_cast<hipStream_t>(stream)),
+                    "stream probe launch");
+}
 
 size_t rmsnorm_linear_bf16_workspace_bytes(int64_t T, int64_t K, int64_t N, int w_dtype,
                                            int out_dtype) {

@@ -90,6 +90,15 @@ int small_m_rows(int64_t N);
 // LDS: small_m_norm_lds(M, K) bytes, which must not exceed kSmallNormLds.
 constexpr size_t kSmallNormLds = 64 * 1024;
 size_t small_m_norm_lds(int64_t M, int64_t K);
+// Two prologues, both for normed rows within kSmallNormLds: up to
+// kFusedNormRowsM rows normed one at a time, or kFusedNormRowsM < M <=
+// kFusedNormAllM rows of at most kFusedNormAllK values, every row requested at
+// once.  small_m_norm_fits tells whether either applies.
+constexpr int64_t kFusedNormRowsM = 4;
+constexpr int64_t kFusedNormAllM = 16;
+constexpr int64_t kFusedNormAllK = 4096;
+constexpr size_t kSmallNormLdsAllRows = kSmallNormLds;
+bool small_m_norm_fits(int64_t M, int64_t K);
 hipError_t launch_small_m_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
                                     void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
                                     hipStream_t s);
@@ -116,5 +125,11 @@ size_t skinny_workspace_bytes(int64_t T, int64_t K, int64_t N);
 hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float eps, const float* W,
                                void* y, int out_kind, float* rstd_out, int64_t T, int64_t K,
                                int64_t N, void* workspace, hipStream_t s);
+
+// Read-only streaming probe (not a step of the method): `workgroups` workgroups of
+// 256 threads read `bytes` (a multiple of 16) from src once, `unroll` (1, 2, 4, 8
+// or 16) loads in flight per thread; sink receives one word per workgroup.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll,
+                              hipStream_t s);
 
 }  // namespace rnl

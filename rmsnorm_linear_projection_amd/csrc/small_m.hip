@@ -144,7 +144,12 @@ __global__ __launch_bounds__(NW * 64) void small_m_kernel(const uint16_t* __rest
 // MFMA output column is never stored, and columns of an MFMA do not mix.
 // LDS: M * ceil(K / 32) * 64 bytes (k-steps past K hold zeros), reused for
 // the cross-wave sum at the end.
-template <int NB, int NW, int KU, bool OUT_BF16, bool GAMMA>
+//
+// RPW > 0 selects the prologue for up to NW * RPW rows of at most 64 * CPL
+// chunks: wavefront w norms rows w, w + NW, ... and requests every chunk of all
+// of them (and gamma's) at once, so the norm costs one L2 round trip instead
+// of one per row; the weight batches are issued right after those requests.
+template <int NB, int NW, int KU, bool OUT_BF16, bool GAMMA, int RPW = 0, int CPL = 8>
 __global__ __launch_bounds__(NW * 64) void small_m_norm_kernel(const uint16_t* __restrict__ X,
                                                                const uint16_t* __restrict__ gamma, float eps,
                                                                float inv_k, const uint16_t* __restrict__ W,
@@ -212,12 +217,67 @@ __global__ __launch_bounds__(NW * 64) void small_m_norm_kernel(const uint16_t* _
       }
     }
   };
+  // n = fl(fl(x * rstd) * gamma) of one chunk, rounded to bf16, stored at its
+  // k-step-major place (zeros past K, up to the next whole k-step)
+  auto store_normed = [&](int t, int idx, u32x4 xv, u32x4 gvv, float rstd) {
+    float n[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      n[2 * j] = __fmul_rn(bf16lo(xv[j]), rstd);
+      n[2 * j + 1] = __fmul_rn(bf16hi(xv[j]), rstd);
+      if constexpr (GAMMA) {
+        n[2 * j] = __fmul_rn(n[2 * j], bf16lo(gvv[j]));
+        n[2 * j + 1] = __fmul_rn(n[2 * j + 1], bf16hi(gvv[j]));
+      }
+    }
+    const u32x4 q = idx < nch ? u32x4{pack_bf16x2(n[0], n[1]), pack_bf16x2(n[2], n[3]), pack_bf16x2(n[4], n[5]),
+                                      pack_bf16x2(n[6], n[7])}
+                              : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(xs + ((uint32_t)((idx >> 2) * M + t) * 64u + (uint32_t)(idx & 3) * 16u)) = q;
+  };
+  Batch cur, alt;
+  if constexpr (RPW > 0) {
+    u32x4 rv[RPW][CPL], rg[CPL];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int t = wave + NW * j;
+      const u32x4* xr = reinterpret_cast<const u32x4*>(X + (size_t)min(t, M - 1) * K);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int idx = lane + kWave * c;
+        rv[j][c] = (t < M && idx < nch) ? xr[idx] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + kWave * c;
+      rg[c] = (GAMMA && idx < nch) ? gr[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(cur, s_beg);
+    issue_w(alt, s_beg + KU);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int t = wave + NW * j;
+      if (t >= M) break;  // wavefront-uniform
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ss += sumsq8(rv[j][c]);
+      const float rstd = rstd_from_sumsq(wave_sum(ss), inv_k, eps);
+      if (blockIdx.x == 0 && lane == 0 && rstd_out != nullptr) rstd_out[t] = rstd;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int idx = lane + kWave * c;
+        if (idx < nch_pad) store_normed(t, idx, rv[j][c], rg[c], rstd);
+      }
+    }
+  } else {
   if (wave < M) {
     load_x(wave, 0);
     load_g(0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  Batch cur, alt;
   issue_w(cur, s_beg);
   issue_w(alt, s_beg + KU);
   __builtin_amdgcn_sched_barrier(0);
@@ -240,25 +300,10 @@ __global__ __launch_bounds__(NW * 64) void small_m_norm_kernel(const uint16_t* _
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int idx = c0 + lane + kWave * c;
-        if (idx < nch_pad) {
-          // n = fl(fl(x * rstd) * gamma), rounded to bf16 (zeros past K)
-          float n[8];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            n[2 * j] = __fmul_rn(bf16lo(v[c][j]), rstd);
-            n[2 * j + 1] = __fmul_rn(bf16hi(v[c][j]), rstd);
-            if constexpr (GAMMA) {
-              n[2 * j] = __fmul_rn(n[2 * j], bf16lo(gv[c][j]));
-              n[2 * j + 1] = __fmul_rn(n[2 * j + 1], bf16hi(gv[c][j]));
-            }
-          }
-          const u32x4 q = idx < nch ? u32x4{pack_bf16x2(n[0], n[1]), pack_bf16x2(n[2], n[3]),
-                                            pack_bf16x2(n[4], n[5]), pack_bf16x2(n[6], n[7])}
-                                    : u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(xs + ((uint32_t)((idx >> 2) * M + t) * 64u + (uint32_t)(idx & 3) * 16u)) = q;
-        }
+        if (idx < nch_pad) store_normed(t, idx, v[c], gv[c], rstd);
       }
     }
+  }
   }
   __syncthreads();
   read_a(cur, s_beg);
@@ -375,15 +420,76 @@ size_t small_m_norm_lds(int64_t M, int64_t K) {
   return rows > red ? rows : red;
 }
 
+namespace {
+// Launch of the prologue that requests every row at once (RPW = 4 rows per
+// wavefront, rows of at most 512 * CPL values): NB = 2 row blocks per
+// workgroup, so that one workgroup per CU covers N = 6144 in one round (the
+// normed rows take up to 128 KiB of LDS, one workgroup per CU).
+template <int NB, bool O, bool G, int CPL>
+hipError_t launch_all_rows(const uint16_t* X, const uint16_t* gamma, float eps, float inv_k, const uint16_t* W,
+                           void* C, float* rstd_out, int M, int K, int N, int R, size_t lds, hipStream_t s) {
+  auto kern = small_m_norm_kernel<NB, 4, 4, O, G, 4, CPL>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kSmallNormLdsAllRows);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((N + R - 1) / R)), dim3(256), lds, s, X, gamma, eps, inv_k, W, C, rstd_out,
+                     M, K, N, R);
+  return hipGetLastError();
+}
+
+template <int NB, bool O, bool G>
+hipError_t launch_all_rows_cpl(int cpl, const uint16_t* X, const uint16_t* gamma, float eps, float inv_k,
+                               const uint16_t* W, void* C, float* rstd_out, int M, int K, int N, int R, size_t lds,
+                               hipStream_t s) {
+  switch (cpl) {
+    case 1: return launch_all_rows<NB, O, G, 1>(X, gamma, eps, inv_k, W, C, rstd_out, M, K, N, R, lds, s);
+    case 2: return launch_all_rows<NB, O, G, 2>(X, gamma, eps, inv_k, W, C, rstd_out, M, K, N, R, lds, s);
+    case 4: return launch_all_rows<NB, O, G, 4>(X, gamma, eps, inv_k, W, C, rstd_out, M, K, N, R, lds, s);
+    default: return launch_all_rows<NB, O, G, 8>(X, gamma, eps, inv_k, W, C, rstd_out, M, K, N, R, lds, s);
+  }
+}
+}  // namespace
+
+// Where fusing pays (graph-timed A/B against pre-pass + weight streaming, rotated
+// weights, us): T = 8, K = 1024, N = 4096: 4.5 against 6.6; T = 16, K = 1024: 5.4
+// against 6.9; T = 8, K = 2048, N = 6144: 9.0 against 10.3; T = 16, K = 2048:
+// 10.7 against 11.0; T = 8, K = 256, N = 128: 3.3 against 4.1; T = 8, K = 4096,
+// N = 6144: 14.6 against 14.9.  Past 64 KiB of normed rows it loses (T = 12, K =
+// 4096: 15.8 against 15.5; T = 16, K = 4096: 17.2 against 16.1): one workgroup
+// per CU cannot overlap a 16-row prologue with the weight stream.
+bool small_m_norm_fits(int64_t M, int64_t K) {
+  if (M < 1 || M > kFusedNormAllM || small_m_norm_lds(M, K) > kSmallNormLds) return false;
+  return M <= kFusedNormRowsM || K <= kFusedNormAllK;
+}
+
 hipError_t launch_small_m_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
                                     void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
                                     hipStream_t s) {
+  if (!small_m_norm_fits(M, K)) return hipErrorInvalidValue;
+  if (M > kFusedNormRowsM) {
+    const int R = small_m_rows(N);
+    const int64_t nch = K / 8;
+    const int cpl = nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8;
+    const size_t lds = small_m_norm_lds(M, K);
+    const float ik = 1.0f / (float)K;
+    const bool ob = out_kind == OUT_BF16, g = gamma != nullptr;
+#define RNL_ALL_ROWS(NB, O, G) \
+  return launch_all_rows_cpl<NB, O, G>(cpl, X, gamma, eps, ik, W, C, rstd_out, (int)M, (int)K, (int)N, R, lds, s)
+    if (R <= 16) {
+      if (ob) { if (g) RNL_ALL_ROWS(1, true, true); else RNL_ALL_ROWS(1, true, false); }
+      else { if (g) RNL_ALL_ROWS(1, false, true); else RNL_ALL_ROWS(1, false, false); }
+    } else {
+      if (ob) { if (g) RNL_ALL_ROWS(2, true, true); else RNL_ALL_ROWS(2, true, false); }
+      else { if (g) RNL_ALL_ROWS(2, false, true); else RNL_ALL_ROWS(2, false, false); }
+    }
+#undef RNL_ALL_ROWS
+  }
   const int R = small_m_norm_rows(N);
   dim3 grid((unsigned)((N + R - 1) / R)), block(256);
   const bool ob = out_kind == OUT_BF16;
   const float inv_k = 1.0f / (float)K;
   const size_t lds = small_m_norm_lds(M, K);
-  if (M < 1 || M > 16 || lds > kSmallNormLds) return hipErrorInvalidValue;
 #define RNL_SMALL_MN(NB, O, G)                                                                                 \
   hipLaunchKernelGGL((small_m_norm_kernel<NB, 4, 4, O, G>), grid, block, lds, s, X, gamma, eps, inv_k, W, C, \
                      rstd_out, (int)M, (int)K, (int)N, R)

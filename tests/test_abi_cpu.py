@@ -335,3 +335,12 @@ def test_noalloc_validation(lib):
     assert f(NULL, NULL, 1e-6, FAKE, 1, FAKE, 1, NULL, 4, 64, 8, NULL) == E["RNL_ERR_NULL"]
     assert f(FAKE, NULL, 1e-6, FAKE, 3, FAKE, 1, NULL, 4, 64, 8, NULL) == E["RNL_ERR_DTYPE"]
     assert f(FAKE, NULL, 1e-6, FAKE, 1, FAKE, 1, NULL, 4, 60, 8, NULL) == E["RNL_ERR_SHAPE"]
+
+
+def test_stream_probe_validation(lib):
+    assert lib.rnl_stream_read(NULL, 64, FAKE, 8, 4, NULL) == E["RNL_ERR_NULL"]
+    assert lib.rnl_stream_read(FAKE, 0, FAKE, 8, 4, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_stream_read(FAKE, 24, FAKE, 8, 4, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_stream_read(FAKE, 64, FAKE, 0, 4, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_stream_read(FAKE, 64, FAKE, 8, 3, NULL) == E["RNL_ERR_ARG"]
+    assert lib.rnl_stream_read(ODD, 64, FAKE, 8, 4, NULL) == E["RNL_ERR_ALIGN"]

@@ -4,6 +4,7 @@ Between replays the outputs are overwritten by eager work and the device is
 synchronised, so a replay that skipped or reordered work would show."""
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -128,3 +129,17 @@ def test_graph_mxfp8():
     check_replays(lambda: rnl.rmsnorm_linear_mxfp8(t["x"], t["gamma"], EPS, t["Wq"], t["w_scale"],
                                                    out_dtype=torch.float32, y=y, xq_out=xq, x_scale_out=xs),
                   [y, xq, xs])
+
+
+@pytest.mark.parametrize("nbytes,workgroups,unroll", [(16, 1, 1), (4096 + 16, 3, 4), (48 << 20, 1024, 8),
+                                                      (29 << 20, 2048, 16)])
+def test_stream_probe_reads_every_word_once(nbytes, workgroups, unroll):
+    """The HBM streaming probe folds every 32-bit word of the buffer exactly once: the XOR of its sink words is
+    the XOR of the buffer's words (a word read twice or skipped would change it)."""
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    sink = rnl.stream_read(host.cuda(), workgroups, unroll)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    assert got == want

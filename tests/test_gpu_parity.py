@@ -127,7 +127,7 @@ BF16_SMALL = [
     (2, 12296, 100),  # the same with two rows and a K tail
     (4, 8192, 200),  # four normed rows filling the 64 KiB LDS budget exactly
     (4, 64, 9),  # two k-steps: two of the four wavefronts have no part of K
-    (8, 4096, 200),  # more rows than the fused norm takes: pre-pass
+    (8, 4096, 200),  # eight rows of 4096: 64 KiB of normed rows, the fused norm's largest
     # one token: whole weight rows per wavefront, each K bucket of the chunk count
     (1, 8, 1),
     (1, 512, 2049),  # one chunk per lane, two rows per wavefront, the last wavefront one row
@@ -142,6 +142,20 @@ BF16_SMALL = [
     (6, 512, 5000),
     (8, 1024, 2049),
     (7, 1032, 77),  # K tail
+    # two tokens in the whole-row kernel: a K tail, a ragged last wavefront with several rows each
+    (2, 520, 300),
+    (2, 4104, 333),
+    (2, 2048, 30001),
+    # 5..16 tokens with the norm fused (every row requested at once, normed rows within 64 KiB): the
+    # smallest K and 1, 2, 4 and 8 chunks per lane (the last with a K tail)
+    (5, 8, 3),
+    (10, 1024, 6144),
+    (16, 2048, 300),
+    (12, 2056, 777),
+    # past 64 KiB of normed rows: pre-pass + weight streaming
+    (13, 4096, 1),
+    (16, 4088, 100),
+    (16, 4104, 40),
 ]
 
 
@@ -153,7 +167,7 @@ def test_bf16_small(T, K, N, gamma, force, variant):
     check_bf16_case(synthetic.norm_linear_case(T, K, N, seed=T + K + N, gamma=gamma))
 
 
-@pytest.mark.parametrize("T,K,N", [(8, 256, 128), (300, 1032, 200), (1, 64, 7)])
+@pytest.mark.parametrize("T,K,N", [(8, 256, 128), (300, 1032, 200), (1, 64, 7), (2, 520, 300), (16, 4096, 200)])
 def test_bf16_fp32_output(T, K, N):
     check_bf16_case(synthetic.norm_linear_case(T, K, N, seed=5), out_dtype=torch.float32)
 
@@ -785,6 +799,8 @@ def check_preattn_case(case, rows=None):
 @pytest.mark.parametrize("T,K,Hq,Hkv,D,residual,rope,head_gamma", [
     (8, 256, 4, 2, 64, False, True, True),
     (8, 256, 4, 2, 64, True, False, False),
+    (2, 256, 4, 2, 64, False, True, True),     # two tokens: the whole-row kernel
+    (16, 512, 4, 2, 64, False, True, True),    # sixteen tokens: the norm fused into the weight streaming
     (40, 1032, 6, 1, 128, True, True, True),   # tiled GEMM, ragged tiles
     (3, 64, 2, 0, 16, False, True, False),     # no key / value heads
     (20, 512, 3, 3, 192, False, True, True),
