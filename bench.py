@@ -307,75 +307,57 @@ class Setup:
         torch.cuda.synchronize()
 
 
-class ClockSampler:
-    """Samples the graphics (sclk) and memory (mclk) clocks of GPU 0 through amdsmi
-    in a background thread while the timed work runs.  summary() is None when
-    amdsmi is not available or reports nothing."""
+def smu_mclk():
+    """The memory clock (MHz) as the SMU's metrics table reports it (amdsmi), or None."""
+    try:
+        import amdsmi
 
-    def __init__(self, period_s=0.0002):
-        self.period, self.samples, self._stop, self._thread, self._h = period_s, [], False, None, None
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            self._amdsmi, self._h = amdsmi, (handles[0] if handles else None)
-        except Exception:  # no amdsmi, or no permission: clocks stay unrecorded
-            self._amdsmi = None
-
-    def _read(self):
-        """(sclk, mclk) in MHz: the SMU metrics table's current clocks (the median over the
-        XCDs' graphics clocks), else the driver's clock info."""
-        a = self._amdsmi
-        try:
-            m = a.amdsmi_get_gpu_metrics_info(self._h)
-            g = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 65535]
-            u = m.get("current_uclk")
-            if g and isinstance(u, (int, float)):
-                g.sort()
-                return (g[len(g) // 2], float(u))
-        except Exception:  # no metrics table: fall back to the clock info
-            pass
-        g = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.GFX)
-        m = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.MEM)
-        return (float(g["clk"]), float(m["clk"]))
-
-    def _run(self):
-        while not self._stop:
-            try:
-                self.samples.append(self._read())
-            except Exception:
-                return
-            time.sleep(self.period)
-
-    def __enter__(self):
-        if self._h is not None:
-            import threading
-
-            self._stop = False
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        if self._thread is not None:
-            self._stop = True
-            self._thread.join()
-        return False
-
-    def summary(self):
-        if not self.samples:
-            return None
-        import statistics
-
-        sc = [a for a, _ in self.samples]
-        mc = [b for _, b in self.samples]
-        return {"sclk_mhz": {"min": min(sc), "median": statistics.median(sc), "max": max(sc)},
-                "mclk_mhz": {"min": min(mc), "median": statistics.median(mc), "max": max(mc)},
-                "samples": len(self.samples), "source": "amdsmi, sampled during the timed replays"}
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        u = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_uclk")
+        if isinstance(u, (int, float)) and 0 < u < 65535:
+            return float(u)
+        return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
+    except Exception:  # no amdsmi, no permission or no such metric
+        return None
 
 
-def time_loop(fn, steps, warmup, graph=True, repeats=1, clocks=None):
+def clock_during(fn, steps, ms_per_step, replays=4):
+    """Shader clock while fn's steps run: the `steps` calls are captured into a
+    graph and replayed `replays` times back to back (untimed) while the library's
+    clock probe, one wavefront per XCD on a second stream, waits out the first
+    replay and then counts shader clocks against the 100 MHz real-time counter over
+    the next two.  Returns {mean, min, max} MHz over the XCDs, or None for replays
+    too short to sample."""
+    import torch
+
+    import rmsnorm_linear_projection_amd as rnl
+
+    replay_us = steps * ms_per_step * 1e3
+    if replay_us < 20:
+        return None
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    out = torch.zeros((8, 2), dtype=torch.int64, device="cuda:0")
+    rnl.clock_probe(int(2 * replay_us), delay_us=int(replay_us), workgroups=8, out=out, stream=side)
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    mhz = [100.0 * c / t for c, t in out.cpu().tolist() if t]
+    del g
+    if not mhz:
+        return None
+    return {"mean": round(sum(mhz) / len(mhz), 1), "min": round(min(mhz), 1), "max": round(max(mhz), 1)}
+
+
+def time_loop(fn, steps, warmup, graph=True, repeats=1):
     """Median ms per call of fn(i) over `repeats` timed runs of `steps` calls,
     after exactly `warmup` untimed calls; also returns every run's ms per call.
 
@@ -384,10 +366,8 @@ def time_loop(fn, steps, warmup, graph=True, repeats=1, clocks=None):
     replay, so host-side launch overhead (Python, ctypes) does not leak into
     the device time; the captured work is exactly the eager calls' kernels.
     Events bracket each replay on the stream it runs on, after a device
-    synchronisation.  `clocks` (a ClockSampler) samples the clocks during the
-    timed runs.
+    synchronisation.
     """
-    import contextlib
     import statistics
 
     import torch
@@ -407,23 +387,21 @@ def time_loop(fn, steps, warmup, graph=True, repeats=1, clocks=None):
                     fn(warmup + i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        with clocks if clocks is not None else contextlib.nullcontext():
-            for _ in range(repeats):
-                start.record()
-                g.replay()
-                end.record()
-                torch.cuda.synchronize()
-                runs.append(start.elapsed_time(end) / steps)
+        for _ in range(repeats):
+            start.record()
+            g.replay()
+            end.record()
+            torch.cuda.synchronize()
+            runs.append(start.elapsed_time(end) / steps)
         del g
     else:
-        with clocks if clocks is not None else contextlib.nullcontext():
-            for r in range(repeats):
-                start.record()
-                for i in range(steps):
-                    fn(warmup + r * steps + i)
-                end.record()
-                torch.cuda.synchronize()
-                runs.append(start.elapsed_time(end) / steps)
+        for r in range(repeats):
+            start.record()
+            for i in range(steps):
+                fn(warmup + r * steps + i)
+            end.record()
+            torch.cuda.synchronize()
+            runs.append(start.elapsed_time(end) / steps)
     return statistics.median(runs), runs  # ms
 
 
@@ -540,9 +518,10 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False, repe
 
     w = WORKLOADS[name]
     s = Setup(name, w)
-    clocks = ClockSampler()
-    ms, runs = time_loop(s.step, steps, warmup, graph, repeats, clocks)
+    ms, runs = time_loop(s.step, steps, warmup, graph, repeats)
     kms = time_loop(s.kern, steps, warmup, graph, repeats)[0] if s.kern is not s.step else ms
+    sclk = clock_during(s.step, steps, ms)
+    mclk = smu_mclk()
     if w["bound"] == "hbm":
         value, unit = bytes_of(w) / (ms * 1e-3) / 1e9, "GB/s"
     else:
@@ -579,7 +558,11 @@ def bench_one(name, steps, warmup, with_cpu=True, graph=True, vendor=False, repe
     }
     if repeats > 1:
         line["ms_per_step_runs"] = [round(r, 6) for r in runs]
-    line["clocks"] = clocks.summary()
+    line["clocks"] = {"sclk_mhz": sclk,
+                      "sclk_source": "clock probe (s_memtime against the 100 MHz s_memrealtime), one wavefront per "
+                                     "XCD on a second stream, over the 2nd and 3rd of 4 extra untimed replays of "
+                                     "the timed steps",
+                      "mclk_mhz": mclk, "mclk_source": "amdsmi (as the SMU reports it)"}
     if w["kind"] in ("chain", "mla"):
         # stage 2 is timed alone (the GEMM on the step's own qr); stage 1 with its reduce
         # and norm is the rest of the step
@@ -714,6 +697,66 @@ def hbm_ceiling(steps, warmup, repeats):
         torch.cuda.empty_cache()
 
 
+def _short_kernel(name):
+    """Kernel name without namespaces and argument list."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("rnl::(anonymous namespace)::", "").replace("rnl::", "")
+    depth = 0
+    for i in range(len(n) - 1, -1, -1):
+        if n[i] == ")":
+            depth += 1
+        elif n[i] == "(":
+            depth -= 1
+            if depth == 0:
+                n = n[:i]
+                break
+    return n.strip()
+
+
+def record_mfma(name, run_dir):
+    """Fold one rocprofv3 run with --pmc MfmaUtil GRBM_GUI_ACTIVE --kernel-trace of a
+    workload into profiles/counters.json: per library kernel, the average over its
+    dispatches of the MFMA busy percentage, of GRBM_GUI_ACTIVE (GPU clock cycles
+    while the kernel ran, summed over the 8 XCDs) and of the kernel's duration,
+    and the clock they imply (cycles per XCD / duration)."""
+    import csv
+    import glob
+
+    cc = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    kt = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not cc or not kt:
+        raise SystemExit(f"no counter_collection / kernel_trace CSV under {run_dir}")
+    dur = {}
+    for r in csv.DictReader(open(kt[0])):
+        dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3  # us
+    per = {}
+    for r in csv.DictReader(open(cc[0])):
+        if "rnl::" not in r["Kernel_Name"]:
+            continue
+        k = _short_kernel(r["Kernel_Name"])
+        d = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for k, disp in per.items():
+        rows = [(v, dur.get(i)) for i, v in disp.items() if dur.get(i)]
+        if not rows:
+            continue
+        n = len(rows)
+        util = sum(v.get("MfmaUtil", 0.0) for v, _ in rows) / n
+        grbm = sum(v.get("GRBM_GUI_ACTIVE", 0.0) for v, _ in rows) / n
+        us = sum(t for _, t in rows) / n
+        out[k] = {"dispatches": n, "mfma_busy_pct": round(util, 2), "grbm_gui_active": round(grbm),
+                  "duration_us": round(us, 3), "sclk_mhz": round(grbm / 8 / us, 1)}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    data = json.load(open(path)) if os.path.exists(path) else {"workloads": {}}
+    key = kernel_key_of(WORKLOADS[name])
+    rec = data["workloads"].setdefault(name, {})
+    rec["mfma"] = {"src_sha": src_sha(KERNEL_SOURCES[key]), "kernels": out}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(rec["mfma"]))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -733,9 +776,15 @@ def main():
                     help="run only the plain copy that calibrates the HBM byte counters")
     ap.add_argument("--record-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="fold rocprofv3 counter_collection.csv files of --workload into profiles/counters.json")
+    ap.add_argument("--record-mfma", metavar="RUN_DIR",
+                    help="fold a rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE --kernel-trace run of --workload "
+                         "into profiles/counters.json")
     args = ap.parse_args()
     if args.record_counters:
         record_counters(args.workload, *args.record_counters)
+        return
+    if args.record_mfma:
+        record_mfma(args.workload, args.record_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not supported",

@@ -413,6 +413,20 @@ RNL_API int linear_mxfp8(const uint8_t* xq, const uint8_t* x_scale, const uint8_
  */
 RNL_API int rnl_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll, void* stream);
 
+/*
+ * rnl_clock_probe -- clock probe; not a step of the method.  `workgroups`
+ * (1 to 1024) wavefronts each wait `delay_us` (0 to 10^7) microseconds, then
+ * spin for `microseconds` (1 to 10^7) of the 100 MHz real-time counter, and
+ * wavefront b writes out[2b] = shader clock cycles elapsed over the spin
+ * (s_memtime), out[2b + 1] = real-time ticks elapsed (s_memrealtime):
+ * 100 * out[2b] / out[2b + 1] is the shader clock in MHz on its compute unit.
+ * With 8 wavefronts each XCD gets one.  Run on a second stream beside a
+ * workload, it records the clock the workload runs at.  Every wait is bounded
+ * by the real-time counter, so it ends whatever else runs.
+ * Errors: RNL_ERR_NULL, RNL_ERR_SHAPE, RNL_ERR_ALIGN (out 8-byte), RNL_ERR_HIP.
+ */
+RNL_API int rnl_clock_probe(uint64_t* out, int64_t delay_us, int64_t microseconds, int workgroups, void* stream);
+
 /* Static description of a status code. */
 RNL_API const char* rnl_status_str(int status);
 

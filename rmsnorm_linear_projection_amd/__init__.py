@@ -34,6 +34,7 @@ __all__ = [
     "rmsnorm_linear_bf16_noalloc",
     "noalloc_scratch_bytes",
     "stream_read",
+    "clock_probe",
     "rmsnorm_linear_int8",
     "add_rmsnorm_linear_bf16",
     "add_rmsnorm_linear_int8",
@@ -143,6 +144,8 @@ def load_library() -> ctypes.CDLL:
     lib.rmsnorm_linear_bf16_noalloc.restype = ctypes.c_int
     lib.rnl_noalloc_scratch_bytes.argtypes = []
     lib.rnl_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.rnl_clock_probe.argtypes = [_c_p, _c_i64, _c_i64, ctypes.c_int, _c_p]
+    lib.rnl_clock_probe.restype = ctypes.c_int
     lib.rnl_stream_read.argtypes = [_c_p, ctypes.c_size_t, _c_p, ctypes.c_int, ctypes.c_int, _c_p]
     lib.rnl_stream_read.restype = ctypes.c_int
     lib.rnl_status_str.argtypes = [ctypes.c_int]
@@ -310,6 +313,23 @@ def stream_read(src, workgroups=1024, unroll=8, sink=None):
         rc = lib.rnl_stream_read(_ptr(src), nbytes, _ptr(sink), int(workgroups), int(unroll), _stream(src.device))
     _check(rc)
     return sink
+
+
+def clock_probe(microseconds, delay_us=0, workgroups=8, out=None, stream=None):
+    """Clock probe (not a step of the method): enqueue ``workgroups`` wavefronts that
+    wait ``delay_us``, then spin for ``microseconds`` of real time, on ``stream``
+    (torch's current stream by default); wavefront b writes [shader clocks, real-time
+    ticks at 100 MHz] to out[b] (int64 [workgroups, 2], on the current device).  The
+    shader clock in MHz is 100 * out[b, 0] / out[b, 1]."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.zeros((workgroups, 2), dtype=torch.int64, device=dev)
+    _dev_tensor(out, "out", torch.int64)
+    _shape(out.numel() >= 2 * workgroups, "out must hold two words per workgroup")
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(dev)).cuda_stream)
+    _check(lib.rnl_clock_probe(_ptr(out), int(delay_us), int(microseconds), int(workgroups), st))
+    return out
 
 
 def noalloc_scratch_bytes() -> int:

@@ -314,6 +314,17 @@ const char* rnl_status_str(int status) {
 
 const char* rnl_last_error(void) { return g_last_error; }
 
+int rnl_clock_probe(uint64_t* out, int64_t delay_us, int64_t microseconds, int workgroups, void* stream) {
+  if (out == nullptr) return fail(RNL_ERR_NULL, "out is required");
+  if (microseconds < 1 || microseconds > 10000000 || delay_us < 0 || delay_us > 10000000)
+    return fail(RNL_ERR_SHAPE, "microseconds must be in [1, 10^7] and delay_us in [0, 10^7]");
+  if (workgroups < 1 || workgroups > 1024) return fail(RNL_ERR_SHAPE, "workgroups must be in [1, 1024]");
+  RNL_ALIGN(out, 8, "out");
+  return hip_status(rnl::launch_clock_probe(out, (uint64_t)delay_us * 100u, (uint64_t)microseconds * 100u, workgroups,
+                                            static_cast<hipStream_t>(stream)),
+                    "clock probe launch");
+}
+
 int rnl_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll, void* stream) {
   if (src == nullptr || sink == nullptr) return fail(RNL_ERR_NULL, "src and sink are required");
   if (bytes == 0 || bytes % 16 != 0) return fail(RNL_ERR_SHAPE, "bytes must be a positive multiple of 16");

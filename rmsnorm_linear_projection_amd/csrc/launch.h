@@ -131,5 +131,9 @@ hipError_t launch_skinny_fp32w(const uint16_t* x, const uint16_t* gamma, float e
 // or 16) loads in flight per thread; sink receives one word per workgroup.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll,
                               hipStream_t s);
+// Clock probe (not a step of the method): `workgroups` wavefronts each wait `delay`
+// periods of the 100 MHz real-time counter, then spin for `ticks` periods;
+// out[2b] = shader clocks elapsed in that span, out[2b + 1] = real-time ticks.
+hipError_t launch_clock_probe(uint64_t* out, uint64_t delay, uint64_t ticks, int workgroups, hipStream_t s);
 
 }  // namespace rnl

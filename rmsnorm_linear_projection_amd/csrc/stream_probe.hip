@@ -1,5 +1,9 @@
-// Read-only HBM streaming probe: the practical ceiling the weight-bound paths
-// are measured against.  Not a step of the method.
+// Measurement probes, not steps of the method:
+//   * a read-only HBM streaming probe, the practical ceiling the weight-bound
+//     paths are measured against;
+//   * a clock probe: one wavefront that spins for a fixed wall time and counts
+//     shader clock ticks (s_memtime) against the 100 MHz real-time counter
+//     (s_memrealtime), run beside a workload to record the clock it runs at.
 //
 // The given number of workgroups of 256 threads read the buffer once with
 // 16-byte loads (each load instruction of a wavefront covers 1 KiB contiguous),
@@ -32,7 +36,38 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+// Spins until `ticks` periods of the 100 MHz real-time counter have passed (a
+// bounded wait: it ends whatever else runs), then stores the elapsed shader
+// clocks and real-time ticks.
+// Workgroup b writes out[2b], out[2b + 1]; with 8 workgroups each XCD gets one
+// (workgroups are dealt round-robin over the XCDs).  `delay` real-time ticks
+// pass before counting starts.
+__global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ out, uint64_t delay, uint64_t ticks) {
+  const uint64_t s0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t r0 = s0;
+  while (r0 - s0 < delay) {
+    __builtin_amdgcn_s_sleep(2);
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  uint64_t r1 = r0;
+  while (r1 - r0 < ticks) {
+    __builtin_amdgcn_s_sleep(2);
+    r1 = __builtin_amdgcn_s_memrealtime();
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_clock_probe(uint64_t* out, uint64_t delay, uint64_t ticks, int workgroups, hipStream_t s) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)workgroups), dim3(64), 0, s, out, delay, ticks);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll,
                               hipStream_t s) {

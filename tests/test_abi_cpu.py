@@ -344,3 +344,11 @@ def test_stream_probe_validation(lib):
     assert lib.rnl_stream_read(FAKE, 64, FAKE, 0, 4, NULL) == E["RNL_ERR_SHAPE"]
     assert lib.rnl_stream_read(FAKE, 64, FAKE, 8, 3, NULL) == E["RNL_ERR_ARG"]
     assert lib.rnl_stream_read(ODD, 64, FAKE, 8, 4, NULL) == E["RNL_ERR_ALIGN"]
+
+
+def test_clock_probe_validation(lib):
+    assert lib.rnl_clock_probe(NULL, 0, 10, 1, NULL) == E["RNL_ERR_NULL"]
+    assert lib.rnl_clock_probe(FAKE, 0, 0, 1, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_clock_probe(FAKE, -1, 10, 1, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_clock_probe(FAKE, 0, 10, 0, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_clock_probe(ctypes.c_void_p(0x10004), 0, 10, 1, NULL) == E["RNL_ERR_ALIGN"]

@@ -143,3 +143,13 @@ def test_stream_probe_reads_every_word_once(nbytes, workgroups, unroll):
     want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
     got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
     assert got == want
+
+
+def test_clock_probe_reads_a_plausible_clock():
+    """The clock probe waits, then spins for the requested wall time counting shader clocks: every wavefront's
+    ratio is a clock between 100 MHz and 3 GHz, and its real-time ticks cover the requested time."""
+    out = rnl.clock_probe(200, delay_us=50, workgroups=8)
+    torch.cuda.synchronize()
+    for cycles, ticks in out.cpu().tolist():
+        assert ticks >= 200 * 100
+        assert 100 <= 100.0 * cycles / ticks <= 3000
