@@ -133,6 +133,14 @@ def e4m3_codes(shape, std: float, seed: int, stream: int) -> torch.Tensor:
     return (t * std).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
 
 
+def e4m3_int_codes(shape, vmax: int, seed: int, stream: int) -> torch.Tensor:
+    """E4M3 bytes of integers uniform in [-vmax, vmax] (vmax <= 16, so every value is
+    exactly representable), as uint8."""
+    assert 0 < vmax <= 16
+    t = torch.randint(-vmax, vmax + 1, tuple(shape), generator=_gen(seed, stream), dtype=torch.int32)
+    return t.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
 def e8m0_codes(shape, lo: int, hi: int, seed: int, stream: int) -> torch.Tensor:
     """E8M0 scale bytes uniform in [lo, hi] (scale 2^(code - 127)), as uint8."""
     return torch.randint(lo, hi + 1, tuple(shape), generator=_gen(seed, stream), dtype=torch.int32).to(torch.uint8)
