@@ -697,6 +697,35 @@ def hbm_ceiling(steps, warmup, repeats):
         torch.cuda.empty_cache()
 
 
+def mfma_ceiling(steps, warmup, repeats):
+    """Matrix-core ceiling: the library's MFMA rate probe (rnl_mfma_probe), one
+    workgroup per CU, with one and with two wavefronts per SIMD, for the bf16,
+    int8 and scaled-E4M3 instructions the contractions use; the shader clock is
+    read beside the timed replays.  One JSON line per instruction."""
+    import torch
+
+    import rmsnorm_linear_projection_amd as rnl
+
+    peaks = {"bf16": PEAK["bf16"], "int8": PEAK["int8"], "fp8": PEAK["fp8"]}
+    for kind, (_, flop) in rnl.MFMA_PROBE_KINDS.items():
+        res = {}
+        for waves in (4, 8):
+            iters = 2048
+            sink = torch.empty(256 * waves, dtype=torch.int32, device="cuda:0")
+            fn = lambda i: rnl.mfma_probe(kind, 256, waves, iters, sink)  # noqa: E731
+            ms, _ = time_loop(fn, steps, warmup, True, repeats)
+            sclk = clock_during(fn, steps, ms)
+            rate = 256 * waves * iters * 8 * flop / (ms * 1e-3) / 1e12
+            res[f"{waves // 4} per SIMD"] = {"us_per_launch": round(ms * 1e3, 2), "rate": round(rate, 1),
+                                             "frac_of_peak": round(rate / peaks[kind], 4),
+                                             "sclk_mhz": sclk and sclk["mean"]}
+        print(json.dumps({"probe": "rnl_mfma_probe (register-only matrix instructions, 8 accumulators per wavefront)",
+                          "kind": kind, "unit": "TOP/s" if kind == "int8" else "TFLOP/s", "peak": peaks[kind],
+                          "wavefronts": res,
+                          "timing": f"hip graph of {steps} launches, median of {repeats} runs, {warmup} untimed"}),
+              flush=True)
+
+
 def _short_kernel(name):
     """Kernel name without namespaces and argument list."""
     n = name[5:] if name.startswith("void ") else name
@@ -770,6 +799,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured graph")
     ap.add_argument("--vendor", action="store_true",
                     help="also time the vendor library (torch.matmul / torch._int_mm) on the dominant kernel's operands")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="measure only the matrix-core rate of the bf16, int8 and scaled-E4M3 instructions")
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="measure only the read-only HBM streaming ceiling at several buffer sizes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -797,6 +828,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling(args.steps, args.warmup, args.repeats)
         return
     if args.hbm_ceiling:
         hbm_ceiling(args.steps, args.warmup, args.repeats)

@@ -427,6 +427,24 @@ RNL_API int rnl_stream_read(const void* src, size_t bytes, uint32_t* sink, int w
  */
 RNL_API int rnl_clock_probe(uint64_t* out, int64_t delay_us, int64_t microseconds, int workgroups, void* stream);
 
+/*
+ * rnl_mfma_probe -- MFMA rate probe; not a step of the method.
+ * `workgroups` (1 to 65536) workgroups of `waves_per_group` (1 to 16) wavefronts
+ * each issue `iterations` (1 to 2^24) x 8 matrix instructions into eight
+ * independent accumulators held in registers, no memory traffic:
+ *   kind 0: v_mfma_f32_16x16x32_bf16            (16384 flop each)
+ *   kind 1: v_mfma_i32_16x16x64_i8              (32768 op each)
+ *   kind 2: v_mfma_scale_f32_16x16x128_f8f6f4   (E4M3 operands, 65536 flop each)
+ * Wavefront w of workgroup b writes one word (a fold of its accumulators) to
+ * sink[b * waves_per_group + w]; sink holds workgroups * waves_per_group words.
+ * Its duration gives the practical matrix-core rate the contractions are
+ * compared with.
+ * Errors: RNL_ERR_NULL, RNL_ERR_ARG (kind), RNL_ERR_SHAPE, RNL_ERR_ALIGN (sink
+ * 4-byte), RNL_ERR_HIP.
+ */
+RNL_API int rnl_mfma_probe(int kind, int workgroups, int waves_per_group, int64_t iterations, uint32_t* sink,
+                           void* stream);
+
 /* Static description of a status code. */
 RNL_API const char* rnl_status_str(int status);
 

@@ -35,6 +35,8 @@ __all__ = [
     "noalloc_scratch_bytes",
     "stream_read",
     "clock_probe",
+    "mfma_probe",
+    "MFMA_PROBE_KINDS",
     "rmsnorm_linear_int8",
     "add_rmsnorm_linear_bf16",
     "add_rmsnorm_linear_int8",
@@ -148,6 +150,8 @@ def load_library() -> ctypes.CDLL:
     lib.rnl_clock_probe.restype = ctypes.c_int
     lib.rnl_stream_read.argtypes = [_c_p, ctypes.c_size_t, _c_p, ctypes.c_int, ctypes.c_int, _c_p]
     lib.rnl_stream_read.restype = ctypes.c_int
+    lib.rnl_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i64, _c_p, _c_p]
+    lib.rnl_mfma_probe.restype = ctypes.c_int
     lib.rnl_status_str.argtypes = [ctypes.c_int]
     lib.rnl_status_str.restype = ctypes.c_char_p
     lib.rnl_last_error.argtypes = []
@@ -312,6 +316,26 @@ def stream_read(src, workgroups=1024, unroll=8, sink=None):
     with torch.cuda.device(src.device):
         rc = lib.rnl_stream_read(_ptr(src), nbytes, _ptr(sink), int(workgroups), int(unroll), _stream(src.device))
     _check(rc)
+    return sink
+
+
+MFMA_PROBE_KINDS = {"bf16": (0, 16384), "int8": (1, 32768), "fp8": (2, 65536)}  # kind code, flop (op) per instruction
+
+
+def mfma_probe(kind, workgroups=256, waves=4, iterations=4096, sink=None, stream=None):
+    """MFMA rate probe (not a step of the method): ``workgroups`` x ``waves`` wavefronts
+    each issue ``iterations`` x 8 matrix instructions of ``kind`` ("bf16", "int8" or
+    "fp8", see MFMA_PROBE_KINDS) on register operands, on ``stream`` (torch's current
+    stream by default); returns the int32 sink, one word per wavefront."""
+    lib = load_library()
+    code = MFMA_PROBE_KINDS[kind][0]
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if sink is None:
+        sink = torch.empty(workgroups * waves, dtype=torch.int32, device=dev)
+    _dev_tensor(sink, "sink", torch.int32)
+    _shape(sink.numel() >= workgroups * waves, "sink must hold one word per wavefront")
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(dev)).cuda_stream)
+    _check(lib.rnl_mfma_probe(code, int(workgroups), int(waves), int(iterations), _ptr(sink), st))
     return sink
 
 

@@ -325,6 +325,18 @@ int rnl_clock_probe(uint64_t* out, int64_t delay_us, int64_t microseconds, int w
                     "clock probe launch");
 }
 
+int rnl_mfma_probe(int kind, int workgroups, int waves_per_group, int64_t iterations, uint32_t* sink, void* stream) {
+  if (sink == nullptr) return fail(RNL_ERR_NULL, "sink is required");
+  if (kind < 0 || kind > 2) return fail(RNL_ERR_ARG, "kind must be 0 (bf16), 1 (int8) or 2 (scaled E4M3)");
+  if (workgroups < 1 || workgroups > 65536) return fail(RNL_ERR_SHAPE, "workgroups must be in [1, 65536]");
+  if (waves_per_group < 1 || waves_per_group > 16) return fail(RNL_ERR_SHAPE, "waves_per_group must be in [1, 16]");
+  if (iterations < 1 || iterations > (int64_t(1) << 24)) return fail(RNL_ERR_SHAPE, "iterations must be in [1, 2^24]");
+  RNL_ALIGN(sink, 4, "sink");
+  return hip_status(rnl::launch_mfma_probe(kind, workgroups, waves_per_group, (int)iterations, sink,
+                                           static_cast<hipStream_t>(stream)),
+                    "MFMA probe launch");
+}
+
 int rnl_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int unroll, void* stream) {
   if (src == nullptr || sink == nullptr) return fail(RNL_ERR_NULL, "src and sink are required");
   if (bytes == 0 || bytes % 16 != 0) return fail(RNL_ERR_SHAPE, "bytes must be a positive multiple of 16");

@@ -135,5 +135,9 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
 // periods of the 100 MHz real-time counter, then spin for `ticks` periods;
 // out[2b] = shader clocks elapsed in that span, out[2b + 1] = real-time ticks.
 hipError_t launch_clock_probe(uint64_t* out, uint64_t delay, uint64_t ticks, int workgroups, hipStream_t s);
+// MFMA rate probe: `workgroups` x `waves` wavefronts, each `iters` x 8 matrix
+// instructions of the given kind (0 bf16, 1 int8, 2 scaled E4M3); one word per
+// wavefront to sink.
+hipError_t launch_mfma_probe(int kind, int workgroups, int waves, int iters, uint32_t* sink, hipStream_t s);
 
 }  // namespace rnl

@@ -3,7 +3,11 @@
 //     paths are measured against;
 //   * a clock probe: one wavefront that spins for a fixed wall time and counts
 //     shader clock ticks (s_memtime) against the 100 MHz real-time counter
-//     (s_memrealtime), run beside a workload to record the clock it runs at.
+//     (s_memrealtime), run beside a workload to record the clock it runs at;
+//   * an MFMA rate probe: every wavefront issues a fixed number of matrix
+//     instructions on register operands into eight independent accumulators,
+//     no memory traffic, the practical ceiling the contractions are measured
+//     against.
 //
 // The given number of workgroups of 256 threads read the buffer once with
 // 16-byte loads (each load instruction of a wavefront covers 1 KiB contiguous),
@@ -62,7 +66,76 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ 
   }
 }
 
+// MFMA rate probe.  KIND 0: v_mfma_f32_16x16x32_bf16 (16384 flop), 1:
+// v_mfma_i32_16x16x64_i8 (32768 op), 2: v_mfma_scale_f32_16x16x128_f8f6f4 with
+// E4M3 operands (65536 flop).  The operands are derived from the lane id so that
+// nothing folds; each wavefront stores a fold of its accumulators to
+// sink[global wavefront id], so the work is kept.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kProbeAcc = 8;
+
+template <int KIND>
+__global__ void mfma_probe_kernel(uint32_t* __restrict__ sink, int iters) {
+  const uint32_t lane = threadIdx.x & 63;
+  uint32_t fold = 0;
+  if constexpr (KIND == 0) {
+    // bf16 values near 2^-8: the sums stay finite over any iteration count used here
+    const uint32_t w = 0x3B803B80u ^ (lane & 7u);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w, w ^ 1u, w ^ 2u, w ^ 3u});
+    const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{w ^ 4u, w ^ 5u, w ^ 6u, w ^ 7u});
+    f32x4 acc[kProbeAcc];
+#pragma unroll
+    for (int j = 0; j < kProbeAcc; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kProbeAcc; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kProbeAcc; ++j) fold ^= __float_as_uint(acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3]);
+  } else if constexpr (KIND == 1) {
+    const i32x4 a = i32x4{(int)(0x01010101u ^ lane), 0x01010101, 0x01010101, 0x01010101};
+    const i32x4 b = i32x4{0x01010101, (int)(0x01010101u ^ (lane << 8)), 0x01010101, 0x01010101};
+    i32x4 acc[kProbeAcc];
+#pragma unroll
+    for (int j = 0; j < kProbeAcc; ++j) acc[j] = i32x4{0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kProbeAcc; ++j) acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kProbeAcc; ++j) fold ^= (uint32_t)(acc[j][0] ^ acc[j][1] ^ acc[j][2] ^ acc[j][3]);
+  } else {
+    // E4M3 0x30 = 0.5; scales 127 = 2^0
+    const int v = (int)(0x30303030u ^ (lane & 1u));
+    const i32x8 a = i32x8{v, v, v, v, v, v, v, v};
+    const i32x8 b = i32x8{v, v, v, v, v, v, v, 0x30303030};
+    f32x4 acc[kProbeAcc];
+#pragma unroll
+    for (int j = 0; j < kProbeAcc; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kProbeAcc; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j], 0, 0, 0, 127, 0, 127);
+    }
+#pragma unroll
+    for (int j = 0; j < kProbeAcc; ++j) fold ^= __float_as_uint(acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) fold ^= __shfl_xor(fold, off, kWave);
+  if (lane == 0) sink[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = fold;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(int kind, int workgroups, int waves, int iters, uint32_t* sink, hipStream_t s) {
+  const dim3 grid((unsigned)workgroups), block((unsigned)(64 * waves));
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((mfma_probe_kernel<0>), grid, block, 0, s, sink, iters); break;
+    case 1: hipLaunchKernelGGL((mfma_probe_kernel<1>), grid, block, 0, s, sink, iters); break;
+    default: hipLaunchKernelGGL((mfma_probe_kernel<2>), grid, block, 0, s, sink, iters); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_clock_probe(uint64_t* out, uint64_t delay, uint64_t ticks, int workgroups, hipStream_t s) {
   hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)workgroups), dim3(64), 0, s, out, delay, ticks);

@@ -346,6 +346,17 @@ def test_stream_probe_validation(lib):
     assert lib.rnl_stream_read(ODD, 64, FAKE, 8, 4, NULL) == E["RNL_ERR_ALIGN"]
 
 
+def test_mfma_probe_validation(lib):
+    assert lib.rnl_mfma_probe(0, 8, 4, 16, NULL, NULL) == E["RNL_ERR_NULL"]
+    assert lib.rnl_mfma_probe(3, 8, 4, 16, FAKE, NULL) == E["RNL_ERR_ARG"]
+    assert lib.rnl_mfma_probe(-1, 8, 4, 16, FAKE, NULL) == E["RNL_ERR_ARG"]
+    assert lib.rnl_mfma_probe(0, 0, 4, 16, FAKE, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_mfma_probe(0, 8, 17, 16, FAKE, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_mfma_probe(0, 8, 4, 0, FAKE, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_mfma_probe(0, 8, 4, (1 << 24) + 1, FAKE, NULL) == E["RNL_ERR_SHAPE"]
+    assert lib.rnl_mfma_probe(1, 8, 4, 16, ODD, NULL) == E["RNL_ERR_ALIGN"]
+
+
 def test_clock_probe_validation(lib):
     assert lib.rnl_clock_probe(NULL, 0, 10, 1, NULL) == E["RNL_ERR_NULL"]
     assert lib.rnl_clock_probe(FAKE, 0, 0, 1, NULL) == E["RNL_ERR_SHAPE"]

@@ -145,6 +145,28 @@ def test_stream_probe_reads_every_word_once(nbytes, workgroups, unroll):
     assert got == want
 
 
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+def test_mfma_probe_runs_its_instructions(kind):
+    """The MFMA rate probe really issues its matrix instructions: the same launch gives the same sink twice, and
+    the rate it implies (workgroups x waves x iterations x 8 instructions of known size over the measured time)
+    lies between 5% and 120% of the published dense peak -- above it the work would have been dropped."""
+    code, flop = rnl.MFMA_PROBE_KINDS[kind]
+    peak = {"bf16": 2500.0, "int8": 5000.0, "fp8": 5000.0}[kind]
+    wg, waves, iters = 256, 4, 2048
+    s1 = rnl.mfma_probe(kind, wg, waves, iters)
+    s2 = rnl.mfma_probe(kind, wg, waves, iters)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        rnl.mfma_probe(kind, wg, waves, iters, sink=s1)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 5 * wg * waves * iters * 8 * flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    assert 0.05 * peak <= rate <= 1.2 * peak, rate
+
+
 def test_clock_probe_reads_a_plausible_clock():
     """The clock probe waits, then spins for the requested wall time counting shader clocks: every wavefront's
     ratio is a clock between 100 MHz and 3 GHz, and its real-time ticks cover the requested time."""
