@@ -5,8 +5,9 @@
 // W streams from HBM.  Two facts shape the kernel:
 //   * a compute unit sustains only a limited number of outstanding HBM misses,
 //     so every CU must stream an equal share of W: a workgroup owns R weight
-//     rows (R in {16, 12, 8}, chosen on the host so that ceil(N / R) workgroups
-//     spread evenly over the 256 CUs, e.g. N = 6144 -> R = 12, 512 workgroups);
+//     rows (R a multiple of 4, at most 32 = two 16-row MFMA blocks, chosen on
+//     the host so that the busiest CU holds the fewest rows, then the largest
+//     R: N = 6144 -> R = 24, 256 workgroups, one per CU);
 //   * the activations (at most 16 x K bf16) are tiny and stay in L2; they are
 //     already normed and rounded (the norm runs once per token in a pre-pass),
 //     so the loop does no vector arithmetic at all.  For at most four rows the
