@@ -157,13 +157,14 @@ int bf16_path(const void* x, const void* residual, void* x_add, const void* gamm
                       "skinny split-K launch");
   }
   const uint16_t* wb = static_cast<const uint16_t*>(W);
-  // one or two tokens: the workgroup norms the rows once and each wavefront streams whole weight rows
-  const bool fuse_ok = rb == nullptr && forced_variant() != V_PREPASS;
+  // one or two tokens: the workgroup adds the residual (if any) and norms the rows once, and each
+  // wavefront streams whole weight rows
+  const bool fuse_ok = forced_variant() != V_PREPASS;
   if (fuse_ok && use_small_m(T) && rnl::row_gemv_fits(T, K))
-    return hip_status(rnl::launch_row_gemv_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
+    return hip_status(rnl::launch_row_gemv_norm_bf16(xb, rb, xab, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
                       "whole-row norm + projection launch (one or two tokens)");
-  // a few tokens whose normed rows fit LDS: the norm runs inside the weight-streaming kernel
-  if (fuse_ok && use_small_m(T) && rnl::small_m_norm_fits(T, K))
+  // a few tokens whose normed rows fit LDS, no residual: the norm runs inside the weight-streaming kernel
+  if (fuse_ok && rb == nullptr && use_small_m(T) && rnl::small_m_norm_fits(T, K))
     return hip_status(rnl::launch_small_m_norm_bf16(xb, gb, eps, wb, y, ok_kind, rstd_out, T, N, K, s),
                       "fused norm + projection launch");
   uint16_t* a = static_cast<uint16_t*>(workspace);

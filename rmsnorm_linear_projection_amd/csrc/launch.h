@@ -105,7 +105,9 @@ hipError_t launch_small_m_norm_bf16(const uint16_t* X, const uint16_t* gamma, fl
 // One or two tokens (M <= kRowGemvMaxM): y[M,N] = bf16(RMSNorm(X) * gamma) .
 // W^T on the VALU, the norm shared by the four wavefronts of a workgroup through
 // LDS, each wavefront streaming whole weight rows, 1 KiB per load instruction;
-// K a multiple of 8 and at most kRowGemvMaxK; gamma and rstd_out may be null.
+// K a multiple of 8 and at most kRowGemvMaxK; gamma and rstd_out may be null;
+// residual and x_add (given together or not at all) add the residual first and
+// write x_add out.
 constexpr int64_t kRowGemvMaxK = 8192;
 constexpr int64_t kRowGemvMaxM = 2;
 bool row_gemv_fits(int64_t M, int64_t K);
@@ -114,9 +116,9 @@ bool row_gemv_fits(int64_t M, int64_t K);
 // past 12)
 constexpr int64_t kRowGemvWaves = 1024;
 int row_gemv_rows(int64_t N, int kc);
-hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
-                                     void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
-                                     hipStream_t s);
+hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* residual, uint16_t* x_add,
+                                     const uint16_t* gamma, float eps, const uint16_t* W, void* C, int out_kind,
+                                     float* rstd_out, int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_small_m_bf16(const uint16_t* A, const uint16_t* W, void* C, int out_kind, int64_t M,
                                int64_t N, int64_t K, int R, hipStream_t s);
 

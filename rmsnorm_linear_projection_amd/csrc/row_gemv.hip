@@ -25,6 +25,10 @@
 //     row (wavefronts with no weight rows past N still take part);
 //   * the products run on the VALU (v_dot2c_f32_bf16: two bf16 products added
 //     to an fp32 accumulator per instruction); one token needs no matrix core;
+//   * with a residual (the pre-attention add of the AT-10 page, section 6) each
+//     chunk of x is first replaced by x_add = bf16(float(x) + float(residual)),
+//     rounded to nearest even -- the value the norm pre-pass forms -- and the
+//     wavefronts of workgroup 0 write x_add out;
 //   * each output's 64 lane partials are summed across the wavefront (DPP, no
 //     LDS) and lane t * RW + r stores token t's output r.  Measured at K = 4096,
 //     N = 6144: 10.1 us at T = 1, 11.4 at T = 2 (against 12.5 for the MFMA
@@ -47,6 +51,15 @@ __device__ __forceinline__ float dot8(u32x4 w, u32x4 a, float acc) {
                                           false);
   }
   return acc;
+}
+
+// bf16(float(x) + float(r)) for 8 elements
+__device__ __forceinline__ u32x4 add8(u32x4 x, u32x4 r) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = pack_bf16x2(__fadd_rn(bf16lo(x[j]), bf16lo(r[j])), __fadd_rn(bf16hi(x[j]), bf16hi(r[j])));
+  return o;
 }
 
 // a = bf16(fl(fl(x * rstd) * g)) for 8 elements (g = 1 without gamma)
@@ -96,6 +109,8 @@ __device__ __forceinline__ float wave_total(float v) {
 // KC: 16-byte chunks per lane and row (K <= 512 * KC); RW: rows per wavefront
 template <int MT, int KC, int RW>
 __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ residual,
+                                                           uint16_t* __restrict__ x_add,
                                                            const uint16_t* __restrict__ gamma, float eps,
                                                            float inv_k, const uint16_t* __restrict__ W,
                                                            void* __restrict__ C, bool out_bf16,
@@ -109,9 +124,11 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
   const int n0 = wv * RW;
   const int rows = n0 < N ? min(RW, N - n0) : 0;  // 0: the wavefront only helps with the norm
   const bool has_g = gamma != nullptr;
+  const bool has_r = residual != nullptr;
   const uint32_t kbytes = (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(has_g ? gamma : X, has_g ? kbytes : 0u);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(has_r ? residual : X, has_r ? (uint32_t)M * kbytes : 0u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)min(n0, N - 1) * K, (uint32_t)rows * kbytes);
 
   u32x4 xv[MT][XC], gv[XC], w[RW][KC];
@@ -124,6 +141,17 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
     for (int t = 0; t < MT; ++t) xv[t][i] = buf_load16(rx, (in && t < M) ? o + (uint32_t)t * kbytes : kOOB);
     gv[i] = buf_load16(rg, in ? o : kOOB);  // zeros without gamma (an empty resource), not used then
   }
+  u32x4 rv[MT][XC];
+  if (has_r) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = wave + 4 * i;
+      const uint32_t o = (uint32_t)(c * 64 + lane) * 16u;
+      const bool in = c < KC && o < kbytes;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) rv[t][i] = buf_load16(rr, (in && t < M) ? o + (uint32_t)t * kbytes : kOOB);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -134,6 +162,18 @@ __global__ __launch_bounds__(256) void row_gemv_norm_kernel(const uint16_t* __re
   // keep every load above issued before the norm arithmetic waits on the first
   __builtin_amdgcn_sched_barrier(0);
 
+  if (has_r) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < XC; ++i) {
+        xv[t][i] = add8(xv[t][i], rv[t][i]);
+        const int c = wave + 4 * i;
+        const uint32_t o = (uint32_t)(c * 64 + lane) * 16u;
+        if (blockIdx.x == 0 && t < M && c < KC && o < kbytes)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(x_add) + (size_t)t * kbytes + o) = xv[t][i];
+      }
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     float ss = 0.f;
@@ -210,9 +250,10 @@ int row_gemv_rows(int64_t N, int kc) {
   return (int)(rw < cap ? rw : cap);
 }
 
-hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* gamma, float eps, const uint16_t* W,
-                                     void* C, int out_kind, float* rstd_out, int64_t M, int64_t N, int64_t K,
-                                     hipStream_t s) {
+hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* residual, uint16_t* x_add,
+                                     const uint16_t* gamma, float eps, const uint16_t* W, void* C, int out_kind,
+                                     float* rstd_out, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if ((residual == nullptr) != (x_add == nullptr)) return hipErrorInvalidValue;
   if (!row_gemv_fits(M, K) || N < 1 || N > 0x7fffffff) return hipErrorInvalidValue;
   const int mt = M <= 1 ? 1 : 2;
   const int kc = (int)((K + 511) / 512);
@@ -222,7 +263,8 @@ hipError_t launch_row_gemv_norm_bf16(const uint16_t* X, const uint16_t* gamma, f
   const int64_t waves = (N + rw - 1) / rw;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
 #define RNL_ROW_GEMV1(MT, KC, RW)                                                                           \
-  hipLaunchKernelGGL((row_gemv_norm_kernel<MT, KC, RW>), grid, block, 0, s, X, gamma, eps, inv_k, W, C, ob, \
+  hipLaunchKernelGGL((row_gemv_norm_kernel<MT, KC, RW>), grid, block, 0, s, X, residual, x_add, gamma, eps,     \
+                     inv_k, W, C, ob,                                                                         \
                      rstd_out, (int)M, (int)K, (int)N)
 #define RNL_ROW_GEMV(KC, RW)                                     \
   do {                                                           \

@@ -590,6 +590,9 @@ def check_add_bf16_case(case, rows=None, out_dtype=torch.bfloat16):
 
 
 ADD_BF16 = [
+    (1, 4096, 6144),   # one and two tokens: the whole-row kernel adds the residual itself
+    (2, 520, 300),
+    (1, 8192, 70),
     (8, 256, 128),     # weight streaming, one wavefront per row
     (16, 4104, 40),
     (300, 1032, 200),  # tiled GEMM, ragged tiles
@@ -800,6 +803,8 @@ def check_preattn_case(case, rows=None):
     (8, 256, 4, 2, 64, False, True, True),
     (8, 256, 4, 2, 64, True, False, False),
     (2, 256, 4, 2, 64, False, True, True),     # two tokens: the whole-row kernel
+    (1, 4096, 32, 8, 128, True, True, True),   # one decode token with the residual add, in the whole-row kernel
+    (2, 520, 4, 2, 64, True, True, True),
     (16, 512, 4, 2, 64, False, True, True),    # sixteen tokens: the norm fused into the weight streaming
     (40, 1032, 6, 1, 128, True, True, True),   # tiled GEMM, ragged tiles
     (3, 64, 2, 0, 16, False, True, False),     # no key / value heads
