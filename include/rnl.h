@@ -33,8 +33,9 @@
  *     is needed and the pointer may be NULL).  Its contents on entry do not
  *     matter and are undefined afterwards.
  *   - bf16 projections with at most 16 activation rows run a weight-streaming
- *     kernel (one or two rows with K <= 8192 and no residual: a kernel that streams
- *     whole weight rows and multiplies on the vector units), larger ones the
+ *     kernel (one or two rows with K <= 8192: a kernel that adds the residual
+ *     if any, norms the rows, streams whole weight rows and multiplies on the
+ *     vector units), larger ones the
  *     tiled GEMM.  Environment variable RNL_VARIANT
  *     (read at every call) set to "gemm" forces the tiled GEMM for any size,
  *     "prepass" forces the separate norm pre-pass (no norm fused into the
