@@ -196,6 +196,27 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Dequant scales of this wavefront's rows and columns, requested before the first stages
+  // so that they have long landed when the epilogue needs them (loading them per element in
+  // the epilogue made it three times as long as the plain int32 one).  Out-of-range rows and
+  // columns read as zero; their outputs are never stored.
+  constexpr bool DEQ = EPI == EPI_DEQ_BF16 || EPI == EPI_DEQ_F32;
+  float xs_r[DEQ ? NMI : 1], ws_r[DEQ ? NNI : 1][4];
+  if constexpr (DEQ) {
+    const __amdgpu_buffer_rsrc_t rxs = make_rsrc(xs, (uint32_t)M * 4u);
+    const __amdgpu_buffer_rsrc_t rws = make_rsrc(ws, (uint32_t)N * 4u);
+#pragma unroll
+    for (int i = 0; i < NMI; ++i)
+      xs_r[i] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rxs, (uint32_t)(m0 + wm * WM + i * 16 + (lane & 15)) * 4u, 0, 0));
+#pragma unroll
+    for (int j = 0; j < NNI; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ws_r[j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rws, (uint32_t)(n0 + wn * WN + j * 16 + 4 * (lane >> 4) + r) * 4u, 0, 0));
+  }
+
   // Every stage slot is always filled (k-steps past the range read as zero), so the
   // number of DMA loads in flight is the same at every wait.
 #pragma unroll
@@ -232,7 +253,7 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
     const int m = m0 + wm * WM + i * 16 + (lane & 15);
     if (m >= M) continue;
     float xsm = 0.f;
-    if constexpr (EPI == EPI_DEQ_BF16 || EPI == EPI_DEQ_F32) xsm = xs[m];
+    if constexpr (DEQ) xsm = xs_r[i];
 #pragma unroll
     for (int j = 0; j < NNI; ++j) {
       const int n = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
@@ -251,9 +272,8 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if constexpr (EPI == EPI_DEQ_BF16 || EPI == EPI_DEQ_F32) {
-            const float wsn = (n + r < N) ? ws[n + r] : 0.f;
-            v[r] = __fmul_rn((float)acc[i][j][r], __fmul_rn(xsm, wsn));
+          if constexpr (DEQ) {
+            v[r] = __fmul_rn((float)acc[i][j][r], __fmul_rn(xsm, ws_r[j][r]));
           } else {
             v[r] = (float)acc[i][j][r];
           }
