@@ -115,10 +115,12 @@ bool add_overlaps(const void* x, const void* residual, const void* x_add, int64_
 
 // The bf16 / fp32-weight path, with an optional residual added before the norm
 // (residual and x_add both non-null) -- shared by rmsnorm_linear_bf16 and
-// add_rmsnorm_linear_bf16.
+// add_rmsnorm_linear_bf16.  With `heads`, a call that reaches the tiled GEMM runs the
+// per-head stage in its epilogue (bf16 weights and output only), and *heads_done is set.
 int bf16_path(const void* x, const void* residual, void* x_add, const void* gamma, float eps, const void* W,
               int w_dtype, void* y, int out_dtype, float* rstd_out, int64_t T, int64_t K, int64_t N,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream, const rnl::HeadArgs* heads = nullptr,
+              bool* heads_done = nullptr) {
   if (x == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "x, W and y are required");
   RNL_TRY(check_dims(T, K, N, kMaxK));
   if (w_dtype != RNL_BF16 && w_dtype != RNL_FP32) return fail(RNL_ERR_DTYPE, "w_dtype must be RNL_BF16 or RNL_FP32");
@@ -171,6 +173,11 @@ int bf16_path(const void* x, const void* residual, void* x_add, const void* gamm
   const hipError_t e = rb != nullptr ? rnl::launch_add_norm_rows_bf16(xb, rb, xab, gb, eps, T, K, a, rstd_out, s)
                                      : rnl::launch_norm_rows_bf16(xb, gb, eps, T, K, a, rstd_out, s);
   if (e != hipSuccess) return hip_status(e, "norm pre-pass launch");
+  if (heads != nullptr && ok_kind == rnl::OUT_BF16 && !use_small_m(T)) {
+    *heads_done = true;
+    return hip_status(rnl::launch_gemm_bf16_heads(a, wb, static_cast<uint16_t*>(y), T, N, K, *heads, s),
+                      "bf16 projection launch with the per-head epilogue");
+  }
   return hip_status(project_bf16(a, wb, y, ok_kind, T, N, K, s), "bf16 projection launch");
 }
 
@@ -600,8 +607,15 @@ int preattn_qkv_bf16(const void* x, const void* residual, void* x_add_out, const
   RNL_ALIGN(sin_t, 16, "sin");
   RNL_ALIGN(head_rstd_out, 4, "head_rstd_out");
   const int64_t N = (Hq + 2 * Hkv) * D;
+  // Heads of 128 on the tiled GEMM: the per-head stage runs in the GEMM's epilogue
+  // (RNL_VARIANT=prepass keeps it a separate pass, as for other head sizes and few tokens).
+  const rnl::HeadArgs ha{static_cast<const uint16_t*>(gamma_q), static_cast<const uint16_t*>(gamma_k), cos_t, sin_t,
+                         head_rstd_out, head_eps, 1.0f / (float)D, (int)Hq, (int)Hkv};
+  const bool epi = D == rnl::kHeadEpiD && forced_variant() != V_PREPASS;
+  bool heads_done = false;
   RNL_TRY(bf16_path(x, residual, x_add_out, gamma, eps, W, RNL_BF16, y, RNL_BF16, rstd_out, T, K, N, workspace,
-                    workspace_bytes, stream));
+                    workspace_bytes, stream, epi ? &ha : nullptr, &heads_done));
+  if (heads_done) return ok();
   uint16_t* yb = static_cast<uint16_t*>(y);
   return hip_status(rnl::launch_head_norm_bf16(yb, yb, T, N, 0, Hq + Hkv, D, Hq,
                                                static_cast<const uint16_t*>(gamma_q),

@@ -28,6 +28,14 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int o
   return launch_shape<uint16_t, EPI_BF16>(sh, A, B, C, nullptr, nullptr, M, N, K, 1, s);
 }
 
+// The per-head epilogue needs whole heads in a tile: 128 x 384 (three heads of 128), eight
+// wavefronts of 64 x 96 as in the 256 x 192 tile, two stages (128 KiB, which also hold the
+// output tile).  At 4096 x 6144 it gives 512 tiles, two rounds of workgroups.
+hipError_t launch_gemm_bf16_heads(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N,
+                                  int64_t K, const HeadArgs& heads, hipStream_t s) {
+  return launch_tile<uint16_t, 128, 384, 2, EPI_HEADS, 1, 4, 2>(A, B, C, nullptr, nullptr, M, N, K, 1, s, heads);
+}
+
 hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, float* partial, int64_t M,
                                    int64_t N, int64_t K, int ksplit, hipStream_t s) {
   return launch_shape<uint16_t, EPI_PART>(pick_shape(M, N), A, B, partial, nullptr, nullptr, M, N, K,

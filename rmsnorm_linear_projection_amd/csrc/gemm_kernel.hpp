@@ -44,6 +44,7 @@
 
 #include "common.hpp"
 #include "launch.h"
+#include "rows.hpp"
 
 namespace rnl {
 namespace gemm_detail {
@@ -76,6 +77,7 @@ enum Epi : int {
   EPI_DEQ_BF16 = 3,  // C bf16 = round(fl(float(acc) * fl(xs[m] * ws[n])))
   EPI_DEQ_F32 = 4,   // C fp32 = fl(float(acc) * fl(xs[m] * ws[n]))
   EPI_PART = 5,      // C[z] = acc (fp32 or int32 partial of split z)
+  EPI_HEADS = 6,     // C bf16 = round(acc), then the per-head stage (HeadArgs) on whole heads of the tile
 };
 
 // s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt unchanged (gfx9 encoding)
@@ -87,7 +89,7 @@ template <typename TIn, int BM, int BN, int NST, int GROUP_M, int EPI, int WPE =
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WMW * WNW, 64 * WMW * WNW), amdgpu_waves_per_eu(WPE * WMW * WNW / 4, WPE * WMW * WNW / 4)))
 void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* __restrict__ C,
                     const float* __restrict__ xs, const float* __restrict__ ws, int M, int N, int K,
-                    int tiles_m, int tiles_n, int ksplit, int steps_per_split) {
+                    int tiles_m, int tiles_n, int ksplit, int steps_per_split, const HeadArgs ha) {
   using Acc = typename Mfma<TIn>::Acc;
   constexpr int ROWB = 128;
   constexpr int NWV = WMW * WNW;       // wavefronts: WMW along M x WNW along N
@@ -196,6 +198,75 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Per-head epilogue.  The bf16-rounded tile goes to LDS (the stages are free once every
+  // wavefront is past its last fragment read), then each group of GP lanes takes one
+  // (token row, head) of the tile: lane q holds elements 8q .. 8q+7 and D/2+8q .. D/2+8q+7, the
+  // layout of the standalone per-head kernel, and the same arithmetic (head_sumsq, group_sum,
+  // head_chunks) gives the same bits.  Value heads are stored as they are.
+  auto heads_epilogue = [&](const HeadArgs& h) {
+    if constexpr (EPI == EPI_HEADS) {
+      constexpr int HD = kHeadEpiD, GP = HD / 16, HPT = BN / HD, UPW = kWave / GP;
+      constexpr int LDY = BN + 8;  // bf16 per LDS tile row (padded)
+      static_assert(sizeof(TIn) == 2 && BN % HD == 0, "whole bf16 heads per tile");
+      static_assert(BM * LDY * 2 <= NST * STAGE, "the output tile fits the stages");
+      static_assert((BM * HPT) % (NWV * UPW) == 0, "whole rounds of head groups");
+      uint16_t* ty = reinterpret_cast<uint16_t*>(smem);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NMI; ++i)
+#pragma unroll
+        for (int j = 0; j < NNI; ++j)
+          *reinterpret_cast<u32x2*>(ty + (wm * WM + i * 16 + (lane & 15)) * LDY + wn * WN + j * 16 + 4 * (lane >> 4)) =
+              u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+      __syncthreads();
+      const int gl = lane & (GP - 1);
+      const int c0 = gl * 8, c1 = c0 + HD / 2;
+      const int nqk = h.hq + h.hkv;
+      const bool rope = h.cos_t != nullptr;
+      uint16_t* y = static_cast<uint16_t*>(C);
+#pragma unroll 1
+      for (int it = 0; it < BM * HPT / (NWV * UPW); ++it) {
+        const int u = (it * NWV + wave) * UPW + lane / GP;
+        const int r = u / HPT, hh = u - r * HPT;
+        const int t = m0 + r, col = n0 + hh * HD, hg = col / HD;
+        const bool live = t < M && col < N;
+        const int ts = live ? t : 0;  // a row that exists, for the loads of dead groups
+        const uint16_t* src = ty + r * LDY + hh * HD;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
+        const bool qk = hg < nqk;
+        const uint16_t* gamma = hg < h.hq ? h.gamma_q : h.gamma_k;
+        const bool g_on = gamma != nullptr;
+        u32x4 g0 = v0, g1 = v1;
+        if (g_on) {
+          g0 = *reinterpret_cast<const u32x4*>(gamma + c0);
+          g1 = *reinterpret_cast<const u32x4*>(gamma + c1);
+        }
+        f32x4 cs[2], sn[2];
+        if (rope) {
+          const float* ca = h.cos_t + (size_t)ts * (HD / 2) + c0;
+          const float* sa = h.sin_t + (size_t)ts * (HD / 2) + c0;
+          cs[0] = *reinterpret_cast<const f32x4*>(ca);
+          cs[1] = *reinterpret_cast<const f32x4*>(ca + 4);
+          sn[0] = *reinterpret_cast<const f32x4*>(sa);
+          sn[1] = *reinterpret_cast<const f32x4*>(sa + 4);
+        }
+        const float rstd = rstd_from_sumsq(group_sum<GP>(head_sumsq(v0, v1)), h.inv_d, h.eps);
+        u32x4 o0 = v0, o1 = v1;
+        if (qk) {
+          if (rope) head_chunks<true>(v0, v1, g0, g1, g_on, cs, sn, rstd, o0, o1);
+          else head_chunks<false>(v0, v1, g0, g1, g_on, cs, sn, rstd, o0, o1);
+        }
+        if (live) {
+          uint16_t* dst = y + (size_t)t * (size_t)N + (size_t)col;
+          *reinterpret_cast<u32x4*>(dst + c0) = o0;
+          *reinterpret_cast<u32x4*>(dst + c1) = o1;
+          if (qk && gl == 0 && h.rstd_out != nullptr) h.rstd_out[(size_t)t * (size_t)nqk + hg] = rstd;
+        }
+      }
+    }
+  };
+
   // Dequant scales of this wavefront's rows and columns, requested before the first stages
   // so that they have long landed when the epilogue needs them (loading them per element in
   // the epilogue made it three times as long as the plain int32 one).  Out-of-range rows and
@@ -245,6 +316,11 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
   phase(F0, F1, slot, 1, -1, 0);
   phase(F1, F0, 0, -1, -1, 0);
   RNL_WAIT_VM_LGKM0(0);
+
+  if constexpr (EPI == EPI_HEADS) {
+    heads_epilogue(ha);
+    return;
+  }
 
   // epilogue: lane holds C[m][n .. n+3]
   const bool vec_ok = (N & 3) == 0;
@@ -305,13 +381,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename TIn, int BM, int BN, int NST, int EPI, int WPE = 1, int WNW = 2, int WMW = 2>
 hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws, int64_t M,
-                       int64_t N, int64_t K, int ksplit, hipStream_t s) {
+                       int64_t N, int64_t K, int ksplit, hipStream_t s, const HeadArgs& ha = HeadArgs{}) {
   const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   const int nk = (int)cdiv(K * (int64_t)sizeof(TIn), 128);
   const int sps = (int)cdiv(nk, ksplit);
   const int nwg = tiles_m * tiles_n * ksplit;
   hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI, WPE, WNW, WMW>), dim3(nwg), dim3(64 * WMW * WNW), 0, s, A, B, C,
-                     xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n, ksplit, sps);
+                     xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n, ksplit, sps, ha);
   return hipGetLastError();
 }
 

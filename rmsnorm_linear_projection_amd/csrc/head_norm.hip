@@ -20,6 +20,8 @@
 // once.  All loads (the two chunks, their gammas, the angles) are issued
 // together.  The sum of squares is reduced inside the group with DPP moves;
 // each chunk is written back by the lane that read it, so y_out may be y_in.
+// The arithmetic (head_sumsq, group_sum, head_chunks) is shared with the
+// projection GEMM's per-head epilogue, so both give the same bits.
 #include "launch.h"
 #include "rows.hpp"
 
@@ -28,29 +30,11 @@ namespace {
 
 constexpr int kHeadThreads = 256;
 
-// sum over the GP lanes of a group (GP a power of two <= 32, groups aligned to
-// GP lanes); every lane of the group ends with the same value
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-template <int GP>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (GP >= 2) v += dpp_f<0xB1>(v);   // quad_perm 1,0,3,2: lane ^ 1
-  if constexpr (GP >= 4) v += dpp_f<0x4E>(v);   // quad_perm 2,3,0,1: lane ^ 2
-  if constexpr (GP >= 8) v += dpp_f<0x141>(v);  // row_half_mirror: the two quads of 8 lanes
-  if constexpr (GP >= 16) v += dpp_f<0x140>(v); // row_mirror: the two halves of 16 lanes
-  if constexpr (GP >= 32) v += __shfl_xor(v, 16, kWave);
-  return v;
-}
-
 template <int GP, bool ROPE>
 __global__ __launch_bounds__(kHeadThreads) void head_norm_kernel(
     const uint16_t* y_in, uint16_t* y_out, int64_t ld, int64_t col0, int64_t nheads_total, int H, int D,
     int H1, const uint16_t* __restrict__ gamma1, const uint16_t* __restrict__ gamma2, float eps, float inv_d,
     const float* __restrict__ cos_t, const float* __restrict__ sin_t, float* __restrict__ rstd_out) {
-#pragma clang fp contract(off)
   constexpr int HPW = kWave / GP;  // heads per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gl = lane & (GP - 1);
@@ -86,41 +70,13 @@ __global__ __launch_bounds__(kHeadThreads) void head_norm_kernel(
     sn[1] = *reinterpret_cast<const f32x4*>(sin_t + ab + 4);
   }
   // lanes that own no chunk (past D/16, or past the last head) add nothing to their group's sum
-  const float ss = act ? sumsq8(v0) + sumsq8(v1) : 0.f;
+  const float ss = act ? head_sumsq(v0, v1) : 0.f;
   const float rstd = rstd_from_sumsq(group_sum<GP>(ss), inv_d, eps);
-
-  float n0[8], n1[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    n0[2 * j] = bf16lo(v0[j]) * rstd;
-    n0[2 * j + 1] = bf16hi(v0[j]) * rstd;
-    n1[2 * j] = bf16lo(v1[j]) * rstd;
-    n1[2 * j + 1] = bf16hi(v1[j]) * rstd;
-  }
-  if (g_on) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      n0[2 * j] = n0[2 * j] * bf16lo(g0[j]);
-      n0[2 * j + 1] = n0[2 * j + 1] * bf16hi(g0[j]);
-      n1[2 * j] = n1[2 * j] * bf16lo(g1[j]);
-      n1[2 * j + 1] = n1[2 * j + 1] * bf16hi(g1[j]);
-    }
-  }
-  if constexpr (ROPE) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float c = cs[e >> 2][e & 3], s = sn[e >> 2][e & 3];
-      const float lo = n0[e] * c - n1[e] * s;  // element i
-      const float hi = n1[e] * c + n0[e] * s;  // element i + D/2
-      n0[e] = lo;
-      n1[e] = hi;
-    }
-  }
+  u32x4 o0, o1;
+  head_chunks<ROPE>(v0, v1, g0, g1, g_on, cs, sn, rstd, o0, o1);
   if (act) {
-    *reinterpret_cast<u32x4*>(y_out + row + c0) =
-        u32x4{pack_bf16x2(n0[0], n0[1]), pack_bf16x2(n0[2], n0[3]), pack_bf16x2(n0[4], n0[5]), pack_bf16x2(n0[6], n0[7])};
-    *reinterpret_cast<u32x4*>(y_out + row + c1) =
-        u32x4{pack_bf16x2(n1[0], n1[1]), pack_bf16x2(n1[2], n1[3]), pack_bf16x2(n1[4], n1[5]), pack_bf16x2(n1[6], n1[7])};
+    *reinterpret_cast<u32x4*>(y_out + row + c0) = o0;
+    *reinterpret_cast<u32x4*>(y_out + row + c1) = o1;
     if (gl == 0 && rstd_out != nullptr) rstd_out[head] = rstd;
   }
 }

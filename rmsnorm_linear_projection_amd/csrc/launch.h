@@ -57,6 +57,26 @@ hipError_t launch_head_norm_bf16(const uint16_t* y_in, uint16_t* y_out, int64_t 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int out_kind, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);
 
+// Per-head stage applied inside the GEMM's epilogue (the pre-attention block):
+// the columns of C are hq query heads, then hkv key heads, then value heads, of
+// kHeadEpiD columns each; query and key heads are normed and rotated exactly as
+// launch_head_norm_bf16 does (gamma_q for query heads, gamma_k for key heads,
+// cos / sin both null for no rotation), value heads are the bf16 product.
+constexpr int kHeadEpiD = 128;
+struct HeadArgs {
+  const uint16_t* gamma_q;  // [D] bf16 or null
+  const uint16_t* gamma_k;  // [D] bf16 or null
+  const float* cos_t;       // [M, D/2] fp32 or null
+  const float* sin_t;       // [M, D/2] fp32 or null
+  float* rstd_out;          // [M, hq + hkv] or null
+  float eps;
+  float inv_d;              // fl(1/D)
+  int hq, hkv;
+};
+// C = bf16(A . B^T) with the per-head stage in the epilogue; N = (hq + 2 hkv) D.
+hipError_t launch_gemm_bf16_heads(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N,
+                                  int64_t K, const HeadArgs& heads, hipStream_t s);
+
 // Number of K splits the bf16/int8 GEMM would use for an output of M x N (1 when
 // the tiles alone fill the chip); elem_bytes is the operand size.
 int gemm_split_plan(int64_t M, int64_t N, int64_t K, int elem_bytes, int* shape);

@@ -816,6 +816,28 @@ def test_preattn_small(T, K, Hq, Hkv, D, residual, rope, head_gamma):
     check_preattn_case(case)
 
 
+@pytest.mark.parametrize("T,K,Hq,Hkv,residual,rope,head_gamma,force_gemm", [
+    (300, 520, 3, 1, False, True, True, False),    # two column tiles, the second holding two heads; ragged rows
+    (130, 256, 2, 0, False, False, False, False),  # query heads only, no rotation, no head gammas
+    (257, 1024, 4, 2, True, True, False, False),   # residual add, key heads without a gamma
+    (40, 1032, 6, 1, True, True, True, False),
+    (8, 256, 1, 1, False, True, True, True),       # eight tokens on the tiled GEMM (RNL_VARIANT=gemm)
+    (4096, 4096, 32, 8, True, True, True, False),  # the pre-attention block
+])
+def test_preattn_head_epilogue(variant, T, K, Hq, Hkv, residual, rope, head_gamma, force_gemm):
+    """Heads of 128 on the tiled GEMM: the per-head stage in the GEMM's epilogue against the oracle, and
+    bit for bit against the separate per-head pass (RNL_VARIANT=prepass)."""
+    case = synthetic.preattn_case(T, K, Hq, Hkv, 128, seed=T + 7 * Hq, residual=residual, rope=rope,
+                                  head_gamma=head_gamma)
+    variant("gemm" if force_gemm else None)
+    y = check_preattn_case(case)
+    _, _, _, rstd, hr = run_preattn(case)
+    variant("prepass")
+    y2, _, _, rstd2, hr2 = run_preattn(case)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "epilogue and separate pass differ"
+    assert np.array_equal(hr, hr2) and np.array_equal(rstd, rstd2)
+
+
 @pytest.mark.parametrize("T", [4096, 16])
 def test_preattn_block_full_size(T):
     """Residual add -> norm -> fused QKV -> per-head norm -> RoPE, K=4096, 32 + 8 + 8 heads of 128."""
