@@ -39,8 +39,9 @@
  *     tiled GEMM.  Environment variable RNL_VARIANT
  *     (read at every call) set to "gemm" forces the tiled GEMM for any size,
  *     "prepass" forces the separate norm pre-pass (no norm fused into the
- *     weight-streaming kernels), for testing; anything else, or unset, lets
- *     the shape decide.
+ *     weight-streaming kernels) and the separate per-head pass of
+ *     preattn_qkv_bf16, for testing; anything else, or unset, lets the shape
+ *     decide.
  */
 #ifndef RNL_H
 #define RNL_H
@@ -306,6 +307,9 @@ RNL_API size_t mla_prolog_bf16_workspace_bytes(int64_t T, int64_t K, int64_t R, 
  *          out[i]       = fl(fl(n[i] c) - fl(n[i+D/2] s)),
  *          out[i + D/2] = fl(fl(n[i+D/2] c) + fl(n[i] s)),  c, s = cos[t,i], sin[t,i];
  *   y     = round_bf16 of that; value heads are p unchanged.
+ * With D = 128 on the tiled GEMM (more than 16 tokens) the per-head stage runs
+ * in the GEMM's epilogue; otherwise it is a separate pass over y.  The results
+ * are the same bits either way.
  *
  *   x, residual, x_add_out, gamma, eps, rstd_out  as in add_rmsnorm_linear_bf16
  *             (residual and x_add_out together, or both NULL for no add).
