@@ -64,7 +64,7 @@ WORKLOADS = {
 }
 DEFAULT = "preattn_qkv_T4096"
 KERNEL_SOURCES = {
-    "gemm": ["gemm_kernel.hpp", "gemm_bf16.hip", "gemm_int8.hip", "common.hpp"],
+    "gemm": ["gemm_kernel.hpp", "gemm_bf16.hip", "gemm_int8.hip", "common.hpp", "rows.hpp"],
     "small_m": ["small_m.hip", "common.hpp", "rows.hpp"],
     "small_m_norm": ["small_m.hip", "common.hpp", "rows.hpp"],
     "row_gemv": ["row_gemv.hip", "common.hpp"],
