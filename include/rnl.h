@@ -371,6 +371,25 @@ RNL_API int head_rms_norm_bf16(const void* y_in, void* y_out, const void* gamma,
                                int64_t D, void* stream);
 
 /*
+ * linear_heads_bf16 -- the projection of already-normed rows followed by the
+ * per-head stage of preattn_qkv_bf16 (AT-10 page section 6): y = bf16(a . W^T)
+ * with W [(Hq + 2 Hkv) D, K], then every query head (gamma_q) and key head
+ * (gamma_k) of y normed and, with cos / sin [M, D/2] fp32, rotated exactly as
+ * preattn_qkv_bf16 does; the Hkv value heads are the bf16 product.
+ *   a [M, K] bf16, y [M, (Hq + 2 Hkv) D] bf16, head_rstd_out [M, Hq + Hkv] or
+ *   NULL.  K a multiple of 8; D a multiple of 16, at most 512; M (Hq + Hkv) < 2^31.
+ * With D = 128 and more than 16 rows the stage runs in the GEMM's epilogue
+ * (one launch); otherwise the projection and a per-head pass over y (two
+ * launches).  The results are the same bits either way.
+ * Errors: RNL_ERR_NULL (a, W, y; cos without sin or the reverse),
+ * RNL_ERR_SHAPE, RNL_ERR_ARG (head_eps), RNL_ERR_ALIGN (16 bytes; 4 for
+ * head_rstd_out), RNL_ERR_HIP.
+ */
+RNL_API int linear_heads_bf16(const void* a, const void* W, void* y, const void* gamma_q, const void* gamma_k,
+                              float head_eps, const float* cos, const float* sin, float* head_rstd_out, int64_t M,
+                              int64_t K, int64_t Hq, int64_t Hkv, int64_t D, void* stream);
+
+/*
  * linear_bf16 -- AT-09 Linear Projection, BF16 mode (AT-10 page section 4):
  * y[M,N] = a[M,K] . W[N,K]^T (b_trans), bf16 operands, fp32 accumulation,
  * y bf16 (out_dtype RNL_BF16, rounded once) or fp32 (RNL_FP32).

@@ -50,6 +50,7 @@ __all__ = [
     "rms_norm_quant_mxfp8",
     "linear_mxfp8",
     "linear_bf16",
+    "linear_heads_bf16",
     "linear_int8",
     "workspace_bytes",
     "load_library",
@@ -109,6 +110,9 @@ def load_library() -> ctypes.CDLL:
     lib.rms_norm_quant_int8.restype = ctypes.c_int
     lib.linear_bf16.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
     lib.linear_bf16.restype = ctypes.c_int
+    lib.linear_heads_bf16.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                                      _c_i64, _c_i64, _c_i64, _c_p]
+    lib.linear_heads_bf16.restype = ctypes.c_int
     lib.linear_int8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p]
     lib.linear_int8.restype = ctypes.c_int
     lib.add_rmsnorm_linear_bf16.argtypes = [_c_p, _c_p, _c_p] + lib.rmsnorm_linear_bf16.argtypes[1:]
@@ -712,6 +716,34 @@ def linear_bf16(a, W, out_dtype=torch.bfloat16, y=None):
     _shape(tuple(y.shape) == (M, N), "y must be [M, N]")
     with torch.cuda.device(a.device):
         rc = lib.linear_bf16(_ptr(a), _ptr(W), _ptr(y), _DTYPE_CODE[out_dtype], M, K, N, _stream(a.device))
+    _check(rc)
+    return y
+
+
+def linear_heads_bf16(a, W, Hq, Hkv, D, gamma_q=None, gamma_k=None, head_eps=1e-6, cos=None, sin=None, y=None,
+                      head_rstd_out=None):
+    """y = bf16(a . W^T) with W [(Hq + 2 Hkv) D, K], then the per-head stage of
+    :func:`preattn_qkv_bf16` on the query and key heads; returns y."""
+    lib = load_library()
+    _dev_tensor(a, "a", torch.bfloat16, 2)
+    _dev_tensor(W, "W", torch.bfloat16, 2)
+    _dev_tensor(gamma_q, "gamma_q", torch.bfloat16, 1)
+    _dev_tensor(gamma_k, "gamma_k", torch.bfloat16, 1)
+    _dev_tensor(head_rstd_out, "head_rstd_out", torch.float32)
+    M, K = a.shape
+    N = (Hq + 2 * Hkv) * D
+    _shape(tuple(W.shape) == (N, K), "W must be [(Hq + 2 Hkv) D, K]")
+    _shape(gamma_q is None or gamma_q.numel() == D, "gamma_q must be [D]")
+    _shape(gamma_k is None or gamma_k.numel() == D, "gamma_k must be [D]")
+    _shape(head_rstd_out is None or head_rstd_out.numel() >= M * (Hq + Hkv), "head_rstd_out must be [M, Hq + Hkv]")
+    _rope_tables(cos, sin, M, D)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _dev_tensor(y, "y", torch.bfloat16)
+    _shape(tuple(y.shape) == (M, N), "y must be [M, (Hq + 2 Hkv) D]")
+    with torch.cuda.device(a.device):
+        rc = lib.linear_heads_bf16(_ptr(a), _ptr(W), _ptr(y), _ptr(gamma_q), _ptr(gamma_k), float(head_eps), _ptr(cos),
+                                   _ptr(sin), _ptr(head_rstd_out), M, K, Hq, Hkv, D, _stream(a.device))
     _check(rc)
     return y
 

@@ -683,6 +683,46 @@ int rms_norm_quant_int8(const void* x, const void* gamma, float eps, int8_t* xq,
                     "norm+quant launch");
 }
 
+int linear_heads_bf16(const void* a, const void* W, void* y, const void* gamma_q, const void* gamma_k,
+                      float head_eps, const float* cos_t, const float* sin_t, float* head_rstd_out, int64_t M,
+                      int64_t K, int64_t Hq, int64_t Hkv, int64_t D, void* stream) {
+  if (a == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "a, W and y are required");
+  if ((cos_t == nullptr) != (sin_t == nullptr)) return fail(RNL_ERR_NULL, "cos and sin are given together or not at all");
+  if (M <= 0 || K <= 0 || Hq <= 0 || Hkv < 0)
+    return fail(RNL_ERR_SHAPE, "need M, K, Hq >= 1 and Hkv >= 0 (M=%lld K=%lld Hq=%lld Hkv=%lld)", (long long)M,
+                (long long)K, (long long)Hq, (long long)Hkv);
+  RNL_TRY(check_head_dim(D));
+  if (Hq + 2 * Hkv > kMaxDim / D) return fail(RNL_ERR_SHAPE, "(Hq + 2 Hkv) * D must be <= 2^24");
+  const int64_t N = (Hq + 2 * Hkv) * D;
+  RNL_TRY(check_dims(M, K, N, kMaxK));
+  if (M > kMaxHeads / (Hq + Hkv)) return fail(RNL_ERR_SHAPE, "M * (Hq + Hkv) must be < 2^31");
+  RNL_TRY(check_eps(head_eps));
+  RNL_ALIGN(a, 16, "a");
+  RNL_ALIGN(W, 16, "W");
+  RNL_ALIGN(y, 16, "y");
+  RNL_ALIGN(gamma_q, 16, "gamma_q");
+  RNL_ALIGN(gamma_k, 16, "gamma_k");
+  RNL_ALIGN(cos_t, 16, "cos");
+  RNL_ALIGN(sin_t, 16, "sin");
+  RNL_ALIGN(head_rstd_out, 4, "head_rstd_out");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* ab = static_cast<const uint16_t*>(a);
+  const uint16_t* wb = static_cast<const uint16_t*>(W);
+  uint16_t* yb = static_cast<uint16_t*>(y);
+  const uint16_t* gq = static_cast<const uint16_t*>(gamma_q);
+  const uint16_t* gk = static_cast<const uint16_t*>(gamma_k);
+  if (D == rnl::kHeadEpiD && !use_small_m(M) && forced_variant() != V_PREPASS) {
+    const rnl::HeadArgs ha{gq, gk, cos_t, sin_t, head_rstd_out, head_eps, 1.0f / (float)D, (int)Hq, (int)Hkv};
+    return hip_status(rnl::launch_gemm_bf16_heads(ab, wb, yb, M, N, K, ha, s),
+                      "bf16 projection launch with the per-head epilogue");
+  }
+  const hipError_t e = project_bf16(ab, wb, yb, rnl::OUT_BF16, M, N, K, s);
+  if (e != hipSuccess) return hip_status(e, "bf16 projection launch");
+  return hip_status(rnl::launch_head_norm_bf16(yb, yb, M, N, 0, Hq + Hkv, D, Hq, gq, gk, head_eps, cos_t, sin_t,
+                                               head_rstd_out, s),
+                    "per-head norm launch");
+}
+
 int linear_bf16(const void* a, const void* W, void* y, int out_dtype, int64_t M, int64_t K, int64_t N,
                 void* stream) {
   if (a == nullptr || W == nullptr || y == nullptr) return fail(RNL_ERR_NULL, "a, W and y are required");

@@ -210,6 +210,32 @@ def test_preattn_validation(lib, kw, code):
     assert preattn_call(lib, **kw) == E[code]
 
 
+def heads_call(lib, a=FAKE, W=FAKE, y=FAKE, gq=NULL, gk=NULL, heps=1e-6, cos=NULL, sin=NULL, hrstd=NULL, M=64, K=64,
+               Hq=4, Hkv=2, D=128):
+    return lib.linear_heads_bf16(a, W, y, gq, gk, heps, cos, sin, hrstd, M, K, Hq, Hkv, D, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=NULL), "RNL_ERR_NULL"),
+    (dict(y=NULL), "RNL_ERR_NULL"),
+    (dict(sin=ctypes.c_void_p(0x40000)), "RNL_ERR_NULL"),  # sin without cos
+    (dict(D=24), "RNL_ERR_SHAPE"),
+    (dict(D=528), "RNL_ERR_SHAPE"),
+    (dict(K=60), "RNL_ERR_SHAPE"),
+    (dict(M=0), "RNL_ERR_SHAPE"),
+    (dict(Hq=0), "RNL_ERR_SHAPE"),
+    (dict(Hkv=-1), "RNL_ERR_SHAPE"),
+    (dict(Hq=1 << 20), "RNL_ERR_SHAPE"),
+    (dict(M=1 << 24, Hq=128, Hkv=0, D=16), "RNL_ERR_SHAPE"),  # M * (Hq + Hkv) = 2^31 heads
+    (dict(heps=float("inf")), "RNL_ERR_ARG"),
+    (dict(W=ODD), "RNL_ERR_ALIGN"),
+    (dict(gk=ODD), "RNL_ERR_ALIGN"),
+    (dict(hrstd=ctypes.c_void_p(0x10002)), "RNL_ERR_ALIGN"),
+])
+def test_linear_heads_validation(lib, kw, code):
+    assert heads_call(lib, **kw) == E[code]
+
+
 def test_preattn_workspace_is_the_projection_workspace(lib):
     assert lib.preattn_qkv_bf16_workspace_bytes(4096, 4096, 32, 8, 128) == \
         lib.rmsnorm_linear_bf16_workspace_bytes(4096, 4096, 6144, 1, 1)

@@ -838,6 +838,31 @@ def test_preattn_head_epilogue(variant, T, K, Hq, Hkv, residual, rope, head_gamm
     assert np.array_equal(hr, hr2) and np.array_equal(rstd, rstd2)
 
 
+@pytest.mark.parametrize("M,K,Hq,Hkv,rope,head_gamma", [
+    (4096, 4096, 32, 8, True, True),   # the pre-attention block's projection (the epilogue)
+    (300, 520, 3, 1, True, False),     # the epilogue, ragged rows and a two-head column tile
+    (12, 256, 2, 1, False, True),      # few rows: projection, then the per-head pass
+])
+def test_linear_heads(M, K, Hq, Hkv, rope, head_gamma):
+    """The projection with the per-head stage equals the projection followed by the standalone per-head stage,
+    bit for bit, rstd included."""
+    case = synthetic.preattn_case(M, K, Hq, Hkv, 128, seed=M + K, rope=rope, head_gamma=head_gamma)
+    t = {k: dev(v) for k, v in case.tensors.items()}
+    a = rnl.rms_norm_bf16(t["x"], t["gamma"], EPS)
+    hr = torch.empty((M, Hq + Hkv), dtype=torch.float32, device="cuda")
+    y = rnl.linear_heads_bf16(a, t["W"], Hq, Hkv, 128, t["gamma_q"], t["gamma_k"], EPS, t["cos"], t["sin"],
+                              head_rstd_out=hr)
+    p = rnl.linear_bf16(a, t["W"])
+    rq = torch.empty((M, Hq), dtype=torch.float32, device="cuda")
+    rk = torch.empty((M, max(Hkv, 1)), dtype=torch.float32, device="cuda")
+    q = rnl.head_rms_norm_bf16(p.clone(), 0, Hq, 128, t["gamma_q"], EPS, t["cos"], t["sin"], rstd_out=rq)
+    if Hkv:
+        q = rnl.head_rms_norm_bf16(q, Hq * 128, Hkv, 128, t["gamma_k"], EPS, t["cos"], t["sin"], rstd_out=rk)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), q.view(torch.int16)), f"{int((y != q).sum())} values differ"
+    assert torch.equal(hr[:, :Hq], rq) and (Hkv == 0 or torch.equal(hr[:, Hq:], rk))
+
+
 @pytest.mark.parametrize("T", [4096, 16])
 def test_preattn_block_full_size(T):
     """Residual add -> norm -> fused QKV -> per-head norm -> RoPE, K=4096, 32 + 8 + 8 heads of 128."""
