@@ -199,17 +199,45 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
   };
 
   // Per-head epilogue.  The bf16-rounded tile goes to LDS (the stages are free once every
-  // wavefront is past its last fragment read), then each group of GP lanes takes one
-  // (token row, head) of the tile: lane q holds elements 8q .. 8q+7 and D/2+8q .. D/2+8q+7, the
-  // layout of the standalone per-head kernel, and the same arithmetic (head_sumsq, group_sum,
-  // head_chunks) gives the same bits.  Value heads are stored as they are.
+  // wavefront is past its last fragment read); each group of GP lanes then takes RPG token rows
+  // of the tile and, row by row, its HPT heads: lane q holds elements 8q .. 8q+7 and
+  // D/2+8q .. D/2+8q+7, the layout of the standalone per-head kernel, and the same arithmetic
+  // (head_sumsq, group_sum, head_chunks) gives the same bits.  Value heads are stored as they
+  // are.  The head gammas and the rows' angles are requested before the tile is staged, so
+  // that no step of the loop waits for global memory.
   auto heads_epilogue = [&](const HeadArgs& h) {
     if constexpr (EPI == EPI_HEADS) {
-      constexpr int HD = kHeadEpiD, GP = HD / 16, HPT = BN / HD, UPW = kWave / GP;
-      constexpr int LDY = BN + 8;  // bf16 per LDS tile row (padded)
+      constexpr int HD = kHeadEpiD, GP = HD / 16, HPT = BN / HD, NG = NWV * (kWave / GP);
+      constexpr int RPG = BM / NG;  // token rows per lane group
+      constexpr int LDY = BN + 8;   // bf16 per LDS tile row (padded)
       static_assert(sizeof(TIn) == 2 && BN % HD == 0, "whole bf16 heads per tile");
       static_assert(BM * LDY * 2 <= NST * STAGE, "the output tile fits the stages");
-      static_assert((BM * HPT) % (NWV * UPW) == 0, "whole rounds of head groups");
+      static_assert(RPG * NG == BM, "whole rows per lane group");
+      const int grp = wave * (kWave / GP) + lane / GP, gl = lane & (GP - 1);
+      const int c0 = gl * 8, c1 = c0 + HD / 2;
+      const bool rope = h.cos_t != nullptr;
+      const bool gq_on = h.gamma_q != nullptr, gk_on = h.gamma_k != nullptr;
+      u32x4 gq0{}, gq1{}, gk0{}, gk1{};
+      if (gq_on) {
+        gq0 = *reinterpret_cast<const u32x4*>(h.gamma_q + c0);
+        gq1 = *reinterpret_cast<const u32x4*>(h.gamma_q + c1);
+      }
+      if (gk_on) {
+        gk0 = *reinterpret_cast<const u32x4*>(h.gamma_k + c0);
+        gk1 = *reinterpret_cast<const u32x4*>(h.gamma_k + c1);
+      }
+      f32x4 cs[RPG][2], sn[RPG][2];
+      if (rope) {
+#pragma unroll
+        for (int j = 0; j < RPG; ++j) {
+          const int t = m0 + grp + j * NG;
+          const size_t ab = (size_t)(t < M ? t : 0) * (HD / 2) + c0;  // a row that exists, for rows past M
+          cs[j][0] = *reinterpret_cast<const f32x4*>(h.cos_t + ab);
+          cs[j][1] = *reinterpret_cast<const f32x4*>(h.cos_t + ab + 4);
+          sn[j][0] = *reinterpret_cast<const f32x4*>(h.sin_t + ab);
+          sn[j][1] = *reinterpret_cast<const f32x4*>(h.sin_t + ab + 4);
+        }
+      }
       uint16_t* ty = reinterpret_cast<uint16_t*>(smem);
       __syncthreads();
 #pragma unroll
@@ -219,49 +247,32 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
           *reinterpret_cast<u32x2*>(ty + (wm * WM + i * 16 + (lane & 15)) * LDY + wn * WN + j * 16 + 4 * (lane >> 4)) =
               u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
       __syncthreads();
-      const int gl = lane & (GP - 1);
-      const int c0 = gl * 8, c1 = c0 + HD / 2;
       const int nqk = h.hq + h.hkv;
-      const bool rope = h.cos_t != nullptr;
       uint16_t* y = static_cast<uint16_t*>(C);
-#pragma unroll 1
-      for (int it = 0; it < BM * HPT / (NWV * UPW); ++it) {
-        const int u = (it * NWV + wave) * UPW + lane / GP;
-        const int r = u / HPT, hh = u - r * HPT;
-        const int t = m0 + r, col = n0 + hh * HD, hg = col / HD;
-        const bool live = t < M && col < N;
-        const int ts = live ? t : 0;  // a row that exists, for the loads of dead groups
-        const uint16_t* src = ty + r * LDY + hh * HD;
-        const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
-        const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
-        const bool qk = hg < nqk;
-        const uint16_t* gamma = hg < h.hq ? h.gamma_q : h.gamma_k;
-        const bool g_on = gamma != nullptr;
-        u32x4 g0 = v0, g1 = v1;
-        if (g_on) {
-          g0 = *reinterpret_cast<const u32x4*>(gamma + c0);
-          g1 = *reinterpret_cast<const u32x4*>(gamma + c1);
-        }
-        f32x4 cs[2], sn[2];
-        if (rope) {
-          const float* ca = h.cos_t + (size_t)ts * (HD / 2) + c0;
-          const float* sa = h.sin_t + (size_t)ts * (HD / 2) + c0;
-          cs[0] = *reinterpret_cast<const f32x4*>(ca);
-          cs[1] = *reinterpret_cast<const f32x4*>(ca + 4);
-          sn[0] = *reinterpret_cast<const f32x4*>(sa);
-          sn[1] = *reinterpret_cast<const f32x4*>(sa + 4);
-        }
-        const float rstd = rstd_from_sumsq(group_sum<GP>(head_sumsq(v0, v1)), h.inv_d, h.eps);
-        u32x4 o0 = v0, o1 = v1;
-        if (qk) {
-          if (rope) head_chunks<true>(v0, v1, g0, g1, g_on, cs, sn, rstd, o0, o1);
-          else head_chunks<false>(v0, v1, g0, g1, g_on, cs, sn, rstd, o0, o1);
-        }
-        if (live) {
-          uint16_t* dst = y + (size_t)t * (size_t)N + (size_t)col;
-          *reinterpret_cast<u32x4*>(dst + c0) = o0;
-          *reinterpret_cast<u32x4*>(dst + c1) = o1;
-          if (qk && gl == 0 && h.rstd_out != nullptr) h.rstd_out[(size_t)t * (size_t)nqk + hg] = rstd;
+#pragma unroll
+      for (int j = 0; j < RPG; ++j) {
+        const int r = grp + j * NG, t = m0 + r;
+#pragma unroll
+        for (int hh = 0; hh < HPT; ++hh) {
+          const int col = n0 + hh * HD, hg = col / HD;
+          const uint16_t* src = ty + r * LDY + hh * HD;
+          const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
+          const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
+          const bool qk = hg < nqk, is_q = hg < h.hq;
+          const float rstd = rstd_from_sumsq(group_sum<GP>(head_sumsq(v0, v1)), h.inv_d, h.eps);
+          u32x4 o0 = v0, o1 = v1;
+          if (qk) {
+            const bool g_on = is_q ? gq_on : gk_on;
+            const u32x4 g0 = is_q ? gq0 : gk0, g1 = is_q ? gq1 : gk1;
+            if (rope) head_chunks<true>(v0, v1, g0, g1, g_on, cs[j], sn[j], rstd, o0, o1);
+            else head_chunks<false>(v0, v1, g0, g1, g_on, cs[j], sn[j], rstd, o0, o1);
+          }
+          if (t < M && col < N) {
+            uint16_t* dst = y + (size_t)t * (size_t)N + (size_t)col;
+            *reinterpret_cast<u32x4*>(dst + c0) = o0;
+            *reinterpret_cast<u32x4*>(dst + c1) = o1;
+            if (qk && gl == 0 && h.rstd_out != nullptr) h.rstd_out[(size_t)t * (size_t)nqk + hg] = rstd;
+          }
         }
       }
     }
