@@ -218,10 +218,8 @@ class Setup:
                 self.kern = lambda i: rnl.linear_bf16(a, Wc[i % len(Wc)], y=y)
                 self.kern_units = ("hbm", N * K * 2 + T * K * 2 + T * N * 2)
             else:
-                # the step's GEMM: heads of 128 run the per-head stage in its epilogue
-                self.kernel, self.kernel_key = "gemm_nt_kernel<bf16> (with the per-head epilogue)", "gemm"
-                self.kern = lambda i: rnl.linear_heads_bf16(a, t["W"], Hq, Hkv, D, t["gamma_q"], t["gamma_k"], eps,
-                                                            t["cos"], t["sin"], y=y)
+                self.kernel, self.kernel_key = "gemm_nt_kernel<bf16>", "gemm"
+                self.kern = lambda i: rnl.linear_bf16(a, t["W"], y=y)
                 self.kern_units = ("bf16", flops_of(w))
             Wv = Wc if T <= 16 else [t["W"]]
             self.vendor = ("torch.matmul(a, W.t()), bf16", lambda i: torch.matmul(a, Wv[i % len(Wv)].t(), out=y))
