@@ -30,10 +30,12 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, int o
 
 // The per-head epilogue needs whole heads in a tile: 128 x 384 (three heads of 128), eight
 // wavefronts of 64 x 96 as in the 256 x 192 tile, two stages (128 KiB, which also hold the
-// output tile).  At 4096 x 6144 it gives 512 tiles, two rounds of workgroups.
+// output tile).  At 4096 x 6144 it gives 512 tiles, two rounds of workgroups.  Groups of 8
+// tile rows: with groups of 4, each XCD's round of 32 tiles spans 8 weight panels of 384
+// rows, and the launch fetched 475 MB from HBM against 328 MB for the 256 x 192 GEMM.
 hipError_t launch_gemm_bf16_heads(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N,
                                   int64_t K, const HeadArgs& heads, hipStream_t s) {
-  return launch_tile<uint16_t, 128, 384, 2, EPI_HEADS, 1, 4, 2>(A, B, C, nullptr, nullptr, M, N, K, 1, s, heads);
+  return launch_tile<uint16_t, 128, 384, 2, EPI_HEADS, 1, 4, 2, 8>(A, B, C, nullptr, nullptr, M, N, K, 1, s, heads);
 }
 
 hipError_t launch_gemm_bf16_splitk(const uint16_t* A, const uint16_t* B, float* partial, int64_t M,

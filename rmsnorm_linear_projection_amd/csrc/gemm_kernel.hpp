@@ -390,14 +390,16 @@ void gemm_nt_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, void* 
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename TIn, int BM, int BN, int NST, int EPI, int WPE = 1, int WNW = 2, int WMW = 2>
+// GM: tiles per group along M (each XCD's run of tiles covers GM tile rows, so the wider the
+// weight panel relative to the activation panel, the more tile rows a group should hold)
+template <typename TIn, int BM, int BN, int NST, int EPI, int WPE = 1, int WNW = 2, int WMW = 2, int GM = 4>
 hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, const float* ws, int64_t M,
                        int64_t N, int64_t K, int ksplit, hipStream_t s, const HeadArgs& ha = HeadArgs{}) {
   const int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   const int nk = (int)cdiv(K * (int64_t)sizeof(TIn), 128);
   const int sps = (int)cdiv(nk, ksplit);
   const int nwg = tiles_m * tiles_n * ksplit;
-  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, 4, EPI, WPE, WNW, WMW>), dim3(nwg), dim3(64 * WMW * WNW), 0, s, A, B, C,
+  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN, NST, GM, EPI, WPE, WNW, WMW>), dim3(nwg), dim3(64 * WMW * WNW), 0, s, A, B, C,
                      xs, ws, (int)M, (int)N, (int)K, tiles_m, tiles_n, ksplit, sps, ha);
   return hipGetLastError();
 }
