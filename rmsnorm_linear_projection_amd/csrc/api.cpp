@@ -558,24 +558,21 @@ int mla_prolog_bf16(const void* x, const void* W_akv, const void* gamma_cq, cons
   hipError_t e;
   // one pass over x for both branches: [q_a | kv] = x . [W_a; W_kv]^T, then each
   // part of the row is normed with its own gamma
+  // the query and the kv columns are normed on their own, in one launch
+  const rnl::NormCols cq{0, R, gq, qr, rstd_q_out}, ckv{R, Rkv, gkv, kvo, rstd_kv_out};
   if (ks > 1) {
     float* part = static_cast<float*>(workspace);
     e = rnl::launch_gemm_bf16_splitk(xb, w, part, T, Rt, K, ks, s);
     if (e != hipSuccess) return hip_status(e, "stage-1 split-K GEMM launch");
-    e = rnl::launch_reduce_norm_bf16(part, ks, Rt, gq, eps, T, R, qr, rstd_q_out, keep, Rt, s);
-    if (e != hipSuccess) return hip_status(e, "query reduce+norm launch");
-    e = rnl::launch_reduce_norm_bf16(part + R, ks, Rt, gkv, eps, T, Rkv, kvo, rstd_kv_out,
-                                     keep == nullptr ? nullptr : keep + R, Rt, s);
-    if (e != hipSuccess) return hip_status(e, "kv reduce+norm launch");
+    e = rnl::launch_reduce_norm_pair_bf16(part, ks, Rt, T, cq, ckv, eps, keep, s);
+    if (e != hipSuccess) return hip_status(e, "query and kv reduce+norm launch");
   } else {
     // the stage-1 rows go to qakv_out when the caller asks for them
     uint16_t* qakv = keep != nullptr ? keep : static_cast<uint16_t*>(workspace);
     e = project_bf16(xb, w, qakv, rnl::OUT_BF16, T, Rt, K, s);
     if (e != hipSuccess) return hip_status(e, "stage-1 projection launch");
-    e = rnl::launch_norm_rows_bf16_strided(qakv, Rt, gq, eps, T, R, qr, rstd_q_out, s);
-    if (e != hipSuccess) return hip_status(e, "query norm launch");
-    e = rnl::launch_norm_rows_bf16_strided(qakv + R, Rt, gkv, eps, T, Rkv, kvo, rstd_kv_out, s);
-    if (e != hipSuccess) return hip_status(e, "kv norm launch");
+    e = rnl::launch_norm_rows_pair_bf16_strided(qakv, Rt, T, cq, ckv, eps, s);
+    if (e != hipSuccess) return hip_status(e, "query and kv norm launch");
   }
   return hip_status(project_bf16(qr, static_cast<const uint16_t*>(W_b), y, rnl::OUT_BF16, T, N, R, s),
                     "stage-2 projection launch");

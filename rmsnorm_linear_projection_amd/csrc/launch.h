@@ -38,10 +38,21 @@ hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t
 hipError_t launch_reduce_norm_bf16(const float* part, int S, int64_t ld, const uint16_t* gamma, float eps,
                                    int64_t T, int64_t K, uint16_t* out, float* rstd_out, uint16_t* sum_out,
                                    int64_t sum_ld, hipStream_t s);
-// The bf16 norm of K values of rows with stride ld (x + t * ld; ld a multiple of
-// 8); out is [T, K].
-hipError_t launch_norm_rows_bf16_strided(const uint16_t* x, int64_t ld, const uint16_t* gamma, float eps, int64_t T,
-                                         int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s);
+// Two column ranges of the same rows normed on their own in one launch: the K
+// columns from col0 (a multiple of 8) with their gamma, to out [T, K] and rstd_out.
+struct NormCols {
+  int64_t col0, K;
+  const uint16_t* gamma;
+  uint16_t* out;
+  float* rstd_out;
+};
+// launch_reduce_norm_bf16 for two column ranges of the partial rows (sum_out, when
+// not null, receives both ranges' bf16 sums at their columns, row stride ld).
+hipError_t launch_reduce_norm_pair_bf16(const float* part, int S, int64_t ld, int64_t T, const NormCols& a,
+                                        const NormCols& b, float eps, uint16_t* sum_out, hipStream_t s);
+// The same for bf16 rows with stride ld (row t at x + t * ld; ld a multiple of 8).
+hipError_t launch_norm_rows_pair_bf16_strided(const uint16_t* x, int64_t ld, int64_t T, const NormCols& a,
+                                              const NormCols& b, float eps, hipStream_t s);
 
 // Per-head RMSNorm (+ rotate-half RoPE when cos_t/sin_t are given) of the H
 // heads of D columns that start at column col0 of y_in[T, ld] (bf16), written

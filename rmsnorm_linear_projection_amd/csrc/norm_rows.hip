@@ -136,13 +136,12 @@ struct RowPartials {
 
 // CPT > 0: each thread keeps CPT 16-byte chunks of the row in registers.
 // CPT == 0: the row is re-read (re-derived) for each pass.
+// One row t, the whole workgroup (red: four floats of LDS for the reductions).
 template <int CPT, bool INT8, class Row>
-__global__ __launch_bounds__(kThreads) void norm_rows_kernel(
-    Row row, const uint16_t* __restrict__ gamma, float eps, float inv_k, int64_t K,
-    void* __restrict__ out, float* __restrict__ x_scale_out, float* __restrict__ rstd_out) {
-  __shared__ float red[4];
+__device__ __forceinline__ void norm_row(Row row, const uint16_t* __restrict__ gamma, float eps, float inv_k,
+                                         int64_t K, void* __restrict__ out, float* __restrict__ x_scale_out,
+                                         float* __restrict__ rstd_out, int64_t t, float* red) {
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
   const int nch = (int)(K >> 3);
   const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
 
@@ -236,6 +235,36 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
       for (int idx = tid; idx < nch; idx += kThreads) emit(row(t, idx), idx);
     }
   }
+}
+
+template <int CPT, bool INT8, class Row>
+__global__ __launch_bounds__(kThreads) void norm_rows_kernel(
+    Row row, const uint16_t* __restrict__ gamma, float eps, float inv_k, int64_t K,
+    void* __restrict__ out, float* __restrict__ x_scale_out, float* __restrict__ rstd_out) {
+  __shared__ float red[4];
+  norm_row<CPT, INT8>(row, gamma, eps, inv_k, K, out, x_scale_out, rstd_out, (int64_t)blockIdx.x, red);
+}
+
+// Two row sets normed in one launch (the query and the key-value parts of the MLA
+// prolog's stage-1 rows): workgroups [0, T) take part a, [T, 2T) part b.
+template <class Row>
+struct NormPart {
+  Row row;
+  const uint16_t* gamma;
+  float inv_k;
+  int64_t K;
+  uint16_t* out;
+  float* rstd_out;
+};
+
+template <int CPT, class Row>
+__global__ __launch_bounds__(kThreads) void norm_rows_pair_kernel(NormPart<Row> a, NormPart<Row> b, float eps,
+                                                                  int64_t T) {
+  __shared__ float red[4];
+  const bool second = (int64_t)blockIdx.x >= T;  // uniform over the workgroup
+  const NormPart<Row> p = second ? b : a;
+  norm_row<CPT, false>(p.row, p.gamma, eps, p.inv_k, p.K, p.out, nullptr, p.rstd_out,
+                       (int64_t)blockIdx.x - (second ? T : 0), red);
 }
 
 // Short rows (K <= 8192): one wavefront per row, four rows per workgroup.  Each
@@ -377,6 +406,20 @@ hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int
   return hipGetLastError();
 }
 
+template <class Row>
+hipError_t launch_norm_pair(const NormPart<Row>& a, const NormPart<Row>& b, float eps, int64_t T, hipStream_t s) {
+  const int64_t per = (std::max(a.K, b.K) / 8 + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)(2 * T)), block(kThreads);
+#define RNL_NORM_PAIR(C) hipLaunchKernelGGL((norm_rows_pair_kernel<C, Row>), grid, block, 0, s, a, b, eps, T)
+  if (per <= 1) RNL_NORM_PAIR(1);
+  else if (per <= 2) RNL_NORM_PAIR(2);
+  else if (per <= 4) RNL_NORM_PAIR(4);
+  else if (per <= 8) RNL_NORM_PAIR(8);
+  else RNL_NORM_PAIR(0);
+#undef RNL_NORM_PAIR
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
@@ -384,11 +427,6 @@ hipError_t launch_norm_rows_bf16(const uint16_t* x, const uint16_t* gamma, float
   if (wave_rows(T, K))
     return launch_norm_wave<false, false>(x, nullptr, nullptr, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
   return launch_norm<false>(RowBf16{x, K}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
-}
-
-hipError_t launch_norm_rows_bf16_strided(const uint16_t* x, int64_t ld, const uint16_t* gamma, float eps, int64_t T,
-                                         int64_t K, uint16_t* a_out, float* rstd_out, hipStream_t s) {
-  return launch_norm<false>(RowBf16{x, ld}, gamma, eps, T, K, a_out, nullptr, rstd_out, s);
 }
 
 hipError_t launch_norm_rows_int8(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
@@ -431,6 +469,23 @@ hipError_t launch_add_rows(const uint16_t* x, const uint16_t* residual, uint16_t
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(residual),
                      reinterpret_cast<u32x4*>(x_add), n);
   return hipGetLastError();
+}
+
+hipError_t launch_reduce_norm_pair_bf16(const float* part, int S, int64_t ld, int64_t T, const NormCols& a,
+                                        const NormCols& b, float eps, uint16_t* sum_out, hipStream_t s) {
+  auto mk = [&](const NormCols& c) {
+    return NormPart<RowPartials>{RowPartials{part + c.col0, T * ld, ld, S, sum_out ? sum_out + c.col0 : nullptr, ld},
+                                 c.gamma, 1.0f / (float)c.K, c.K, c.out, c.rstd_out};
+  };
+  return launch_norm_pair(mk(a), mk(b), eps, T, s);
+}
+
+hipError_t launch_norm_rows_pair_bf16_strided(const uint16_t* x, int64_t ld, int64_t T, const NormCols& a,
+                                              const NormCols& b, float eps, hipStream_t s) {
+  auto mk = [&](const NormCols& c) {
+    return NormPart<RowBf16>{RowBf16{x + c.col0, ld}, c.gamma, 1.0f / (float)c.K, c.K, c.out, c.rstd_out};
+  };
+  return launch_norm_pair(mk(a), mk(b), eps, T, s);
 }
 
 hipError_t launch_reduce_norm_bf16(const float* part, int S, int64_t ld, const uint16_t* gamma, float eps,
