@@ -407,8 +407,9 @@ hipError_t launch_tile(const TIn* A, const TIn* B, void* C, const float* xs, con
 // Tile shapes, largest first: 256x192 (2 LDS stages, 112 KiB), 256x128 and 128x256
 // (3 stages, 144 KiB), 128x128 (4 stages, 128 KiB); and 128x128 with 2 stages
 // (64 KiB), two workgroups per CU, so that one tile's prologue, barriers and
-// output writes overlap the other's k-loop (used by the int8 GEMM).
-enum Shape { S256x192, S256x128, S128x256, S128x128, S128x128_2PerCU };
+// output writes overlap the other's k-loop (used by the int8 GEMM); 128x96 (3
+// stages, 84 KiB) for split-K stages whose 128x128 tiles would leave CUs idle.
+enum Shape { S256x192, S256x128, S128x256, S128x128, S128x128_2PerCU, S128x96 };
 
 inline Shape pick_shape(int64_t M, int64_t N) {
   // Largest tile that still gives every CU at least one workgroup.
@@ -426,6 +427,7 @@ hipError_t launch_shape(Shape sh, const TIn* A, const TIn* B, void* C, const flo
     case S256x128: return launch_tile<TIn, 256, 128, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x256: return launch_tile<TIn, 128, 256, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     case S128x128_2PerCU: return launch_tile<TIn, 128, 128, 2, EPI, 2>(A, B, C, xs, ws, M, N, K, ksplit, s);
+    case S128x96: return launch_tile<TIn, 128, 96, 3, EPI>(A, B, C, xs, ws, M, N, K, ksplit, s);
     default: return launch_tile<TIn, 128, 128, 4, EPI, 1, 2, 4>(A, B, C, xs, ws, M, N, K, ksplit, s);
   }
 }
