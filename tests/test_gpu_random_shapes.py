@@ -17,6 +17,7 @@ import synthetic
 from tests.test_gpu_parity import (check_add_bf16_case, check_add_int8_case, check_bf16_case, check_chain_case,
                                    check_fp32w_case, check_int8_case, check_mla_case, check_mx_case,
                                    check_preattn_case)
+from tests.test_gpu_parity import test_linear_heads as linear_heads_case
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +47,8 @@ CHAIN = [(_t(), _k(8, 3000), _k(8, 400), _n(500)) for _ in range(5)]
 MLA = [(_t(), _k(8, 3000), _k(8, 300), _k(8, 200), _n(400)) for _ in range(4)]
 PREATTN = [(_t(), _k(8, 3000), int(_rng.integers(1, 9)), int(_rng.integers(0, 5)), int(_rng.integers(1, 17)) * 16,
             bool(_rng.integers(0, 2)), bool(_rng.integers(0, 2))) for _ in range(6)]
+HEADS = [(int(_rng.integers(17, 600)), _k(8, 3000), int(_rng.integers(1, 9)), int(_rng.integers(0, 5)),
+          bool(_rng.integers(0, 2)), bool(_rng.integers(0, 2))) for _ in range(5)]
 
 
 def _seed(*dims):
@@ -96,3 +99,10 @@ def test_mla_prolog(T, K, R, Rkv, N):
 def test_preattn_block(T, K, Hq, Hkv, D, residual, rope):
     check_preattn_case(synthetic.preattn_case(T, K, Hq, Hkv, D, seed=_seed(T, K, Hq, Hkv, D), residual=residual,
                                               rope=rope))
+
+
+@pytest.mark.parametrize("M,K,Hq,Hkv,rope,head_gamma", HEADS)
+def test_linear_heads_random(M, K, Hq, Hkv, rope, head_gamma):
+    """Heads of 128 on the tiled GEMM (more than 16 rows): the per-head epilogue against the projection and the
+    standalone per-head stage, bit for bit."""
+    linear_heads_case(M, K, Hq, Hkv, rope, head_gamma)
