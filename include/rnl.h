@@ -22,9 +22,11 @@
  *     invalid call touches no memory.  rnl_last_error() gives a detail string
  *     for the calling thread.  No exception or abort crosses the ABI.
  *   - Sizes are int64_t and must be >= 1.  K must be a multiple of 8 (16-byte
- *     vectors of bf16) and at most 2^20; T and N at most 2^24.  Any T and N
- *     in range are accepted: partial tiles are masked (the pages'
- *     valid_shape tails).
+ *     vectors of bf16) and at most 2^20; T below 2^24 (some stages launch a
+ *     workgroup of 256 threads per row, and a grid axis counts its work-items
+ *     in 32 bits) and N at most 2^24.  Any T and N in range are accepted:
+ *     partial tiles are masked (the pages' valid_shape tails).  Buffers may be
+ *     larger than 4 GiB: rows and tiles are addressed from 64-bit bases.
  *   - Alignment: x, gamma, W, Wq, W_a, W_b, y, qr_out, xq_out must be 16-byte
  *     aligned; rstd_out, x_scale_out, w_scale 4-byte; workspace 256-byte.
  *   - eps must be finite and >= 0; it is used as the fp32 value fl(eps).

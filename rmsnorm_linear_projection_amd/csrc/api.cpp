@@ -38,7 +38,11 @@ int hip_status(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxK_int8 = 133144;  // K * 127 * 127 <= 2^31 - 1
-constexpr int64_t kMaxDim = int64_t(1) << 24;  // T and N: keeps grid sizes and 32-bit tile offsets in range
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // N: keeps grid sizes and 32-bit tile offsets in range
+// T: below 2^24, because the long-row norm, the split-K reduce and the fp32-weight
+// finalize launch one workgroup of 256 threads per row, and a dispatch counts its
+// work-items along one grid axis in 32 bits
+constexpr int64_t kMaxT = kMaxDim - 1;
 constexpr int64_t kMaxHeads = (int64_t(1) << 31) - 1;  // T * heads: the per-head kernel divides in 32 bits
 constexpr int64_t kMaxN_fp32w = int64_t(1) << 20;  // fp32 weights: column blocks of 32 fit one grid axis
 constexpr int64_t kSmallM = 16;  // at most this many activation rows: weight-streaming kernel
@@ -76,7 +80,7 @@ int check_dims(int64_t T, int64_t K, int64_t N, int64_t maxK) {
   if (T <= 0 || K <= 0 || N <= 0) return fail(RNL_ERR_SHAPE, "sizes must be >= 1 (T=%lld K=%lld N=%lld)", (long long)T, (long long)K, (long long)N);
   if (K % 8 != 0) return fail(RNL_ERR_SHAPE, "K=%lld is not a multiple of 8", (long long)K);
   if (K > maxK) return fail(RNL_ERR_SHAPE, "K=%lld exceeds the limit %lld", (long long)K, (long long)maxK);
-  if (T > kMaxDim || N > kMaxDim) return fail(RNL_ERR_SHAPE, "T and N must be <= 2^24");
+  if (T > kMaxT || N > kMaxDim) return fail(RNL_ERR_SHAPE, "T must be < 2^24 and N <= 2^24");
   return RNL_OK;
 }
 
@@ -629,7 +633,7 @@ int head_rms_norm_bf16(const void* y_in, void* y_out, const void* gamma, float e
   if (T <= 0 || H <= 0 || col0 < 0 || ld <= 0)
     return fail(RNL_ERR_SHAPE, "need T, H, ld >= 1 and col0 >= 0");
   RNL_TRY(check_head_dim(D));
-  if (T > kMaxDim || ld > kMaxDim) return fail(RNL_ERR_SHAPE, "T and ld must be <= 2^24");
+  if (T > kMaxT || ld > kMaxDim) return fail(RNL_ERR_SHAPE, "T must be < 2^24 and ld <= 2^24");
   if (ld % 8 != 0 || col0 % 8 != 0) return fail(RNL_ERR_SHAPE, "ld and col0 must be multiples of 8");
   if (H > (ld - col0) / D) return fail(RNL_ERR_SHAPE, "col0 + H * D exceeds the row length ld");
   if (T > kMaxHeads / H) return fail(RNL_ERR_SHAPE, "T * H must be < 2^31");

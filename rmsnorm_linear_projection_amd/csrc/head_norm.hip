@@ -22,6 +22,8 @@
 // each chunk is written back by the lane that read it, so y_out may be y_in.
 // The arithmetic (head_sumsq, group_sum, head_chunks) is shared with the
 // projection GEMM's per-head epilogue, so both give the same bits.
+#include <algorithm>
+
 #include "launch.h"
 #include "rows.hpp"
 
@@ -38,7 +40,9 @@ __global__ __launch_bounds__(kHeadThreads) void head_norm_kernel(
   constexpr int HPW = kWave / GP;  // heads per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gl = lane & (GP - 1);
-  const int64_t head = ((int64_t)blockIdx.x * (kHeadThreads / kWave) + wave) * HPW + lane / GP;
+  // a two-axis grid (the x axis alone would overflow the 32-bit work-item count past 2^28 heads)
+  const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t head = (blk * (kHeadThreads / kWave) + wave) * HPW + lane / GP;
   const int P = D >> 4;  // chunk pairs per head
   const bool live = head < nheads_total;
   const bool act = live && gl < P;
@@ -93,7 +97,9 @@ hipError_t launch_head_norm_bf16(const uint16_t* y_in, uint16_t* y_out, int64_t 
   const int64_t total = T * H;
   if (total > 0x7fffffff) return hipErrorInvalidValue;  // the kernel divides head indices in 32 bits
   const int64_t heads_per_block = (kHeadThreads / kWave) * (kWave / gp);
-  const dim3 grid((unsigned)((total + heads_per_block - 1) / heads_per_block)), block(kHeadThreads);
+  const int64_t wgs = (total + heads_per_block - 1) / heads_per_block;
+  const int64_t gx = std::min<int64_t>(wgs, int64_t(1) << 16);
+  const dim3 grid((unsigned)gx, (unsigned)((wgs + gx - 1) / gx)), block(kHeadThreads);
   const float inv_d = 1.0f / (float)D;
   const bool rope = cos_t != nullptr;
 #define RNL_HEAD(GP, R)                                                                                      \

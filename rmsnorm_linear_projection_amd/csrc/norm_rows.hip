@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(
 }
 
 // Two row sets normed in one launch (the query and the key-value parts of the MLA
-// prolog's stage-1 rows): workgroups [0, T) take part a, [T, 2T) part b.
+// prolog's stage-1 rows): grid row 0 takes part a, grid row 1 part b (a second
+// grid axis, so that the x axis holds T workgroups, not 2T).
 template <class Row>
 struct NormPart {
   Row row;
@@ -258,13 +259,10 @@ struct NormPart {
 };
 
 template <int CPT, class Row>
-__global__ __launch_bounds__(kThreads) void norm_rows_pair_kernel(NormPart<Row> a, NormPart<Row> b, float eps,
-                                                                  int64_t T) {
+__global__ __launch_bounds__(kThreads) void norm_rows_pair_kernel(NormPart<Row> a, NormPart<Row> b, float eps) {
   __shared__ float red[4];
-  const bool second = (int64_t)blockIdx.x >= T;  // uniform over the workgroup
-  const NormPart<Row> p = second ? b : a;
-  norm_row<CPT, false>(p.row, p.gamma, eps, p.inv_k, p.K, p.out, nullptr, p.rstd_out,
-                       (int64_t)blockIdx.x - (second ? T : 0), red);
+  const NormPart<Row> p = blockIdx.y != 0 ? b : a;  // uniform over the workgroup
+  norm_row<CPT, false>(p.row, p.gamma, eps, p.inv_k, p.K, p.out, nullptr, p.rstd_out, (int64_t)blockIdx.x, red);
 }
 
 // Short rows (K <= 8192): one wavefront per row, four rows per workgroup.  Each
@@ -409,8 +407,8 @@ hipError_t launch_norm(Row row, const uint16_t* gamma, float eps, int64_t T, int
 template <class Row>
 hipError_t launch_norm_pair(const NormPart<Row>& a, const NormPart<Row>& b, float eps, int64_t T, hipStream_t s) {
   const int64_t per = (std::max(a.K, b.K) / 8 + kThreads - 1) / kThreads;
-  dim3 grid((unsigned)(2 * T)), block(kThreads);
-#define RNL_NORM_PAIR(C) hipLaunchKernelGGL((norm_rows_pair_kernel<C, Row>), grid, block, 0, s, a, b, eps, T)
+  dim3 grid((unsigned)T, 2u), block(kThreads);
+#define RNL_NORM_PAIR(C) hipLaunchKernelGGL((norm_rows_pair_kernel<C, Row>), grid, block, 0, s, a, b, eps)
   if (per <= 1) RNL_NORM_PAIR(1);
   else if (per <= 2) RNL_NORM_PAIR(2);
   else if (per <= 4) RNL_NORM_PAIR(4);

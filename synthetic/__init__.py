@@ -45,6 +45,26 @@ def normal(shape, std: float, seed: int, stream: int, dtype=torch.bfloat16) -> t
     return t.to(dtype).contiguous()
 
 
+def normal_on_device(shape, std: float, seed: int, stream: int, device="cuda", dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0, std^2) draws made on ``device`` by that device's own torch generator (seeded from ``(seed, stream)``
+    like the host draws), in fp32 slabs of at most 2^28 values, each stored as ``dtype``: for operands of several
+    GB, too large to draw on the host in a test.  A given (shape, seed, stream) gives the same tensor every time
+    on a given device; it is not the host draw of the same arguments."""
+    shape = tuple(int(d) for d in shape)
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream)) & 0x7FFF_FFFF_FFFF_FFFF)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    row = math.prod(shape[1:])
+    slab = max(1, (1 << 28) // max(row, 1))
+    for r0 in range(0, shape[0], slab):
+        r1 = min(shape[0], r0 + slab)
+        t = torch.randn((r1 - r0,) + shape[1:], generator=g, dtype=torch.float32, device=device)
+        if std != 1.0:
+            t.mul_(std)
+        out[r0:r1].copy_(t)
+    return out
+
+
 def uniform(shape, lo: float, hi: float, seed: int, stream: int, dtype=torch.bfloat16) -> torch.Tensor:
     """U(lo, hi) draws, made in fp32 and stored as ``dtype`` (CPU tensor)."""
     t = torch.rand(tuple(shape), generator=_gen(seed, stream), dtype=torch.float32)

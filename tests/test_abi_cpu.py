@@ -73,6 +73,7 @@ def bf16_call(lib, x=FAKE, g=NULL, eps=1e-6, W=FAKE, wd=1, y=FAKE, od=1, rstd=NU
     (dict(K=12), "RNL_ERR_SHAPE"),
     (dict(K=(1 << 20) + 8), "RNL_ERR_SHAPE"),
     (dict(T=(1 << 24) + 1), "RNL_ERR_SHAPE"),
+    (dict(T=1 << 24), "RNL_ERR_SHAPE"),  # T < 2^24: one 256-thread workgroup per row must fit a 32-bit grid axis
     (dict(wd=2, N=(1 << 20) + 1), "RNL_ERR_SHAPE"),  # fp32 weights: N <= 2^20
     (dict(wd=3), "RNL_ERR_DTYPE"),
     (dict(od=4), "RNL_ERR_DTYPE"),
@@ -200,7 +201,7 @@ def preattn_call(lib, x=FAKE, r=NULL, xa=NULL, g=NULL, eps=1e-6, W=FAKE, y=FAKE,
     (dict(Hq=0), "RNL_ERR_SHAPE"),
     (dict(Hkv=-1), "RNL_ERR_SHAPE"),
     (dict(Hq=1 << 20), "RNL_ERR_SHAPE"),
-    (dict(T=1 << 24, Hq=128, Hkv=0, D=16), "RNL_ERR_SHAPE"),  # T * (Hq + Hkv) = 2^31 heads
+    (dict(T=(1 << 24) - 1, Hq=129, Hkv=0, D=16), "RNL_ERR_SHAPE"),  # T * (Hq + Hkv) > 2^31 heads
     (dict(heps=-1.0), "RNL_ERR_ARG"),
     (dict(gq=ODD), "RNL_ERR_ALIGN"),
     (dict(cos=ctypes.c_void_p(0x40004), sin=ctypes.c_void_p(0x50000)), "RNL_ERR_ALIGN"),
@@ -226,7 +227,7 @@ def heads_call(lib, a=FAKE, W=FAKE, y=FAKE, gq=NULL, gk=NULL, heps=1e-6, cos=NUL
     (dict(Hq=0), "RNL_ERR_SHAPE"),
     (dict(Hkv=-1), "RNL_ERR_SHAPE"),
     (dict(Hq=1 << 20), "RNL_ERR_SHAPE"),
-    (dict(M=1 << 24, Hq=128, Hkv=0, D=16), "RNL_ERR_SHAPE"),  # M * (Hq + Hkv) = 2^31 heads
+    (dict(M=(1 << 24) - 1, Hq=129, Hkv=0, D=16), "RNL_ERR_SHAPE"),  # M * (Hq + Hkv) > 2^31 heads
     (dict(heps=float("inf")), "RNL_ERR_ARG"),
     (dict(W=ODD), "RNL_ERR_ALIGN"),
     (dict(gk=ODD), "RNL_ERR_ALIGN"),
@@ -257,7 +258,8 @@ def head_call(lib, yi=FAKE, yo=FAKE, g=NULL, eps=1e-6, cos=NULL, sin=NULL, rstd=
     (dict(ld=516, H=1), "RNL_ERR_SHAPE"),    # ld not a multiple of 8
     (dict(D=40, H=1), "RNL_ERR_SHAPE"),      # D not a multiple of 16
     (dict(T=0), "RNL_ERR_SHAPE"),
-    (dict(T=1 << 24, ld=4096, H=256, D=16), "RNL_ERR_SHAPE"),  # T * H = 2^32 heads
+    (dict(T=(1 << 24) - 1, ld=4096, H=256, D=16), "RNL_ERR_SHAPE"),  # T * H > 2^31 heads
+    (dict(T=1 << 24, H=1), "RNL_ERR_SHAPE"),  # T < 2^24
     (dict(eps=float("nan")), "RNL_ERR_ARG"),
     (dict(yo=ctypes.c_void_p(0x10000 + 1024)), "RNL_ERR_ARG"),  # overlaps y_in without being it
     (dict(g=ODD), "RNL_ERR_ALIGN"),
