@@ -1,4 +1,5 @@
-"""Operands past 4 GiB and grids past 2^16 workgroups per axis, through the C ABI.
+"""Operands past 4 GiB, the largest T and N the library accepts, and grids past 2^16
+workgroups per axis, through the C ABI.
 
 One MI355X holds 288 GB, so a single activation, weight or output can exceed the
 4 GiB that a 32-bit byte offset reaches.  The kernels address every row, weight
@@ -266,4 +267,110 @@ def test_head_norm_two_grid_rows():
     ob = bits(rows_of(out, rows))
     assert np.array_equal(ob, ref), f"{int((ob != ref).sum())} head values differ"
     del y, rstd, out
+    free()
+
+
+# The largest token count the library accepts: 2^24 - 1 rows.  Launches with one 256-thread workgroup per row on
+# one grid axis (the fp32-weight finalize, the MLA prolog's paired norm) then hold 2^32 - 256 work-items on it.
+T_MAX = (1 << 24) - 1
+
+
+def test_max_tokens_fp32_weights():
+    T, K, N = T_MAX, 8, 8
+    x = synthetic.normal_on_device((T, K), 1.0, seed=48, stream=1)
+    case = synthetic.norm_linear_case(1, K, N, seed=48, gamma=False, w_dtype="fp32")
+    y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    rstd = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    rnl.rmsnorm_linear_bf16(x, None, EPS, case["W"].cuda(), out_dtype=torch.float32, y=y, rstd_out=rstd)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()) and bool((rstd > 0).all()), "outputs left unwritten"
+    rows = sample(T, [], seed=8, extra=64)
+    xb = bits(rows_of(x, rows))
+    r = rows_of(rstd, rows).numpy()
+    assert_rstd(r, O.rms_norm_rows(xb, None, EPS)[1], "fp32 weights, 2^24 - 1 tokens")
+    y_ref, _ = O.rmsnorm_linear_fp32w(xb, None, EPS, case["W"].numpy(), rstd=r)
+    scale = max(float(np.sqrt(np.mean(y_ref.astype(np.float64) ** 2))), 1e-30)
+    err = np.abs(rows_of(y, rows).numpy().astype(np.float64) - y_ref)
+    assert (err <= 1e-5 * np.maximum(np.abs(y_ref), scale)).all(), f"max err {err.max():.3g}"
+    del x, y, rstd
+    free()
+
+
+def test_max_tokens_mla_prolog():
+    T, K, R, Rkv, N = T_MAX, 8, 8, 8, 8
+    case = synthetic.mla_case(1, K, R, Rkv, N, seed=49)
+    x = synthetic.normal_on_device((T, K), 1.0, seed=49, stream=1)
+    W_akv = torch.cat([case["W_a"], case["W_kv"]], dim=0).contiguous().cuda()
+    rq = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    rkv = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    qakv = torch.empty((T, R + Rkv), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    _, qr, kv = rnl.mla_prolog_bf16(x, W_akv, R, case["gamma"].cuda(), case["gamma_ckv"].cuda(), EPS,
+                                    case["W_b"].cuda(), rstd_q_out=rq, rstd_kv_out=rkv, qakv_out=qakv, y=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()) and bool((rq > 0).all()) and bool((rkv > 0).all()), "rows left unwritten"
+    rows = sample(T, [], seed=9, extra=64)
+    sb = bits(rows_of(qakv, rows))
+    qr_b = bits(rows_of(qr, rows))
+    check_normed_stage(np.ascontiguousarray(sb[:, :R]), bits(case["gamma"]), rows_of(rq, rows).numpy(), qr_b, "qr")
+    check_normed_stage(np.ascontiguousarray(sb[:, R:]), bits(case["gamma_ckv"]), rows_of(rkv, rows).numpy(),
+                       bits(rows_of(kv, rows)), "kv")
+    assert_bf16_close(f32(rows_of(y, rows)), O.project_bf16(O.bf16_bits_to_f32(qr_b), bits(case["W_b"])), "y")
+    del x, qr, kv, rq, rkv, qakv, y
+    free()
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8"])
+def test_max_tokens_gemm(kind):
+    """2^24 - 1 rows through the norm pre-pass and the tiled GEMM (65536 row tiles)."""
+    T, N = T_MAX, 8
+    K = 8 if kind == "bf16" else 16
+    x = synthetic.normal_on_device((T, K), 1.0, seed=50, stream=1)
+    rstd = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    rows = sample(T, [], seed=10, extra=64)
+    if kind == "bf16":
+        case = synthetic.norm_linear_case(1, K, N, seed=50)
+        y = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        rnl.rmsnorm_linear_bf16(x, case["gamma"].cuda(), EPS, case["W"].cuda(), y=y, rstd_out=rstd)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(y).all()) and bool((rstd > 0).all()), "outputs left unwritten"
+        xb, gb, r = bits(rows_of(x, rows)), bits(case["gamma"]), rows_of(rstd, rows).numpy()
+        assert_rstd(r, O.rms_norm_rows(xb, gb, EPS)[1], "bf16, 2^24 - 1 tokens")
+        y32, _, _ = O.rmsnorm_linear_bf16(xb, gb, EPS, bits(case["W"]), rstd=r)
+        assert_bf16_close(f32(rows_of(y, rows)), y32, "bf16, 2^24 - 1 tokens")
+    else:
+        case = synthetic.int8_case(1, K, N, seed=50)
+        xq = torch.full((T, K), -128, dtype=torch.int8, device="cuda")
+        acc = torch.full((T, N), -(2 ** 31), dtype=torch.int32, device="cuda")
+        rnl.rmsnorm_linear_int8(x, case["gamma"].cuda(), EPS, case["Wq"].cuda(), case["w_scale"].cuda(),
+                                out_dtype=torch.int32, xq_out=xq, rstd_out=rstd, y=acc)
+        torch.cuda.synchronize()
+        assert bool((xq != -128).all()) and bool((acc != -(2 ** 31)).all()) and bool((rstd > 0).all())
+        xb, gb, r = bits(rows_of(x, rows)), bits(case["gamma"]), rows_of(rstd, rows).numpy()
+        assert_rstd(r, O.rms_norm_rows(xb, gb, EPS)[1], "int8, 2^24 - 1 tokens")
+        q_ref, _, _ = O.quant_rows(O.rms_norm_rows(xb, gb, EPS, rstd=r)[0])
+        q = rows_of(xq, rows).numpy()
+        assert np.array_equal(q, q_ref), f"xq not bit-exact ({int((q != q_ref).sum())} differ)"
+        assert np.array_equal(rows_of(acc, rows).numpy().astype(np.int64), O.int8_gemm(q, case["Wq"].numpy()))
+    free()
+
+
+@pytest.mark.parametrize("T", [1, 16, 40])
+def test_max_width(T):
+    """N = 2^24 output columns (the largest the library accepts), K = 8: the single-row kernel, the weight
+    streaming kernel (524288 workgroups) and the tiled GEMM."""
+    N, K = 1 << 24, 8
+    W = synthetic.normal_on_device((N, K), K ** -0.5, seed=51, stream=3)
+    case = synthetic.norm_linear_case(T, K, 1, seed=51 + T)
+    y = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    rstd = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    rnl.rmsnorm_linear_bf16(case["x"].cuda(), case["gamma"].cuda(), EPS, W, y=y, rstd_out=rstd)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()), "outputs left unwritten"
+    cols = sample(N, [], seed=11 + T, extra=80)
+    xb, gb, r = bits(case["x"]), bits(case["gamma"]), rstd.cpu().numpy()
+    assert_rstd(r, O.rms_norm_rows(xb, gb, EPS)[1], f"N = 2^24, T={T}")
+    y32, _, _ = O.rmsnorm_linear_bf16(xb, gb, EPS, bits(rows_of(W, cols)), rstd=r)
+    assert_bf16_close(f32(y)[:, cols], y32, f"N = 2^24, T={T}")
+    del W, y, rstd
     free()
