@@ -131,6 +131,42 @@ def test_graph_mxfp8():
                   [y, xq, xs])
 
 
+@pytest.mark.parametrize("T,K,N", [(300, 1032, 200), (16, 4096, 512)])
+def test_graph_noalloc(T, K, N):
+    """The allocation-free entry point, captured as a caller that cannot allocate would capture it.  Between
+    replays an eager call on other inputs runs through the same static scratch, so a replay that read anything
+    left over in the scratch would show; every replay equals the eager call bit for bit."""
+    t = dev(synthetic.norm_linear_case(T, K, N, seed=T + 7))
+    o = dev(synthetic.norm_linear_case(T + 5, K + 8, N, seed=T + 8))
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    r = torch.empty(T, dtype=torch.float32, device="cuda")
+    yo = torch.empty((T + 5, N), dtype=torch.bfloat16, device="cuda")
+
+    def fn():
+        rnl.rmsnorm_linear_bf16_noalloc(t["x"], t["gamma"], EPS, t["W"], y, rstd_out=r)
+    fn()
+    torch.cuda.synchronize()
+    ref = [y.clone(), r.clone()]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    for rep in range(3):
+        rnl.rmsnorm_linear_bf16_noalloc(o["x"], o["gamma"], EPS, o["W"], yo)  # other data through the scratch
+        y.view(torch.uint8).fill_(0xA5)
+        r.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.uint8), ref[0].view(torch.uint8)), f"replay {rep}: y differs"
+        assert torch.equal(r.view(torch.uint8), ref[1].view(torch.uint8)), f"replay {rep}: rstd differs"
+
+
 @pytest.mark.parametrize("nbytes,workgroups,unroll", [(16, 1, 1), (4096 + 16, 3, 4), (48 << 20, 1024, 8),
                                                       (29 << 20, 2048, 16)])
 def test_stream_probe_reads_every_word_once(nbytes, workgroups, unroll):
