@@ -220,9 +220,13 @@ void gemm_mx_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B
     // phase B: refill `slot` with k-step kt + 2; MFMAs of [HM, NMI); read the next
     // k-step's first half and, after its last use, each weight fragment
 #pragma unroll
-    for (int g = 0; g < LPS; ++g) dload_one(kt + 2, slot, g);
-#pragma unroll
     for (int j = 0; j < NNI; ++j) {
+      // the refill is spread over the weight-fragment groups: issued as one burst by all
+      // eight wavefronts, it filled the texture unit's address and command queues (5x the
+      // stall cycles of the bf16 GEMM, which interleaves its refill the same way) and the
+      // MFMAs behind it waited
+#pragma unroll
+      for (int g = j * LPS / NNI; g < (j + 1) * LPS / NNI; ++g) dload_one(kt + 2, slot, g);
       if (j < HM) read_a(nslot, j);
 #pragma unroll
       for (int i = HM; i < NMI; ++i) mma(shift, i, j);
