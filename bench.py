@@ -793,8 +793,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=1000, help="untimed calls before the timed ones")
-    ap.add_argument("--repeats", type=int, default=1,
-                    help="timed runs of --steps calls each; the line reports their median")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of --steps calls each (each bracketed by synchronisations); the line reports "
+                         "their median")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
